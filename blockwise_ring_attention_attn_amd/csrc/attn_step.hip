@@ -1,0 +1,568 @@
+// Fused block-attention step kernels for gfx950 (CDNA4).
+//
+// Pages cited (by title; section or equation named alone):
+//   [TKG] "RingAttention 심층 아키텍처: 통신-연산 완전 중첩과 블록 단위 온라인
+//         소프트맥스로 1,000만 토큰 컨텍스트를 정복한 분산 어텐션 엔지니어링"
+//         (techknowgenie.com).
+//   [AIT] FlashAttention video summary (aitrends.kr): tiling into on-chip
+//         memory, online softmax, Q outer loop / KV inner loop.
+//
+// One launch performs one ring step for a set of query hosts: every
+// workgroup owns BM query rows of one (host, batch, head) and sweeps the
+// visible key/value tiles of that host's current kv block, fusing
+//   S = Q K^T * scale                          [TKG] §3 equation S
+//   causal mask on global positions           [TKG] §7
+//   m_new = max(m, rowmax S), alpha, l update  [TKG] §3 m_block / m_new / alpha / l_new
+//   O = alpha O + P V                          [TKG] §3 O_new
+// and, at the end, merges with the state of earlier ring steps and either
+// stores the fp32 state or finalizes (O / l, lse = m + ln l; [TKG] §3
+// O_final).  The kernel uses the form P = exp(S - m_new) (the page's beta
+// factor folded into P), base-2 exponentials with log2(e) folded into the
+// scale, and keeps m stale while the new tile max stays within 2^8 of it
+// (skipping the alpha rescale; l and O stay relative to the same m, so the
+// result is unchanged).
+//
+// bf16 path: S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16.
+// With K as the A operand every lane ends up owning one query column of
+// S^T, so row max / row sum are in-lane reductions plus one permlane32 swap,
+// and the output accumulator's rescale is a per-lane scalar.  P^T feeds the
+// second MFMA straight from registers: the contraction index is permuted to
+// the order the first MFMA left the keys in, and V^T is read from LDS in
+// that same order.  K tiles are stored row-major and V tiles transposed in
+// LDS, double-buffered: the next tile's global loads are in flight while the
+// current tile computes.
+#include "ra_internal.h"
+
+namespace ra {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kTau = 8.0f;   // lazy-rescale threshold, base-2 units
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ int64_t host_row(int layout, int rank, int64_t i, int blk, int P) {
+  return layout == 0 ? (int64_t)rank * blk + i : i * P + rank;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value of the same query held by the lane 32 apart (the two halves of a
+// wave hold the same 32 queries and disjoint keys / dims).
+__device__ __forceinline__ float partner_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float partner_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Work decomposition shared by both kernels.
+struct Work {
+  int a, b, h, hkv, qtile;
+  int q_rank, kv_rank;
+};
+
+__device__ __forceinline__ Work decode_work(const StepArgs& A) {
+  // XCD-aware remap: consecutive workgroup ids are dealt round-robin to the
+  // 8 XCDs; give each XCD a contiguous range of logical work so the
+  // workgroups that share one kv plane sit behind the same L2.
+  const int G = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, idx = bid >> 3;
+  const int qq = G >> 3, rr = G & 7;
+  const int Lw = xcd * qq + (xcd < rr ? xcd : rr) + idx;
+  const int group = A.H / A.Hkv;
+  const int per_plane = group * A.n_qtiles;
+  const int plane = Lw / per_plane;          // (a, b, hkv)
+  const int rem = Lw - plane * per_plane;
+  const int t = rem / group;                 // heaviest (last) query tile first
+  Work w;
+  const int hg = rem - t * group;
+  w.qtile = A.n_qtiles - 1 - t;
+  w.hkv = plane % A.Hkv;
+  const int ab = plane / A.Hkv;
+  w.b = ab % A.B;
+  w.a = ab / A.B;
+  w.h = w.hkv * group + hg;
+  w.q_rank = A.host_lo + w.a;
+  int kr = (w.q_rank - A.kv_shift) % A.P;
+  w.kv_rank = kr < 0 ? kr + A.P : kr;
+  return w;
+}
+
+// Largest visible key index (within the kv block) for query row i of the
+// block, or -1 if none; clamped to Lkv - 1.
+__device__ __forceinline__ int64_t key_limit(const StepArgs& A, const Work& w, int64_t i) {
+  int64_t lim;
+  if (!A.causal) {
+    lim = A.Lkv - 1;
+  } else if (A.layout == 0) {
+    lim = (int64_t)w.q_rank * A.Lq + i - (int64_t)w.kv_rank * A.Lkv;
+  } else {
+    lim = i - (w.kv_rank > w.q_rank ? 1 : 0);
+  }
+  if (lim > A.Lkv - 1) lim = A.Lkv - 1;
+  if (lim < -1) lim = -1;
+  return lim;
+}
+
+__device__ __forceinline__ int64_t q_row_index(const StepArgs& A, const Work& w, int64_t i) {
+  const int64_t row = A.q_mode == ROWS_COMPACT ? i : host_row(A.layout, w.q_rank, i, A.Lq, A.P);
+  return ((int64_t)w.b * A.H + w.h) * A.q_plane_rows + row;
+}
+
+__device__ __forceinline__ int64_t kv_row_index(const StepArgs& A, const Work& w, int64_t j) {
+  int64_t row;
+  if (A.kv_mode == ROWS_COMPACT) row = j;
+  else row = host_row(A.layout, A.kv_mode == ROWS_HOST_Q ? w.q_rank : w.kv_rank, j, A.Lkv, A.P);
+  return ((int64_t)w.b * A.Hkv + w.hkv) * A.kv_plane_rows + row;
+}
+
+// Epilogue.  The previous state of a row (earlier ring steps) is read once,
+// the merge weights are formed once per row, every group of 4 dims is merged
+// and written, and only then are the row scalars (m, l or lse) written.
+struct RowMerge {
+  float ca, cb;      // weights of the stored state and of this launch's partial
+  float m_new, l_new;
+};
+
+__device__ __forceinline__ RowMerge row_merge(const StepArgs& A, int64_t idx, float m2, float l) {
+  RowMerge r{0.f, 1.f, m2, l};
+  if (A.has_prev) {
+    const float mp = A.m[idx] * kLog2e;
+    const float lp = A.l[idx];
+    r.m_new = fmaxf(mp, m2);
+    r.ca = 0.f;
+    r.cb = 0.f;
+    if (r.m_new != kNegInf) {
+      r.ca = fast_exp2(mp - r.m_new);
+      r.cb = fast_exp2(m2 - r.m_new);
+    }
+    r.l_new = r.ca * lp + r.cb * l;
+  }
+  return r;
+}
+
+template <typename OutT>
+__device__ __forceinline__ void store_dims4(const StepArgs& A, int64_t idx, int dim, int D, bool fin,
+                                            const RowMerge& rm, const float o[4]) {
+  float oo[4] = {rm.cb * o[0], rm.cb * o[1], rm.cb * o[2], rm.cb * o[3]};
+  if (A.has_prev) {
+    const float4 op = *reinterpret_cast<const float4*>(A.o + idx * D + dim);
+    oo[0] += rm.ca * op.x;
+    oo[1] += rm.ca * op.y;
+    oo[2] += rm.ca * op.z;
+    oo[3] += rm.ca * op.w;
+  }
+  if (fin) {
+    const float inv = rm.l_new > 0.f ? 1.f / rm.l_new : 0.f;
+    OutT* out = reinterpret_cast<OutT*>(A.out) + idx * D + dim;
+    if constexpr (sizeof(OutT) == 2) {
+      bf16x2 p0, p1;
+      p0[0] = (__bf16)(oo[0] * inv); p0[1] = (__bf16)(oo[1] * inv);
+      p1[0] = (__bf16)(oo[2] * inv); p1[1] = (__bf16)(oo[3] * inv);
+      u32x2 pk;
+      pk[0] = __builtin_bit_cast(unsigned, p0);
+      pk[1] = __builtin_bit_cast(unsigned, p1);
+      *reinterpret_cast<u32x2*>(out) = pk;
+    } else {
+      *reinterpret_cast<float4*>(out) = make_float4(oo[0] * inv, oo[1] * inv, oo[2] * inv, oo[3] * inv);
+    }
+  } else {
+    *reinterpret_cast<float4*>(A.o + idx * D + dim) = make_float4(oo[0], oo[1], oo[2], oo[3]);
+  }
+}
+
+__device__ __forceinline__ void store_row(const StepArgs& A, int64_t idx, bool fin, const RowMerge& rm) {
+  if (fin) {
+    A.lse[idx] = rm.l_new > 0.f ? (rm.m_new + fast_log2(rm.l_new)) * kLn2 : kNegInf;
+  } else {
+    A.m[idx] = rm.m_new == kNegInf ? kNegInf : rm.m_new * kLn2;
+    A.l[idx] = rm.l_new;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel.  BM = 128 query rows (4 waves x 32), BN = 64 keys / tile.
+// ---------------------------------------------------------------------------
+constexpr int kBM = 128;
+constexpr int kBN = 64;
+constexpr int kThreads = 256;
+
+template <int D>
+struct Lds {
+  static constexpr int KP = D + 8;      // K row pitch (bf16 elements)
+  static constexpr int VP = kBN + 4;    // V^T row pitch (bf16 elements)
+  static constexpr int K_ELEMS = kBN * KP;
+  static constexpr int V_ELEMS = D * VP;
+  static constexpr int BUF = K_ELEMS + V_ELEMS;
+  static constexpr int BYTES = 2 * BUF * 2;
+};
+
+template <int D>
+struct KvRegs {
+  static constexpr int KCH = kBN * D / 8 / kThreads;          // 16-byte K chunks per thread
+  static constexpr int VUNITS = (kBN / 4) * (D / 8);          // 4-key x 8-dim units
+  static constexpr int VU = (VUNITS + kThreads - 1) / kThreads;
+  u32x4 k[KCH];
+  u32x4 v[VU][4];
+};
+
+template <int D>
+__device__ __forceinline__ void load_kv_tile(const StepArgs& A, const Work& w, int tile0,
+                                             KvRegs<D>& R) {
+  const int t = threadIdx.x;
+  const unsigned short* K = reinterpret_cast<const unsigned short*>(A.k);
+  const unsigned short* V = reinterpret_cast<const unsigned short*>(A.v);
+  constexpr int CPR = D / 8;  // chunks per row
+#pragma unroll
+  for (int u = 0; u < KvRegs<D>::KCH; ++u) {
+    const int c = t + u * kThreads;
+    const int row = c / CPR, col = c % CPR;
+    const int j = tile0 + row;
+    if (j < A.Lkv) {
+      R.k[u] = *reinterpret_cast<const u32x4*>(K + kv_row_index(A, w, j) * D + col * 8);
+    } else {
+      R.k[u] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < KvRegs<D>::VU; ++u) {
+    const int unit = t + u * kThreads;
+    if (unit < KvRegs<D>::VUNITS) {
+      const int dg = unit % CPR, kg = unit / CPR;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int j = tile0 + kg * 4 + kk;
+        if (j < A.Lkv) {
+          R.v[u][kk] = *reinterpret_cast<const u32x4*>(V + kv_row_index(A, w, j) * D + dg * 8);
+        } else {
+          R.v[u][kk] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_kv_tile(unsigned short* lds_buf, const KvRegs<D>& R) {
+  const int t = threadIdx.x;
+  constexpr int CPR = D / 8;
+  unsigned short* Ks = lds_buf;
+  unsigned short* Vt = lds_buf + Lds<D>::K_ELEMS;
+#pragma unroll
+  for (int u = 0; u < KvRegs<D>::KCH; ++u) {
+    const int c = t + u * kThreads;
+    const int row = c / CPR, col = c % CPR;
+    *reinterpret_cast<u32x4*>(Ks + row * Lds<D>::KP + col * 8) = R.k[u];
+  }
+#pragma unroll
+  for (int u = 0; u < KvRegs<D>::VU; ++u) {
+    const int unit = t + u * kThreads;
+    if (unit < KvRegs<D>::VUNITS) {
+      const int dg = unit % CPR, kg = unit / CPR;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const unsigned sel = (i & 1) ? 0x07060302u : 0x05040100u;
+        const int dw = i >> 1;
+        u32x2 pr;
+        pr[0] = __builtin_amdgcn_perm(R.v[u][1][dw], R.v[u][0][dw], sel);
+        pr[1] = __builtin_amdgcn_perm(R.v[u][3][dw], R.v[u][2][dw], sel);
+        *reinterpret_cast<u32x2*>(Vt + (dg * 8 + i) * Lds<D>::VP + kg * 4) = pr;
+      }
+    }
+  }
+}
+
+template <int D, typename OutT>
+__global__ __launch_bounds__(kThreads, 2) void step_bf16_kernel(StepArgs A) {
+  extern __shared__ __align__(16) unsigned short lds[];
+  const Work w = decode_work(A);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5;       // which half of the wave
+  const int col = lane & 31;        // query column owned by this lane
+  const int64_t row_first = (int64_t)w.qtile * kBM;
+  const int64_t row_last = (row_first + kBM < A.Lq ? row_first + kBM : A.Lq) - 1;
+  const int64_t my_row = row_first + wave * 32 + col;
+  const bool row_ok = my_row < A.Lq;
+
+  // Visible key range of this tile of queries.
+  const int64_t kv_end = key_limit(A, w, row_last) + 1;     // keys [0, kv_end) may be visible
+  const int64_t full_end = key_limit(A, w, row_first) + 1;  // keys [0, full_end) visible to all rows
+  const int64_t my_lim = key_limit(A, w, my_row < A.Lq ? my_row : row_last);
+  const int ntiles = (int)((kv_end + kBN - 1) / kBN);
+
+  // Resident query fragment: B operand of S^T = K Q^T (16 dims per MFMA).
+  bf16x8 qf[D / 16];
+  {
+    const unsigned short* Q = reinterpret_cast<const unsigned short*>(A.q);
+    const int64_t qi = q_row_index(A, w, row_ok ? my_row : row_first);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      u32x4 x = row_ok ? *reinterpret_cast<const u32x4*>(Q + qi * D + ks * 16 + half * 8)
+                       : u32x4{0u, 0u, 0u, 0u};
+      qf[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+  float m_run = kNegInf, l_run = 0.f;
+  const float c = A.scale_log2;
+
+  KvRegs<D> R;
+  if (ntiles > 0) {
+    load_kv_tile<D>(A, w, 0, R);
+    store_kv_tile<D>(lds, R);
+  }
+  __syncthreads();
+
+  for (int jt = 0; jt < ntiles; ++jt) {
+    unsigned short* cur = lds + (jt & 1) * Lds<D>::BUF;
+    if (jt + 1 < ntiles) load_kv_tile<D>(A, w, (jt + 1) * kBN, R);
+
+    // S^T = K Q^T for two blocks of 32 keys.
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      const unsigned short* kr = cur + (kb * 32 + col) * Lds<D>::KP + half * 8;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + ks * 16));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+      }
+    }
+
+    // Mask: only tiles that reach past the all-visible prefix.
+    const int64_t tile0 = (int64_t)jt * kBN;
+    if (tile0 + kBN > full_end) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t j = tile0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (j > my_lim) s[kb][r] = kNegInf;
+        }
+    }
+
+    // Row max of this tile (raw scores), shared by both halves.
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = partner_max(mx);
+    const float m_tile = mx * c;
+
+    // Online-softmax update with a lazily refreshed reference max.
+    const bool need = m_tile > m_run + kTau;
+    if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+
+    // P = exp2(S c - m): the row sum l takes the fp32 values, the PV
+    // product their bf16 rounding (the page's listing does the same: block
+    // sum from the fp32 exponentials, P cast to the V dtype for P V).
+    bf16x8 pk[2][2];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hc = 0; hc < 2; ++hc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = fast_exp2(__builtin_fmaf(s[kb][hc * 8 + e], c, -m_use));
+          lsum += p;
+          pk[kb][hc][e] = (__bf16)p;
+        }
+    l_run += lsum;
+
+    // O^T += V^T P^T.  Contraction index k = 8*half + e maps to key
+    // 16*hc + 8*(e/4) + 4*half + e%4 of key block kb (the S^T register order).
+    const unsigned short* vt = cur + Lds<D>::K_ELEMS;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const unsigned short* vr = vt + (db * 32 + col) * Lds<D>::VP + 4 * half;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hc = 0; hc < 2; ++hc) {
+          const int k0 = kb * 32 + hc * 16;
+          u32x2 lo = *reinterpret_cast<const u32x2*>(vr + k0);
+          u32x2 hi = *reinterpret_cast<const u32x2*>(vr + k0 + 8);
+          u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                             pk[kb][hc], oacc[db], 0, 0, 0);
+        }
+    }
+
+    if (jt + 1 < ntiles) store_kv_tile<D>(lds + ((jt + 1) & 1) * Lds<D>::BUF, R);
+    __syncthreads();
+  }
+
+  // Combine the two halves' partial sums (they saw disjoint keys).
+  const float l_tot = partner_sum(l_run);
+  if (!row_ok) return;
+  const bool fin = w.q_rank >= A.fin_lo && w.q_rank < A.fin_hi;
+  const int64_t idx = q_row_index(A, w, my_row);
+  const RowMerge rm = row_merge(A, idx, m_run, l_tot);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float o4[4] = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+      store_dims4<OutT>(A, idx, db * 32 + 8 * g + 4 * half, D, fin, rm, o4);
+    }
+  if (half == 0) store_row(A, idx, fin, rm);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: one thread per query row, K/V tiles of 32 rows in LDS.
+// Plain fp32 FMA arithmetic (no reduced-precision products).
+// ---------------------------------------------------------------------------
+constexpr int kF32BM = 64;
+constexpr int kF32BN = 32;
+
+template <int D>
+__global__ __launch_bounds__(kF32BM) void step_f32_kernel(StepArgs A) {
+  __shared__ float Ks[kF32BN][D];
+  __shared__ float Vs[kF32BN][D];
+  const Work w = decode_work(A);
+  const int t = threadIdx.x;
+  const int64_t row_first = (int64_t)w.qtile * kF32BM;
+  const int64_t row_last = (row_first + kF32BM < A.Lq ? row_first + kF32BM : A.Lq) - 1;
+  const int64_t my_row = row_first + t;
+  const bool row_ok = my_row < A.Lq;
+  const int64_t kv_end = key_limit(A, w, row_last) + 1;
+  const int64_t my_lim = key_limit(A, w, row_ok ? my_row : row_last);
+  const float* Q = reinterpret_cast<const float*>(A.q);
+  const float* K = reinterpret_cast<const float*>(A.k);
+  const float* V = reinterpret_cast<const float*>(A.v);
+
+  float q[D], o[D];
+  {
+    const int64_t qi = q_row_index(A, w, row_ok ? my_row : row_first);
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+      q[c] = row_ok ? Q[qi * D + c] : 0.f;
+      o[c] = 0.f;
+    }
+  }
+  float m_run = kNegInf, l_run = 0.f;
+  const float cs = A.scale_log2;
+  for (int64_t tile0 = 0; tile0 < kv_end; tile0 += kF32BN) {
+    __syncthreads();
+    for (int e = t; e < kF32BN * D; e += kF32BM) {
+      const int r = e / D, cc = e % D;
+      const int64_t j = tile0 + r;
+      float kv = 0.f, vv = 0.f;
+      if (j < A.Lkv) {
+        const int64_t ri = kv_row_index(A, w, j);
+        kv = K[ri * D + cc];
+        vv = V[ri * D + cc];
+      }
+      Ks[r][cc] = kv;
+      Vs[r][cc] = vv;
+    }
+    __syncthreads();
+    float s[kF32BN];
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < kF32BN; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int c2 = 0; c2 < D; ++c2) acc = __builtin_fmaf(q[c2], Ks[r][c2], acc);
+      s[r] = (tile0 + r <= my_lim) ? acc * cs : kNegInf;
+      mx = fmaxf(mx, s[r]);
+    }
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    l_run *= alpha;
+#pragma unroll
+    for (int c2 = 0; c2 < D; ++c2) o[c2] *= alpha;
+#pragma unroll
+    for (int r = 0; r < kF32BN; ++r) {
+      const float p = fast_exp2(s[r] - m_use);
+      l_run += p;
+#pragma unroll
+      for (int c2 = 0; c2 < D; ++c2) o[c2] = __builtin_fmaf(p, Vs[r][c2], o[c2]);
+    }
+    m_run = m_new;
+  }
+  if (!row_ok) return;
+  const bool fin = w.q_rank >= A.fin_lo && w.q_rank < A.fin_hi;
+  const int64_t idx = q_row_index(A, w, my_row);
+  const RowMerge rm = row_merge(A, idx, m_run, l_run);
+#pragma unroll
+  for (int c2 = 0; c2 < D; c2 += 4) {
+    const float o4[4] = {o[c2], o[c2 + 1], o[c2 + 2], o[c2 + 3]};
+    store_dims4<float>(A, idx, c2, D, fin, rm, o4);
+  }
+  store_row(A, idx, fin, rm);
+}
+
+}  // namespace
+
+int step_block_rows_bf16(int) { return kBM; }
+int step_block_rows_f32(int) { return kF32BM; }
+
+static int grid_size(const StepArgs& a) {
+  return a.n_hosts * a.B * a.H * a.n_qtiles;
+}
+
+hipError_t launch_step_bf16(const StepArgs& a, int d, hipStream_t s) {
+  const int g = grid_size(a);
+  if (g <= 0) return hipSuccess;
+  if (d == 128) {
+    hipLaunchKernelGGL((step_bf16_kernel<128, __bf16>), dim3(g), dim3(kThreads), Lds<128>::BYTES, s, a);
+  } else if (d == 64) {
+    hipLaunchKernelGGL((step_bf16_kernel<64, __bf16>), dim3(g), dim3(kThreads), Lds<64>::BYTES, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_step_f32(const StepArgs& a, int d, hipStream_t s) {
+  const int g = grid_size(a);
+  if (g <= 0) return hipSuccess;
+  if (d == 128) {
+    hipLaunchKernelGGL((step_f32_kernel<128>), dim3(g), dim3(kF32BM), 0, s, a);
+  } else if (d == 64) {
+    hipLaunchKernelGGL((step_f32_kernel<64>), dim3(g), dim3(kF32BM), 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// The bf16 kernel needs more than the default 64 KiB of dynamic LDS.
+hipError_t step_kernel_setup() {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(step_bf16_kernel<128, __bf16>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::BYTES);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(step_bf16_kernel<64, __bf16>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, Lds<64>::BYTES);
+}
+
+}  // namespace ra

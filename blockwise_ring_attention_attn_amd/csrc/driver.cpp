@@ -1,0 +1,700 @@
+// Host side of the ring-attention library: argument checks, the mask-aware
+// step scheduler, the ring-step driver (two HIP streams, events, staging
+// double buffer) and the C ABI of include/ring_attn.h.
+//
+// Pages cited (by title; section named alone):
+//   [TKG] "RingAttention 심층 아키텍처 ..." (techknowgenie.com): §2 sequence
+//         sharding and the KV ring, §4 compute/communication overlap,
+//         §5 the per-rank step loop with a dedicated communication stream and
+//         a double-buffered KV block, §7 causal imbalance and striping.
+//
+// The P ranks of the page are P virtual hosts on one GPU.  The page's
+// send-to-next / receive-from-previous exchange becomes a device-to-device
+// copy on a second stream: at step s host r computes with the kv block of
+// host (r - s) mod P, which sits at host r's own row positions of the
+// staging buffer used at step s; the copy for step s + 1 shifts that buffer
+// by one host into the other staging buffer while step s computes.
+// Ordering (both directions, unlike a one-way wait):
+//   copy(s+1)    waits for compute(s-1)  (it overwrites what step s-1 read)
+//   compute(s)   waits for copy(s)
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "ra_internal.h"
+#include "ring_attn.h"
+
+using namespace ra;
+
+namespace {
+
+thread_local std::string g_err;
+
+ra_status fail(ra_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+ra_status hip_fail(hipError_t e, const char* what) {
+  return fail(RA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define RA_HIP(call, what)                          \
+  do {                                              \
+    hipError_t _e = (call);                         \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+  } while (0)
+
+constexpr int kMaxDevices = 64;
+constexpr int kMaxP = 64;
+constexpr size_t kAlign = 256;
+
+struct DeviceCtx {
+  bool ready = false;
+  std::mutex enqueue;  // one multi-stream call at a time per device (shared events)
+  hipStream_t copy = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t copied[2] = {nullptr, nullptr};
+  hipEvent_t done[2] = {nullptr, nullptr};
+};
+
+std::mutex g_mu;
+DeviceCtx g_dev[kMaxDevices];
+
+ra_status get_ctx(DeviceCtx** out) {
+  int dev = 0;
+  RA_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(RA_EUNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_mu);
+  DeviceCtx& c = g_dev[dev];
+  if (!c.ready) {
+    RA_HIP(hipStreamCreateWithFlags(&c.copy, hipStreamNonBlocking), "hipStreamCreateWithFlags");
+    RA_HIP(hipEventCreateWithFlags(&c.fork, hipEventDisableTiming), "hipEventCreate");
+    RA_HIP(hipEventCreateWithFlags(&c.join, hipEventDisableTiming), "hipEventCreate");
+    for (int i = 0; i < 2; ++i) {
+      RA_HIP(hipEventCreateWithFlags(&c.copied[i], hipEventDisableTiming), "hipEventCreate");
+      RA_HIP(hipEventCreateWithFlags(&c.done[i], hipEventDisableTiming), "hipEventCreate");
+    }
+    RA_HIP(step_kernel_setup(), "hipFuncSetAttribute");
+    c.ready = true;
+  }
+  *out = &c;
+  return RA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Profiling: timing events around the fused step / decode kernels.
+// ---------------------------------------------------------------------------
+struct ProfRec {
+  hipEvent_t a, b;
+  double work;
+  int kind;  // 0 step kernel, 1 decode kernel
+};
+struct Prof {
+  bool on = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  double acc[6] = {0, 0, 0, 0, 0, 0};
+} g_prof;
+
+hipEvent_t prof_event() {
+  if (!g_prof.pool.empty()) {
+    hipEvent_t e = g_prof.pool.back();
+    g_prof.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct ProfScope {
+  hipEvent_t a = nullptr, b = nullptr;
+  hipStream_t s;
+  double work;
+  int kind;
+  ProfScope(hipStream_t st, double w, int k) : s(st), work(w), kind(k) {
+    if (!g_prof.on) return;
+    std::lock_guard<std::mutex> lk(g_mu);
+    a = prof_event();
+    b = prof_event();
+    if (a) hipEventRecord(a, s);
+  }
+  ~ProfScope() {
+    if (!a || !b) return;
+    hipEventRecord(b, s);
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_prof.recs.push_back({a, b, work, kind});
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Scheduler: which query hosts have visible work at a ring step, and the
+// exact number of visible (query, key) pairs of a block pair.
+// ---------------------------------------------------------------------------
+int64_t clamp_prefix(int64_t x, int64_t M) {
+  // F(x) = sum_{t=0}^{x-1} clamp(t, 0, M), F(x) = 0 for x <= 0.
+  if (x <= 0) return 0;
+  if (x <= M + 1) return x * (x - 1) / 2;
+  return M * (M + 1) / 2 + (x - M - 1) * M;
+}
+
+// Visible pairs between query block q_rank (Lq rows) and kv block kv_rank
+// (Lkv rows): query i sees keys j <= lim(i), lim(i) = i + c0 - 1.
+int64_t visible_pairs(int layout, int causal, int P, int q_rank, int kv_rank, int64_t Lq, int64_t Lkv) {
+  (void)P;
+  if (!causal) return Lq * Lkv;
+  int64_t c0 = layout == RA_CONTIGUOUS ? (int64_t)q_rank * Lq - (int64_t)kv_rank * Lkv + 1
+                                       : 1 - (kv_rank > q_rank ? 1 : 0);
+  // sum_{i=0}^{Lq-1} clamp(i + c0, 0, Lkv)
+  return clamp_prefix(c0 + Lq, Lkv) - clamp_prefix(c0, Lkv);
+}
+
+// Does query host q_rank see anything of kv host kv_rank?
+bool pair_active(int layout, int causal, int P, int q_rank, int kv_rank, int64_t Lq, int64_t Lkv) {
+  return visible_pairs(layout, causal, P, q_rank, kv_rank, Lq, Lkv) > 0;
+}
+
+struct StepPlan {
+  int host_lo, n_hosts;  // contiguous range of query hosts with work
+  int fin_lo, fin_hi;    // hosts whose last active step this is
+};
+
+// Hosts r with work at step s (kv = (r - s) mod P).  For a contiguous causal
+// ring these are r = s .. P-1 and host s finishes at step s ([TKG] §7: the
+// later hosts see more of the past); for striped or unmasked rings every host
+// works at every step and all finish at step P-1.
+StepPlan plan_step(int layout, int causal, int P, int s, int64_t Bl) {
+  StepPlan p{0, 0, 0, 0};
+  int lo = -1, hi = -1;
+  for (int r = 0; r < P; ++r) {
+    const int kv = ((r - s) % P + P) % P;
+    if (pair_active(layout, causal, P, r, kv, Bl, Bl)) {
+      if (lo < 0) lo = r;
+      hi = r;
+    }
+  }
+  if (lo < 0) return p;
+  p.host_lo = lo;
+  p.n_hosts = hi - lo + 1;
+  // last active step of each host in [lo, hi]
+  int flo = P, fhi = -1;
+  for (int r = lo; r <= hi; ++r) {
+    int last = -1;
+    for (int t = 0; t < P; ++t) {
+      const int kv = ((r - t) % P + P) % P;
+      if (pair_active(layout, causal, P, r, kv, Bl, Bl)) last = t;
+    }
+    if (last == s) {
+      if (r < flo) flo = r;
+      if (r > fhi) fhi = r;
+    }
+  }
+  if (fhi >= flo) {
+    p.fin_lo = flo;
+    p.fin_hi = fhi + 1;
+  }
+  return p;
+}
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+size_t esize(ra_dtype t) { return t == RA_BF16 ? 2 : 4; }
+
+bool dtype_ok(int t) { return t == RA_F32 || t == RA_BF16; }
+bool layout_ok(int l) { return l == RA_CONTIGUOUS || l == RA_STRIPED; }
+
+ra_status check_common(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype, float scale) {
+  if (B < 1 || H < 1 || Hkv < 1) return fail(RA_EINVAL, "B, H, Hkv must be >= 1 (got %d, %d, %d)", B, H, Hkv);
+  if (H % Hkv) return fail(RA_EINVAL, "H (%d) must be a multiple of Hkv (%d)", H, Hkv);
+  if (d != 64 && d != 128) return fail(RA_EINVAL, "head dim d must be 64 or 128 (got %d)", d);
+  if (P < 1 || P > kMaxP) return fail(RA_EINVAL, "P must be in [1, %d] (got %d)", kMaxP, P);
+  if (N < 1) return fail(RA_EINVAL, "N must be >= 1");
+  if (N % P) return fail(RA_EINVAL, "N (%lld) must be a multiple of P (%d)", N, P);
+  if (N / P > (1LL << 30)) return fail(RA_EINVAL, "block length N/P too large");
+  if (!dtype_ok(dtype)) return fail(RA_EINVAL, "unknown dtype %d", (int)dtype);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(RA_EINVAL, "scale must be finite and > 0");
+  return RA_OK;
+}
+
+struct FwdWs {
+  size_t stage_bytes;  // one staging buffer (K and V)
+  size_t kv_bytes;     // K (or V) part of a staging buffer
+  size_t off_stage[2], off_m, off_l, off_o, total;
+};
+
+FwdWs fwd_ws_layout(int B, int H, int Hkv, long long Nq, long long Nkv_stage, int d, int P, ra_dtype dtype) {
+  FwdWs w{};
+  if (P == 1) return w;  // single block: no staging, no state
+  w.kv_bytes = align_up((size_t)B * Hkv * Nkv_stage * d * esize(dtype));
+  w.stage_bytes = 2 * w.kv_bytes;
+  size_t off = 0;
+  w.off_stage[0] = off; off += w.stage_bytes;
+  w.off_stage[1] = off; off += w.stage_bytes;
+  w.off_m = off; off += align_up((size_t)B * H * Nq * 4);
+  w.off_l = off; off += align_up((size_t)B * H * Nq * 4);
+  w.off_o = off; off += align_up((size_t)B * H * Nq * d * 4);
+  w.total = off;
+  return w;
+}
+
+hipError_t launch_step(const StepArgs& a, int d, ra_dtype dtype, hipStream_t s, double flops) {
+  ProfScope ps(s, flops, 0);
+  return dtype == RA_BF16 ? launch_step_bf16(a, d, s) : launch_step_f32(a, d, s);
+}
+
+int block_rows(ra_dtype dtype, int d) {
+  return dtype == RA_BF16 ? step_block_rows_bf16(d) : step_block_rows_f32(d);
+}
+
+double step_flops(const StepArgs& a, int d) {
+  if (!g_prof.on) return 0.0;
+  double pairs = 0;
+  for (int i = 0; i < a.n_hosts; ++i) {
+    const int qr = a.host_lo + i;
+    const int kr = ((qr - a.kv_shift) % a.P + a.P) % a.P;
+    pairs += (double)visible_pairs(a.layout, a.causal, a.P, qr, kr, a.Lq, a.Lkv);
+  }
+  return 4.0 * d * pairs * a.B * a.H;
+}
+
+// Staging copy helpers (2-D copies on the copy stream).
+hipError_t copy2d(void* dst, size_t dpitch, const void* src, size_t spitch, size_t width, size_t height,
+                  hipStream_t s) {
+  if (width == 0 || height == 0) return hipSuccess;
+  return hipMemcpy2DAsync(dst, dpitch, src, spitch, width, height, hipMemcpyDeviceToDevice, s);
+}
+
+// dst <- src shifted by one host (host r receives host r-1's block), both in
+// natural row order [planes, N, d].
+hipError_t ring_shift(void* dst, const void* src, int layout, int64_t planes, int64_t N, int64_t Bl,
+                      int P, size_t row_bytes, hipStream_t s) {
+  char* D = static_cast<char*>(dst);
+  const char* S = static_cast<const char*>(src);
+  hipError_t e;
+  if (layout == RA_CONTIGUOUS) {
+    const size_t plane = (size_t)N * row_bytes;
+    // rows [Bl, N) <- [0, N - Bl);  rows [0, Bl) <- [N - Bl, N)
+    e = copy2d(D + Bl * row_bytes, plane, S, plane, (size_t)(N - Bl) * row_bytes, planes, s);
+    if (e != hipSuccess) return e;
+    return copy2d(D, plane, S + (N - Bl) * row_bytes, plane, (size_t)Bl * row_bytes, planes, s);
+  }
+  // striped: within every group of P consecutive rows, row r <- row r-1, row 0 <- row P-1
+  const size_t grp = (size_t)P * row_bytes;
+  const size_t groups = (size_t)planes * Bl;
+  e = copy2d(D + row_bytes, grp, S, grp, (size_t)(P - 1) * row_bytes, groups, s);
+  if (e != hipSuccess) return e;
+  return copy2d(D, grp, S + (size_t)(P - 1) * row_bytes, grp, row_bytes, groups, s);
+}
+
+// dst (compact [planes, Bl, d]) <- block `kv` of src (natural [planes, N, d]).
+hipError_t gather_block(void* dst, const void* src, int layout, int64_t planes, int64_t N, int64_t Bl,
+                        int P, int kv, size_t row_bytes, hipStream_t s) {
+  char* D = static_cast<char*>(dst);
+  const char* S = static_cast<const char*>(src);
+  if (layout == RA_CONTIGUOUS) {
+    return copy2d(D, (size_t)Bl * row_bytes, S + (size_t)kv * Bl * row_bytes, (size_t)N * row_bytes,
+                  (size_t)Bl * row_bytes, planes, s);
+  }
+  return copy2d(D, row_bytes, S + (size_t)kv * row_bytes, (size_t)P * row_bytes, row_bytes,
+                (size_t)planes * Bl, s);
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char* ra_last_error(void) { return g_err.c_str(); }
+const char* ra_version(void) { return "ring_attn 0.1 gfx950"; }
+
+size_t ring_attn_fwd_ws_bytes(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype) {
+  if (B < 1 || H < 1 || Hkv < 1 || P < 1 || N < 1 || N % P) return 0;
+  return fwd_ws_layout(B, H, Hkv, N, N, d, P, dtype).total;
+}
+
+size_t ring_attn_fwd_share_ws_bytes(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype) {
+  if (B < 1 || H < 1 || Hkv < 1 || P < 1 || N < 1 || N % P) return 0;
+  return fwd_ws_layout(B, H, Hkv, N / P, N / P, d, P, dtype).total;
+}
+
+ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                        int Hkv, long long N, int d, int P, int causal, ra_layout layout, float scale,
+                        ra_dtype dtype, void* stream, void* ws, size_t ws_bytes) {
+  g_err.clear();
+  if (!q || !k || !v || !out || !lse) return fail(RA_EINVAL, "null tensor pointer");
+  ra_status st = check_common(B, H, Hkv, N, d, P, dtype, scale);
+  if (st != RA_OK) return st;
+  if (!layout_ok(layout)) return fail(RA_EINVAL, "unknown layout %d", (int)layout);
+  const FwdWs W = fwd_ws_layout(B, H, Hkv, N, N, d, P, dtype);
+  if (ws_bytes < W.total) return fail(RA_EINVAL, "workspace too small: need %zu bytes, got %zu", W.total, ws_bytes);
+  if (W.total && !ws) return fail(RA_EINVAL, "null workspace");
+  if (W.total && (reinterpret_cast<uintptr_t>(ws) % kAlign)) return fail(RA_EINVAL, "workspace must be 256-byte aligned");
+  const int64_t Bl = N / P;
+  const int BM = block_rows(dtype, d);
+  const int64_t nqt = (Bl + BM - 1) / BM;
+  if ((int64_t)P * B * H * nqt > 0x7fffffffLL) return fail(RA_EINVAL, "problem too large for one launch");
+  DeviceCtx* ctx = nullptr;
+  if ((st = get_ctx(&ctx)) != RA_OK) return st;
+  std::lock_guard<std::mutex> enq(ctx->enqueue);
+  hipStream_t cs = static_cast<hipStream_t>(stream);
+  const size_t row_bytes = (size_t)d * esize(dtype);
+  char* wsb = static_cast<char*>(ws);
+
+  StepArgs a{};
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.q_plane_rows = N;
+  a.kv_plane_rows = N;
+  a.B = B; a.H = H; a.Hkv = Hkv;
+  a.Lq = (int)Bl; a.Lkv = (int)Bl;
+  a.P = P;
+  a.layout = layout;
+  a.q_mode = ROWS_HOST_Q;
+  a.kv_mode = ROWS_HOST_Q;
+  a.causal = causal ? 1 : 0;
+  a.n_qtiles = (int)nqt;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  if (P > 1) {
+    a.m = reinterpret_cast<float*>(wsb + W.off_m);
+    a.l = reinterpret_cast<float*>(wsb + W.off_l);
+    a.o = reinterpret_cast<float*>(wsb + W.off_o);
+  }
+
+  auto kbuf = [&](int s) -> const void* {
+    return s == 0 ? k : static_cast<const void*>(wsb + W.off_stage[s & 1]);
+  };
+  auto vbuf = [&](int s) -> const void* {
+    return s == 0 ? v : static_cast<const void*>(wsb + W.off_stage[s & 1] + W.kv_bytes);
+  };
+
+  if (P > 1) {
+    RA_HIP(hipEventRecord(ctx->fork, cs), "hipEventRecord");
+    RA_HIP(hipStreamWaitEvent(ctx->copy, ctx->fork, 0), "hipStreamWaitEvent");
+  }
+  for (int s = 0; s < P; ++s) {
+    // Copy stream: stage the blocks of step s + 1 while step s computes.
+    if (s + 1 < P) {
+      if (s >= 1) RA_HIP(hipStreamWaitEvent(ctx->copy, ctx->done[(s - 1) & 1], 0), "hipStreamWaitEvent");
+      void* kd = wsb + W.off_stage[(s + 1) & 1];
+      void* vd = wsb + W.off_stage[(s + 1) & 1] + W.kv_bytes;
+      RA_HIP(ring_shift(kd, kbuf(s), layout, (int64_t)B * Hkv, N, Bl, P, row_bytes, ctx->copy), "staging copy");
+      RA_HIP(ring_shift(vd, vbuf(s), layout, (int64_t)B * Hkv, N, Bl, P, row_bytes, ctx->copy), "staging copy");
+      RA_HIP(hipEventRecord(ctx->copied[(s + 1) & 1], ctx->copy), "hipEventRecord");
+    }
+    // Compute stream: step s.
+    if (s >= 1) RA_HIP(hipStreamWaitEvent(cs, ctx->copied[s & 1], 0), "hipStreamWaitEvent");
+    const StepPlan sp = plan_step(layout, a.causal, P, s, Bl);
+    a.k = kbuf(s);
+    a.v = vbuf(s);
+    a.host_lo = sp.host_lo;
+    a.n_hosts = sp.n_hosts;
+    a.kv_shift = s;
+    a.has_prev = s > 0 ? 1 : 0;
+    a.fin_lo = sp.fin_lo;
+    a.fin_hi = sp.fin_hi;
+    if (sp.n_hosts > 0) RA_HIP(launch_step(a, d, dtype, cs, step_flops(a, d)), "step kernel launch");
+    if (s + 2 < P) RA_HIP(hipEventRecord(ctx->done[s & 1], cs), "hipEventRecord");
+  }
+  return RA_OK;
+}
+
+ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                              int H, int Hkv, long long N, int d, int P, int rank, int causal,
+                              ra_layout layout, float scale, ra_dtype dtype, void* stream, void* ws,
+                              size_t ws_bytes) {
+  g_err.clear();
+  if (!q || !k || !v || !out || !lse) return fail(RA_EINVAL, "null tensor pointer");
+  ra_status st = check_common(B, H, Hkv, N, d, P, dtype, scale);
+  if (st != RA_OK) return st;
+  if (!layout_ok(layout)) return fail(RA_EINVAL, "unknown layout %d", (int)layout);
+  if (rank < 0 || rank >= P) return fail(RA_EINVAL, "rank %d out of [0, %d)", rank, P);
+  const int64_t Bl = N / P;
+  const FwdWs W = fwd_ws_layout(B, H, Hkv, Bl, Bl, d, P, dtype);
+  if (ws_bytes < W.total) return fail(RA_EINVAL, "workspace too small: need %zu bytes, got %zu", W.total, ws_bytes);
+  if (W.total && !ws) return fail(RA_EINVAL, "null workspace");
+  if (W.total && (reinterpret_cast<uintptr_t>(ws) % kAlign)) return fail(RA_EINVAL, "workspace must be 256-byte aligned");
+  const int BM = block_rows(dtype, d);
+  const int64_t nqt = (Bl + BM - 1) / BM;
+  if ((int64_t)B * H * nqt > 0x7fffffffLL) return fail(RA_EINVAL, "problem too large for one launch");
+  DeviceCtx* ctx = nullptr;
+  if ((st = get_ctx(&ctx)) != RA_OK) return st;
+  std::lock_guard<std::mutex> enq(ctx->enqueue);
+  hipStream_t cs = static_cast<hipStream_t>(stream);
+  const size_t row_bytes = (size_t)d * esize(dtype);
+  char* wsb = static_cast<char*>(ws);
+
+  // Steps with visible work, in ring order.
+  std::vector<int> steps;
+  for (int s = 0; s < P; ++s) {
+    const int kv = ((rank - s) % P + P) % P;
+    if (pair_active(layout, causal ? 1 : 0, P, rank, kv, Bl, Bl)) steps.push_back(s);
+  }
+
+  StepArgs a{};
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.q_plane_rows = Bl;
+  a.B = B; a.H = H; a.Hkv = Hkv;
+  a.Lq = (int)Bl; a.Lkv = (int)Bl;
+  a.P = P;
+  a.layout = layout;
+  a.q_mode = ROWS_COMPACT;
+  a.causal = causal ? 1 : 0;
+  a.n_qtiles = (int)nqt;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.host_lo = rank;
+  a.n_hosts = 1;
+  if (P > 1) {
+    a.m = reinterpret_cast<float*>(wsb + W.off_m);
+    a.l = reinterpret_cast<float*>(wsb + W.off_l);
+    a.o = reinterpret_cast<float*>(wsb + W.off_o);
+  }
+  const int n = (int)steps.size();
+  if (n > 1) {
+    RA_HIP(hipEventRecord(ctx->fork, cs), "hipEventRecord");
+    RA_HIP(hipStreamWaitEvent(ctx->copy, ctx->fork, 0), "hipStreamWaitEvent");
+  }
+  // Step index i uses staging buffer i & 1 (i >= 1); the first step reads
+  // its block in place from the natural-order k / v.
+  for (int i = 0; i < n; ++i) {
+    const int s = steps[i];
+    if (i + 1 < n) {
+      const int s1 = steps[i + 1];
+      const int kv1 = ((rank - s1) % P + P) % P;
+      if (i >= 1) RA_HIP(hipStreamWaitEvent(ctx->copy, ctx->done[(i - 1) & 1], 0), "hipStreamWaitEvent");
+      void* kd = wsb + W.off_stage[(i + 1) & 1];
+      void* vd = wsb + W.off_stage[(i + 1) & 1] + W.kv_bytes;
+      RA_HIP(gather_block(kd, k, layout, (int64_t)B * Hkv, N, Bl, P, kv1, row_bytes, ctx->copy), "staging copy");
+      RA_HIP(gather_block(vd, v, layout, (int64_t)B * Hkv, N, Bl, P, kv1, row_bytes, ctx->copy), "staging copy");
+      RA_HIP(hipEventRecord(ctx->copied[(i + 1) & 1], ctx->copy), "hipEventRecord");
+    }
+    if (i >= 1) RA_HIP(hipStreamWaitEvent(cs, ctx->copied[i & 1], 0), "hipStreamWaitEvent");
+    if (i == 0) {
+      a.k = k;
+      a.v = v;
+      a.kv_mode = ROWS_HOST_KV;
+      a.kv_plane_rows = N;
+    } else {
+      a.k = wsb + W.off_stage[i & 1];
+      a.v = wsb + W.off_stage[i & 1] + W.kv_bytes;
+      a.kv_mode = ROWS_COMPACT;
+      a.kv_plane_rows = Bl;
+    }
+    a.kv_shift = s;
+    a.has_prev = i > 0 ? 1 : 0;
+    a.fin_lo = (i == n - 1) ? rank : 0;
+    a.fin_hi = (i == n - 1) ? rank + 1 : 0;
+    RA_HIP(launch_step(a, d, dtype, cs, step_flops(a, d)), "step kernel launch");
+    if (i + 2 < n) RA_HIP(hipEventRecord(ctx->done[i & 1], cs), "hipEventRecord");
+  }
+  if (n == 0) {
+    // Nothing visible (cannot happen for a causal ring: a host sees itself).
+    return fail(RA_EINVAL, "no visible keys for rank %d", rank);
+  }
+  return RA_OK;
+}
+
+ra_status ring_attn_step(const void* q_blk, ra_kv_block kv_blk, float* m, float* l, float* o,
+                         const ra_mask_desc* md, void* stream) {
+  g_err.clear();
+  if (!md) return fail(RA_EINVAL, "null mask_desc");
+  if (!q_blk || !kv_blk.k || !kv_blk.v || !m || !l || !o) return fail(RA_EINVAL, "null tensor pointer");
+  if (md->B < 1 || md->H < 1 || md->Hkv < 1 || md->H % md->Hkv)
+    return fail(RA_EINVAL, "bad head counts B=%d H=%d Hkv=%d", md->B, md->H, md->Hkv);
+  if (md->d != 64 && md->d != 128) return fail(RA_EINVAL, "head dim d must be 64 or 128 (got %d)", md->d);
+  if (md->Lq < 1 || md->Lkv < 1 || md->Lq > (1LL << 30) || md->Lkv > (1LL << 30))
+    return fail(RA_EINVAL, "block lengths must be in [1, 2^30]");
+  if (!dtype_ok(md->dtype)) return fail(RA_EINVAL, "unknown dtype %d", (int)md->dtype);
+  if (!layout_ok(md->layout)) return fail(RA_EINVAL, "unknown layout %d", (int)md->layout);
+  if (md->P < 1 || md->P > kMaxP || md->q_rank < 0 || md->q_rank >= md->P || md->kv_rank < 0 ||
+      md->kv_rank >= md->P)
+    return fail(RA_EINVAL, "bad ring description P=%d q_rank=%d kv_rank=%d", md->P, md->q_rank, md->kv_rank);
+  if (md->layout == RA_STRIPED && md->causal && md->Lq != md->Lkv)
+    return fail(RA_EINVAL, "striped causal blocks must have Lq == Lkv");
+  if (!(md->scale > 0.f) || !std::isfinite(md->scale)) return fail(RA_EINVAL, "scale must be finite and > 0");
+  const int BM = block_rows(md->dtype, md->d);
+  const int64_t nqt = (md->Lq + BM - 1) / BM;
+  if ((int64_t)md->B * md->H * nqt > 0x7fffffffLL) return fail(RA_EINVAL, "problem too large for one launch");
+  if (!pair_active(md->layout, md->causal, md->P, md->q_rank, md->kv_rank, md->Lq, md->Lkv)) return RA_OK;
+  DeviceCtx* ctx = nullptr;
+  ra_status st = get_ctx(&ctx);
+  if (st != RA_OK) return st;
+  StepArgs a{};
+  a.q = q_blk;
+  a.k = kv_blk.k;
+  a.v = kv_blk.v;
+  a.m = m; a.l = l; a.o = o;
+  a.q_plane_rows = md->Lq;
+  a.kv_plane_rows = md->Lkv;
+  a.B = md->B; a.H = md->H; a.Hkv = md->Hkv;
+  a.Lq = (int)md->Lq; a.Lkv = (int)md->Lkv;
+  a.P = md->P;
+  a.layout = md->layout;
+  a.host_lo = md->q_rank;
+  a.n_hosts = 1;
+  a.kv_shift = md->q_rank - md->kv_rank;
+  a.q_mode = ROWS_COMPACT;
+  a.kv_mode = ROWS_COMPACT;
+  a.causal = md->causal ? 1 : 0;
+  a.has_prev = 1;
+  a.fin_lo = a.fin_hi = 0;
+  a.n_qtiles = (int)nqt;
+  a.scale_log2 = md->scale * 1.4426950408889634f;
+  RA_HIP(launch_step(a, md->d, md->dtype, static_cast<hipStream_t>(stream), step_flops(a, md->d)),
+         "step kernel launch");
+  return RA_OK;
+}
+
+ra_status ring_attn_finalize(const float* m, const float* l, const float* o, void* out, float* lse,
+                             long long rows, int d, ra_dtype out_dtype, void* stream) {
+  g_err.clear();
+  if (!m || !l || !o || !out || !lse) return fail(RA_EINVAL, "null tensor pointer");
+  if (rows < 0 || d < 1 || d > 1024) return fail(RA_EINVAL, "bad rows/d");
+  if (!dtype_ok(out_dtype)) return fail(RA_EINVAL, "unknown dtype %d", (int)out_dtype);
+  FinalizeArgs a{m, l, o, out, lse, rows, d};
+  RA_HIP(launch_finalize(a, out_dtype == RA_BF16, static_cast<hipStream_t>(stream)), "finalize launch");
+  return RA_OK;
+}
+
+ra_status lse_merge(float* o_a, float* lse_a, const float* o_b, const float* lse_b, long long rows, int d,
+                    void* stream) {
+  g_err.clear();
+  if (!o_a || !lse_a || !o_b || !lse_b) return fail(RA_EINVAL, "null tensor pointer");
+  if (rows < 0 || d < 1 || d > 1024) return fail(RA_EINVAL, "bad rows/d");
+  MergeArgs a{o_a, lse_a, o_b, lse_b, rows, d};
+  RA_HIP(launch_lse_merge(a, static_cast<hipStream_t>(stream)), "lse_merge launch");
+  return RA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+constexpr int kDecodeTargetWgs = 4096;
+constexpr int kDecodeWaves = 4;
+constexpr int64_t kDecodeQuantum = 128;  // keys per workgroup iteration (4 waves x 32)
+
+void decode_split(int B, int Hkv, long long L, int P, int64_t* chunk, int* cpb) {
+  const int64_t block = L / P;
+  int64_t c = (kDecodeTargetWgs + (int64_t)B * Hkv * P - 1) / ((int64_t)B * Hkv * P);
+  if (c < 1) c = 1;
+  int64_t ch = (block + c - 1) / c;
+  ch = (ch + kDecodeQuantum - 1) / kDecodeQuantum * kDecodeQuantum;
+  if (ch < kDecodeQuantum) ch = kDecodeQuantum;
+  *chunk = ch;
+  *cpb = (int)((block + ch - 1) / ch);
+}
+}  // namespace
+
+extern "C" {
+
+size_t ring_attn_decode_ws_bytes(int B, int H, int Hkv, long long L, int d, int P) {
+  if (B < 1 || H < 1 || Hkv < 1 || P < 1 || L < 1 || L % P || d < 1) return 0;
+  int64_t chunk;
+  int cpb;
+  decode_split(B, Hkv, L, P, &chunk, &cpb);
+  const int64_t S = (int64_t)P * cpb * kDecodeWaves;
+  return align_up((size_t)B * H * S * d * 4) + align_up((size_t)B * H * S * 4);
+}
+
+ra_status ring_attn_decode(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                           int Hkv, long long L, int d, int P, float scale, ra_dtype dtype, void* stream,
+                           void* ws, size_t ws_bytes) {
+  g_err.clear();
+  if (!q || !k || !v || !out || !lse) return fail(RA_EINVAL, "null tensor pointer");
+  ra_status st = check_common(B, H, Hkv, L, d, P, dtype, scale);
+  if (st != RA_OK) return st;
+  if (dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "decode supports bf16 only");
+  if (H / Hkv > 16) return fail(RA_EINVAL, "H/Hkv must be <= 16 (got %d)", H / Hkv);
+  const size_t need = ring_attn_decode_ws_bytes(B, H, Hkv, L, d, P);
+  if (ws_bytes < need) return fail(RA_EINVAL, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
+  if (!ws) return fail(RA_EINVAL, "null workspace");
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(RA_EINVAL, "workspace must be 256-byte aligned");
+  int64_t chunk;
+  int cpb;
+  decode_split(B, Hkv, L, P, &chunk, &cpb);
+  if ((int64_t)B * Hkv * P * cpb > 0x7fffffffLL) return fail(RA_EINVAL, "problem too large");
+  DeviceCtx* ctx = nullptr;
+  if ((st = get_ctx(&ctx)) != RA_OK) return st;
+  DecodeArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.S = P * cpb * kDecodeWaves;
+  char* wsb = static_cast<char*>(ws);
+  a.o_part = reinterpret_cast<float*>(wsb);
+  a.lse_part = reinterpret_cast<float*>(wsb + align_up((size_t)B * H * a.S * d * 4));
+  a.out = out; a.lse = lse;
+  a.B = B; a.H = H; a.Hkv = Hkv; a.group = H / Hkv;
+  a.L = L;
+  a.chunk = chunk;
+  a.block = L / P;
+  a.chunks_per_block = cpb;
+  a.P = P;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipStream_t cs = static_cast<hipStream_t>(stream);
+  {
+    const double bytes = 2.0 * B * Hkv * (double)L * d * 2 + (double)B * H * d * 2 +
+                         (double)B * H * a.S * (d + 1) * 4;
+    ProfScope ps(cs, bytes, 1);
+    RA_HIP(launch_decode_partial(a, d, 1, cs), "decode partial launch");
+  }
+  RA_HIP(launch_decode_merge(a, d, 1, cs), "decode merge launch");
+  return RA_OK;
+}
+
+ra_status ra_prof_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_prof.on = on != 0;
+  return RA_OK;
+}
+
+ra_status ra_prof_reset(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  for (auto& r : g_prof.recs) {
+    hipEventSynchronize(r.b);
+    g_prof.pool.push_back(r.a);
+    g_prof.pool.push_back(r.b);
+  }
+  g_prof.recs.clear();
+  for (double& x : g_prof.acc) x = 0;
+  return RA_OK;
+}
+
+ra_status ra_prof_read(double* out6) {
+  if (!out6) return fail(RA_EINVAL, "null output");
+  std::lock_guard<std::mutex> lk(g_mu);
+  for (auto& r : g_prof.recs) {
+    RA_HIP(hipEventSynchronize(r.b), "hipEventSynchronize");
+    float ms = 0.f;
+    RA_HIP(hipEventElapsedTime(&ms, r.a, r.b), "hipEventElapsedTime");
+    if (r.kind == 0) {
+      g_prof.acc[0] += ms;
+      g_prof.acc[1] += 1;
+      g_prof.acc[4] += r.work;
+    } else {
+      g_prof.acc[2] += ms;
+      g_prof.acc[3] += 1;
+      g_prof.acc[5] += r.work;
+    }
+    g_prof.pool.push_back(r.a);
+    g_prof.pool.push_back(r.b);
+  }
+  g_prof.recs.clear();
+  for (int i = 0; i < 6; ++i) out6[i] = g_prof.acc[i];
+  return RA_OK;
+}
+
+}  // extern "C"

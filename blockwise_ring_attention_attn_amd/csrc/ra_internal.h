@@ -1,0 +1,82 @@
+// Internal types shared by the host driver and the HIP kernels.
+// Not part of the public ABI (see include/ring_attn.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+// How a row index inside a host block maps to a row of the backing array.
+enum RowMode : int {
+  ROWS_COMPACT = 0,   // row = i                        (a compact block)
+  ROWS_HOST_Q = 1,    // row = host_row(q_rank, i)      (natural order array)
+  ROWS_HOST_KV = 2,   // row = host_row(kv_rank, i)     (natural order array)
+};
+
+// One launch of the fused block-attention step kernel.  A launch covers
+// `n_hosts` query hosts q_rank = host_lo .. host_lo + n_hosts - 1, each
+// against the kv block of host kv_rank = (q_rank - kv_shift) mod P.
+struct StepArgs {
+  const void* q;        // element type per kernel instantiation
+  const void* k;
+  const void* v;
+  float* m;             // state rows follow q's row mode / plane
+  float* l;
+  float* o;
+  void* out;            // final output (element type), same rows as q
+  float* lse;
+  int64_t q_plane_rows;   // rows per (b, h) plane of q / out / state
+  int64_t kv_plane_rows;  // rows per (b, hkv) plane of k / v
+  int B, H, Hkv;
+  int Lq, Lkv;            // rows per host block (query / key)
+  int P;
+  int layout;             // 0 contiguous, 1 striped
+  int host_lo, n_hosts;
+  int kv_shift;           // kv_rank = (q_rank - kv_shift) mod P
+  int q_mode;             // RowMode for q / out / state (COMPACT or HOST_Q)
+  int kv_mode;            // RowMode for k / v
+  int causal;
+  int has_prev;           // merge with the state already in (m, l, o)
+  int fin_lo, fin_hi;     // query hosts in [fin_lo, fin_hi) finalize (write out / lse);
+                          // the others store the fp32 state
+  int n_qtiles;           // ceil(Lq / BM)
+  float scale_log2;       // scale * log2(e)
+};
+
+struct MergeArgs {
+  float* o_a; float* lse_a; const float* o_b; const float* lse_b;
+  int64_t rows; int d;
+};
+
+struct FinalizeArgs {
+  const float* m; const float* l; const float* o; void* out; float* lse;
+  int64_t rows; int d;
+};
+
+// Split-KV decode: partial pass writes one normalized (O, lse) per
+// (b, h, split); splits are ordered ring block major, chunk minor.
+struct DecodeArgs {
+  const void* q; const void* k; const void* v;
+  float* o_part;          // [B, H, S, d]
+  float* lse_part;        // [B, H, S]
+  void* out; float* lse;  // [B, H, d], [B, H]
+  int B, H, Hkv, group;
+  int64_t L;              // keys per sequence
+  int64_t chunk;          // keys per split (last split of a ring block may be shorter)
+  int64_t block;          // keys per ring block (L / P)
+  int chunks_per_block, P, S;
+  float scale_log2;
+};
+
+// Launchers (return hipError_t of the launch).
+hipError_t step_kernel_setup();   // once per device, before the first launch
+hipError_t launch_step_bf16(const StepArgs& a, int d, hipStream_t s);
+hipError_t launch_step_f32(const StepArgs& a, int d, hipStream_t s);
+int step_block_rows_bf16(int d);  // BM of the bf16 kernel
+int step_block_rows_f32(int d);   // BM of the f32 kernel
+hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_finalize(const FinalizeArgs& a, int out_bf16, hipStream_t s);
+hipError_t launch_decode_partial(const DecodeArgs& a, int d, int bf16, hipStream_t s);
+hipError_t launch_decode_merge(const DecodeArgs& a, int d, int bf16, hipStream_t s);
+
+}  // namespace ra

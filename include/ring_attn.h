@@ -1,0 +1,198 @@
+/*
+ * ring_attn.h -- C ABI of the MI355X (gfx950) blockwise ring-attention library.
+ *
+ * Pages cited (by title; the section, equation or table is named alone):
+ *   [TKG] "RingAttention 심층 아키텍처: 통신-연산 완전 중첩과 블록 단위 온라인
+ *         소프트맥스로 1,000만 토큰 컨텍스트를 정복한 분산 어텐션 엔지니어링"
+ *         (techknowgenie.com).
+ *   [AIT] FlashAttention video summary (aitrends.kr).
+ *   [CML] RingAttention paper newsletter (cmlonder.com, "Makale Bülteni").
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensors are row-major and contiguous, in natural token order:
+ *      q, out  [B, H,   Nq, d]   (element type `dtype`)
+ *      k, v    [B, Hkv, N,  d]   (element type `dtype`)
+ *      lse     [B, H,   Nq]      float32, natural log of the scaled logits
+ *    Query head h reads kv head floor(h * Hkv / H) (grouped-query attention,
+ *    consecutive groups).  d must be 64 or 128.
+ *  - All pointers named q, k, v, out, lse, m, l, o, ws are DEVICE pointers
+ *    owned by the caller; the library never allocates device memory inside a
+ *    call and never frees caller memory.  Scratch state lives in `ws`, a
+ *    caller-allocated device workspace of at least the size reported by the
+ *    matching *_ws_bytes() query, aligned to 256 bytes.
+ *  - `stream` is a hipStream_t (passed as void*; NULL = the null stream).
+ *    Every call is asynchronous with respect to the host.  Calls that use a
+ *    second stream internally fork it from `stream` and join it back before
+ *    returning, so callers see ordinary single-stream semantics.
+ *  - Errors: a call returns RA_OK or an error code BEFORE launching anything
+ *    when an argument is invalid (RA_EINVAL: null pointer, N % P != 0,
+ *    H % Hkv != 0, unsupported d, workspace too small, ...).  A failed HIP
+ *    runtime call returns RA_EHIP.  ra_last_error() then gives a message
+ *    (thread-local).  Faults inside kernels surface at the caller's next
+ *    synchronization, as with any HIP kernel.  No call aborts the process.
+ */
+#ifndef RING_ATTN_H
+#define RING_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { RA_OK = 0, RA_EINVAL = 1, RA_ENOMEM = 2, RA_EHIP = 3, RA_EUNSUPPORTED = 4 } ra_status;
+
+/* Which tokens each of the P virtual hosts owns ([TKG] §2 sequence sharding,
+ * §7 round-robin striping):
+ *   RA_CONTIGUOUS: host r owns tokens r*Bl .. r*Bl + Bl - 1   (Bl = N / P)
+ *   RA_STRIPED:    host r owns tokens r, r + P, r + 2P, ...                */
+typedef enum { RA_CONTIGUOUS = 0, RA_STRIPED = 1 } ra_layout;
+
+/* Element type of q, k, v and out.  RA_BF16: bfloat16 inputs, bf16 MFMA
+ * products with fp32 accumulation.  RA_F32: float32 throughout.          */
+typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
+
+/* ------------------------------------------------------------------------
+ * ring_attn_fwd -- full attention by the ring method over P virtual hosts
+ * that share this GPU ([TKG] §2-§5).
+ *
+ * Host r keeps its query block resident and, at ring step s = 0..P-1,
+ * attends to the key/value block of host (r - s) mod P ([TKG] §5: every
+ * host sends to (r + 1) mod P and receives from (r - 1) mod P).  Each step
+ * fuses S = Q K^T * scale, the causal mask, the online-softmax update of the
+ * running row max m and row sum l with rescaling of the output accumulator,
+ * and the P V product ([TKG] §3, equations S, m_block, m_new, alpha, l_new,
+ * O_new); the last step normalizes (O_final = O / l) and writes lse = m +
+ * ln l.  The next step's key/value blocks are moved into a staging buffer
+ * on a second stream while the current step computes ([TKG] §4 overlap).
+ *
+ * causal: key j is visible to query i iff pos(j) <= pos(i) on global token
+ * positions ([TKG] §7); 0 = no mask.  layout only decides which tokens each
+ * host owns; inputs and outputs stay in natural order, so the result does
+ * not depend on layout or P (up to rounding).  scale: usually 1/sqrt(d)
+ * ([TKG] §3 equation S).  Requires N % P == 0 and 1 <= P <= 64.
+ * ws: at least ring_attn_fwd_ws_bytes(...) bytes.
+ * ---------------------------------------------------------------------- */
+size_t ring_attn_fwd_ws_bytes(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype);
+ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                        int B, int H, int Hkv, long long N, int d, int P, int causal,
+                        ra_layout layout, float scale, ra_dtype dtype, void* stream,
+                        void* ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------
+ * ring_attn_fwd_share -- one device's share of a P-host ring: the query
+ * block of host `rank` against all P key/value blocks, visited in ring order
+ * rank, rank-1, ..., rank-P+1 (mod P), each next block staged on a second
+ * stream while the current one computes ([TKG] §2, §5).
+ *
+ * q, out [B, H, N/P, d] hold the rank's Nq = N/P query tokens (in the order
+ * the layout gives them: contiguous r*Bl + i, striped i*P + r); lse is
+ * [B, H, N/P].  k, v [B, Hkv, N, d] hold the whole sequence in natural
+ * order (the blocks the other hosts would send).  ws: at least
+ * ring_attn_fwd_share_ws_bytes(...) bytes.
+ * ---------------------------------------------------------------------- */
+size_t ring_attn_fwd_share_ws_bytes(int B, int H, int Hkv, long long N, int d, int P,
+                                    ra_dtype dtype);
+ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void* out, float* lse,
+                              int B, int H, int Hkv, long long N, int d, int P, int rank,
+                              int causal, ra_layout layout, float scale, ra_dtype dtype,
+                              void* stream, void* ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------
+ * ring_attn_step -- one ring step for one (query block, key/value block)
+ * pair, updating caller-owned online-softmax state in place ([TKG] §3).
+ *
+ * q_blk [B, H, Lq, d]; kv_blk.k, kv_blk.v [B, Hkv, Lkv, d] (compact blocks,
+ * element type mask_desc->dtype).  State, float32, caller-owned:
+ *   m [B, H, Lq]      reference row max of the scaled logits (natural units)
+ *   l [B, H, Lq]      sum over keys seen so far of exp(s - m)
+ *   o [B, H, Lq, d]   sum over keys seen so far of exp(s - m) * v
+ * Initialize with m = -inf, l = 0, o = 0.  After the call (m, l, o) describe
+ * the keys seen before plus this block.  The kernel may keep m below the
+ * true running max (by at most 8 / log2(e) in natural units) to skip
+ * rescaling; l and o are always relative to the stored m, so O = o / l and
+ * lse = m + ln l are exact either way (ring_attn_finalize computes them).
+ *
+ * Positions for the causal mask come from mask_desc: contiguous
+ * pos_q(i) = q_rank*Lq + i, pos_k(j) = kv_rank*Lkv + j; striped
+ * pos_q(i) = i*P + q_rank, pos_k(j) = j*P + kv_rank.  A query row with no
+ * visible key in the block leaves its state unchanged.
+ * ---------------------------------------------------------------------- */
+typedef struct { const void* k; const void* v; } ra_kv_block;
+typedef struct {
+  int B, H, Hkv, d;
+  long long Lq, Lkv;
+  float scale;
+  ra_dtype dtype;
+  int causal;
+  ra_layout layout;
+  int P, q_rank, kv_rank;
+} ra_mask_desc;
+ra_status ring_attn_step(const void* q_blk, ra_kv_block kv_blk, float* m, float* l, float* o,
+                         const ra_mask_desc* mask_desc, void* stream);
+
+/* ring_attn_finalize -- O_final = o / l ([TKG] §3 equation O_final) cast to
+ * out_dtype, and lse = m + ln l, for `rows` independent rows of width d.
+ * A row with l == 0 (no visible key) gives out = 0 and lse = -inf.        */
+ra_status ring_attn_finalize(const float* m, const float* l, const float* o, void* out,
+                             float* lse, long long rows, int d, ra_dtype out_dtype,
+                             void* stream);
+
+/* ------------------------------------------------------------------------
+ * lse_merge -- merge two normalized partial attention results over disjoint
+ * key sets, in place into (o_a, lse_a):
+ *   lse = ln(e^lse_a + e^lse_b)
+ *   o_a = e^(lse_a - lse) * o_a + e^(lse_b - lse) * o_b
+ * This is the [TKG] §3 m_new / alpha / beta / l_new / O_new update applied to
+ * two partial states written as (O, lse).  A row whose two lse are -inf
+ * gets o = 0, lse = -inf.  o_a, o_b [rows, d] and lse_a, lse_b [rows],
+ * float32; d any positive value up to 1024.
+ * ---------------------------------------------------------------------- */
+ra_status lse_merge(float* o_a, float* lse_a, const float* o_b, const float* lse_b,
+                    long long rows, int d, void* stream);
+
+/* ------------------------------------------------------------------------
+ * ring_attn_decode -- split-KV decode: one new query token per sequence
+ * against a key/value cache split into P ring blocks ([CML]: the decode
+ * KV-cache footprint of a long prompt).  Each ring block is processed in
+ * chunks; every chunk yields a normalized partial (O, lse) that reads each
+ * key/value row once for all H/Hkv query heads of its group; the partials
+ * are merged with the lse_merge rule, chunks within a ring block first, then
+ * the ring blocks in order.
+ *
+ * q, out [B, H, 1, d]; k, v [B, Hkv, L, d]; lse [B, H] float32.  The query
+ * sees every cached key (no mask).  Requires L % P == 0 and H / Hkv <= 16.
+ * ws: at least ring_attn_decode_ws_bytes(...) bytes.
+ * ---------------------------------------------------------------------- */
+size_t ring_attn_decode_ws_bytes(int B, int H, int Hkv, long long L, int d, int P);
+ra_status ring_attn_decode(const void* q, const void* k, const void* v, void* out, float* lse,
+                           int B, int H, int Hkv, long long L, int d, int P, float scale,
+                           ra_dtype dtype, void* stream, void* ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------
+ * Diagnostics.
+ * ra_last_error: message of the last failed call on this thread ("" if none).
+ * ra_version: library version string.
+ * ra_prof_enable(1) makes the library bracket every fused block-attention
+ * kernel launch (one per ring step) and every decode-partial launch with
+ * HIP events on the stream the kernel runs on; ra_prof_read() synchronizes
+ * on the recorded events and returns, since the last ra_prof_reset():
+ *   out[0] total step-kernel milliseconds   out[1] step-kernel launches
+ *   out[2] total decode-kernel milliseconds out[3] decode-kernel launches
+ *   out[4] algorithmic FLOPs of the timed step kernels (4 d per unmasked
+ *          query/key pair per query head, [TKG] §4 table)
+ *   out[5] algorithmic bytes of the timed decode kernels (K and V once, q,
+ *          and the fp32 partials written)
+ * Events are created once per process and reused.
+ * ---------------------------------------------------------------------- */
+const char* ra_last_error(void);
+const char* ra_version(void);
+ra_status ra_prof_enable(int on);
+ra_status ra_prof_reset(void);
+ra_status ra_prof_read(double* out6);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RING_ATTN_H */

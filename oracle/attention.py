@@ -134,26 +134,36 @@ def attention(q, k, v, *, scale=None, causal=False, q_pos=None, k_pos=None,
     lse = np.full((B, H, R), np.nan)
     pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
     chunk = max(1, min(R, _CHUNK_ELEMS // max(1, Nk)))
-    units = [(b, h, s) for (b, h) in pairs for s in range(0, R, chunk)]
     group = H // Hkv
-
-    def work(unit):
-        b, h, s = unit
-        g = h // group
-        sel = row_idx[s:s + chunk]
-        o, ls, _, _ = attention_rows(q[b, h, sel], k[b, g], v[b, g], scale=scale,
-                                     causal=causal, q_pos=qp_all[sel], k_pos=kp)
-        O[b, h, s:s + chunk] = o
-        lse[b, h, s:s + chunk] = ls
-
+    # one kv plane at a time, converted to fp64 once and shared by its units
+    planes = {}
+    for (b, h) in pairs:
+        planes.setdefault((b, h // group), []).append(h)
     nthr = _threads(threads)
-    if threadpool_limits is not None:
-        with threadpool_limits(limits=1):
-            with ThreadPoolExecutor(nthr) as ex:
-                list(ex.map(work, units))
-    else:  # pragma: no cover
+
+    def run_plane(b, g, hs):
+        K = np.asarray(k[b, g], dtype=np.float64)
+        V = np.asarray(v[b, g], dtype=np.float64)
+        units = [(h, s) for h in hs for s in range(0, R, chunk)]
+
+        def work(unit):
+            h, s = unit
+            sel = row_idx[s:s + chunk]
+            o, ls, _, _ = attention_rows(q[b, h, sel], K, V, scale=scale,
+                                         causal=causal, q_pos=qp_all[sel], k_pos=kp)
+            O[b, h, s:s + chunk] = o
+            lse[b, h, s:s + chunk] = ls
+
         with ThreadPoolExecutor(nthr) as ex:
             list(ex.map(work, units))
+
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            for (b, g), hs in planes.items():
+                run_plane(b, g, hs)
+    else:  # pragma: no cover
+        for (b, g), hs in planes.items():
+            run_plane(b, g, hs)
     return O, lse
 
 

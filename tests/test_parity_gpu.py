@@ -1,0 +1,214 @@
+"""GPU parity: the HIP library against the fp64 oracle on the same seeded inputs.
+
+Small and ragged shapes that span several 128-row query tiles and 64-key
+tiles plus a tail; every call goes through the C ABI (via the ctypes
+binding).  Tolerances: fp32 max|dO|, max|dlse| <= 1e-5; bf16 max|dO| <= 1e-2,
+max|dlse| <= 1e-3.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import blockwise_ring_attention_attn_amd as ra
+import oracle
+import synth
+from _util import assert_close, from_dev, host_vals, max_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, B, H, Hkv, N, d, dtype, Nq=None):
+    print(f"\n[case] seed={seed} B={B} H={H} Hkv={Hkv} N={N} d={d} dtype={dtype} Nq={Nq}", flush=True)
+    return synth.qkv(seed, B, H, Hkv, N, d, dtype, Nq=Nq)
+
+
+def _fwd_and_check(seed, B, H, Hkv, N, d, P, causal, layout, dtype):
+    q, k, v = _case(seed, B, H, Hkv, N, d, dtype)
+    out, lse = ra.ring_attn_fwd(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), P=P, causal=causal,
+                                layout=layout)
+    import torch
+    torch.cuda.synchronize()
+    Ow, Lw = oracle.attention(host_vals(q, dtype), host_vals(k, dtype), host_vals(v, dtype),
+                              scale=1 / math.sqrt(d), causal=causal)
+    return assert_close(from_dev(out), from_dev(lse), Ow, Lw, dtype,
+                        f"fwd B={B} H={H}/{Hkv} N={N} d={d} P={P} causal={causal} {layout} {dtype}")
+
+
+def test_config1_fp32_noncausal_P4():
+    """Single head, N=1024, d=64, fp32, non-causal, P=4 ring blocks of 256."""
+    eo, el = _fwd_and_check(1, 1, 1, 1, 1024, 64, 4, False, "contiguous", "f32")
+    print(f"config1 max|dO|={eo:.2e} max|dlse|={el:.2e}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+def test_fp32_small(d, causal, layout):
+    _fwd_and_check(7, 1, 2, 1, 4 * 75, d, 4, causal, layout, "f32")
+
+
+@pytest.mark.parametrize("N,P", [(8, 8), (24, 8), (8 * 130, 8), (4 * 257, 4), (3 * 384, 3), (700, 1)])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+def test_bf16_causal_ragged(N, P, d, layout):
+    _fwd_and_check(2, 1, 4, 2, N, d, P, True, layout, "bf16")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_batched_gqa(causal):
+    _fwd_and_check(3, 2, 8, 2, 4 * 320, 128, 4, causal, "contiguous", "bf16")
+
+
+def test_bf16_layout_and_P_invariance():
+    """Same inputs: contiguous P=8, striped P=8, striped P=2 and P=1 agree
+    with each other within twice the tolerance and each with the oracle."""
+    dtype, N, d = "bf16", 8 * 256, 128
+    q, k, v = _case(4, 1, 2, 2, N, d, dtype)
+    outs = []
+    for layout, P in (("contiguous", 8), ("striped", 8), ("striped", 2), ("contiguous", 1)):
+        o, l = ra.ring_attn_fwd(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), P=P, causal=True,
+                                layout=layout)
+        outs.append((from_dev(o), from_dev(l)))
+    for o, l in outs[1:]:
+        assert max_err(o, outs[0][0]) <= 2e-2 and max_err(l, outs[0][1]) <= 2e-3
+
+
+def test_gqa_equals_repeated_kv_bitwise():
+    dtype, N, d = "bf16", 4 * 200, 64
+    q, k, v = _case(5, 1, 4, 2, N, d, dtype)
+    kr, vr = np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1)
+    o1, l1 = ra.ring_attn_fwd(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), P=4, causal=True)
+    o2, l2 = ra.ring_attn_fwd(to_dev(q, dtype), to_dev(kr, dtype), to_dev(vr, dtype), P=4, causal=True)
+    assert np.array_equal(from_dev(o1), from_dev(o2)) and np.array_equal(from_dev(l1), from_dev(l2))
+
+
+def test_deterministic_bitwise():
+    dtype, N, d = "bf16", 8 * 300, 128
+    q, k, v = _case(6, 1, 4, 4, N, d, dtype)
+    qd, kd, vd = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    r1 = ra.ring_attn_fwd(qd, kd, vd, P=8, causal=True, layout="striped")
+    r2 = ra.ring_attn_fwd(qd, kd, vd, P=8, causal=True, layout="striped")
+    assert np.array_equal(from_dev(r1[0]), from_dev(r2[0]))
+    assert np.array_equal(from_dev(r1[1]), from_dev(r2[1]))
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_share_matches_oracle(layout, dtype):
+    """One host's share: q holds host `rank`'s tokens, k, v the whole sequence."""
+    import torch
+    B, H, Hkv, N, d, P = 1, 4, 2, 8 * 192, 128, 8
+    q, k, v = _case(8, B, H, Hkv, N, d, dtype)
+    pos = oracle.host_positions(N, P, layout)
+    for rank in (0, 3, 7):
+        qr = np.ascontiguousarray(q[:, :, pos[rank]])
+        o, l = ra.ring_attn_fwd_share(to_dev(qr, dtype), to_dev(k, dtype), to_dev(v, dtype), P=P, rank=rank,
+                                      causal=True, layout=layout)
+        torch.cuda.synchronize()
+        Ow, Lw = oracle.attention(host_vals(qr, dtype), host_vals(k, dtype), host_vals(v, dtype),
+                                  causal=True, q_pos=pos[rank])
+        assert_close(from_dev(o), from_dev(l), Ow, Lw, dtype, f"share rank={rank} {layout}")
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_step_state_against_oracle(layout, dtype):
+    """ring_attn_step on one (q block, kv block) pair, then on a second kv
+    block: lse = m + ln l and O = o / l match the oracle's partial over the
+    keys seen; m stays within 8/log2(e) below the true max."""
+    import torch
+    B, H, Hkv, N, d, P = 1, 2, 1, 4 * 200, 64, 4
+    q, k, v = _case(9, B, H, Hkv, N, d, dtype)
+    pos = oracle.host_positions(N, P, layout)
+    qr, kr_ = 2, 1
+    qb = np.ascontiguousarray(q[:, :, pos[qr]])
+    m, l, o = ra.init_state(B, H, N // P, d, "cuda:0")
+    seen = []
+    for kvr in (kr_, qr):
+        kb = np.ascontiguousarray(k[:, :, pos[kvr]])
+        vb = np.ascontiguousarray(v[:, :, pos[kvr]])
+        ra.ring_attn_step(to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype), m, l, o, causal=True,
+                          layout=layout, P=P, q_rank=qr, kv_rank=kvr)
+        seen.append(kvr)
+        torch.cuda.synchronize()
+        kp = np.concatenate([pos[r] for r in seen])
+        ks = np.concatenate([host_vals(k, dtype)[:, :, pos[r]] for r in seen], axis=2)
+        vs = np.concatenate([host_vals(v, dtype)[:, :, pos[r]] for r in seen], axis=2)
+        Ow, Lw = oracle.attention(host_vals(qb, dtype), ks, vs, causal=True, q_pos=pos[qr], k_pos=kp)
+        mh, lh, oh = from_dev(m), from_dev(l), from_dev(o)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            lse = mh + np.log(lh)
+            On = np.where(lh[..., None] > 0, oh / lh[..., None], 0.0)
+        assert_close(On, lse, Ow, Lw, dtype, f"step kv={seen}")
+        # the stored m is a valid reference: never above the true max, at most 8/log2 e below
+        S = np.einsum("bhid,bhjd->bhij", host_vals(qb, dtype).astype(np.float64),
+                      np.repeat(ks, H // Hkv, axis=1).astype(np.float64)) / math.sqrt(d)
+        S = np.where(kp[None, None, None, :] <= pos[qr][None, None, :, None], S, -np.inf)
+        true_max = S.max(axis=-1)
+        fin = np.isfinite(true_max)
+        assert np.all(mh[fin] <= true_max[fin] + 1e-4)
+        assert np.all(mh[fin] >= true_max[fin] - 8 / math.log2(math.e) - 1e-4)
+        assert np.all(np.isneginf(mh[~fin]))
+
+
+def test_step_then_finalize_and_empty_rows():
+    """Striped causal step with kv_rank > q_rank: row 0 sees no key, so its
+    state stays (m=-inf, l=0, o=0) and finalize gives O=0, lse=-inf."""
+    import torch
+    dtype, B, H, N, d, P = "bf16", 1, 1, 4 * 64, 64, 4
+    q, k, v = _case(10, B, H, H, N, d, dtype)
+    pos = oracle.host_positions(N, P, "striped")
+    qb = np.ascontiguousarray(q[:, :, pos[1]])
+    kb = np.ascontiguousarray(k[:, :, pos[3]])
+    vb = np.ascontiguousarray(v[:, :, pos[3]])
+    m, l, o = ra.init_state(B, H, N // P, d, "cuda:0")
+    ra.ring_attn_step(to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype), m, l, o, causal=True,
+                      layout="striped", P=P, q_rank=1, kv_rank=3)
+    out, lse = ra.ring_attn_finalize(m, l, o, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    Ow, Lw = oracle.attention(host_vals(qb, dtype), host_vals(kb, dtype), host_vals(vb, dtype), causal=True,
+                              q_pos=pos[1], k_pos=pos[3])
+    assert from_dev(l)[0, 0, 0] == 0 and np.isneginf(from_dev(lse)[0, 0, 0])
+    assert np.all(from_dev(out)[0, 0, 0] == 0)
+    assert_close(from_dev(out), from_dev(lse), Ow, Lw, dtype, "step+finalize")
+
+
+def test_lse_merge_against_oracle():
+    import torch
+    rng = np.random.default_rng(11)
+    rows, d = 1000, 96
+    oa, ob = rng.standard_normal((rows, d)).astype(np.float32), rng.standard_normal((rows, d)).astype(np.float32)
+    la, lb = (rng.standard_normal(rows) * 5).astype(np.float32), (rng.standard_normal(rows) * 5).astype(np.float32)
+    la[:10] = -np.inf
+    lb[5:15] = -np.inf
+    Ow, Lw = oracle.lse_merge(oa, la, ob, lb)
+    ta, tla = torch.from_numpy(oa).cuda(), torch.from_numpy(la).cuda()
+    ra.lse_merge(ta, tla, torch.from_numpy(ob).cuda(), torch.from_numpy(lb).cuda())
+    torch.cuda.synchronize()
+    assert max_err(from_dev(ta), Ow) <= 1e-5 and max_err(from_dev(tla), Lw) <= 1e-5
+    assert np.all(from_dev(ta)[5:10] == 0) and np.all(np.isneginf(from_dev(tla)[5:10]))
+
+
+@pytest.mark.parametrize("B,H,Hkv,L,d,P", [(2, 8, 2, 8 * 1000, 128, 8), (3, 4, 4, 4 * 77, 64, 4),
+                                           (1, 16, 1, 2 * 4096, 128, 2), (2, 2, 2, 1, 128, 1)])
+def test_decode_against_oracle(B, H, Hkv, L, d, P):
+    import torch
+    dtype = "bf16"
+    q, k, v = _case(12, B, H, Hkv, L, d, dtype, Nq=1)
+    out, lse = ra.ring_attn_decode(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), P=P)
+    torch.cuda.synchronize()
+    Ow, Lw = oracle.decode(host_vals(q, dtype), host_vals(k, dtype), host_vals(v, dtype))
+    assert_close(from_dev(out), from_dev(lse), Ow, Lw[:, :, 0], dtype, f"decode B={B} H={H}/{Hkv} L={L}")
+
+
+def test_decode_P1_equals_P8():
+    import torch
+    dtype = "bf16"
+    q, k, v = _case(13, 2, 8, 2, 8 * 512, 128, dtype, Nq=1)
+    r1 = ra.ring_attn_decode(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), P=1)
+    r8 = ra.ring_attn_decode(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), P=8)
+    torch.cuda.synchronize()
+    assert max_err(from_dev(r1[0]), from_dev(r8[0])) <= 1e-2
+    assert max_err(from_dev(r1[1]), from_dev(r8[1])) <= 1e-4
