@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark: blockwise ring attention on one MI355X.
+
+One step = one ring_attn_fwd call over the whole causal prefill workload
+(bf16, B=1, H=32, N=32768, d=128, contiguous layout, P=8 virtual hosts,
+all ring steps with the staging copies on the second stream), inputs already
+resident in HBM.  Prints ONE JSON line:
+  value        causal-adjusted TFLOP/s of the whole call (4 d FLOPs per
+               unmasked query/key pair per query head)
+  roofline     the fused step kernel: algorithmic FLOPs per launch / mean
+               launch time (HIP events on the compute stream) vs the bf16
+               dense MFMA peak
+  cpu_baseline the fp64 oracle on a bounded row sample of the same workload
+  decode       split-KV decode (16 sequences, H=32/Hkv=8, L=262144, d=128,
+               P=8): algorithmic HBM GB/s, with its kernel's roofline
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+METRIC = "causal ring-attn fwd TFLOP/s + % bf16 MFMA peak; split-KV decode HBM GB/s"
+
+PREFILL = dict(B=1, H=32, Hkv=32, N=32768, d=128, P=8, layout="contiguous", causal=True, seed=2)
+DECODE = dict(B=16, H=32, Hkv=8, L=262144, d=128, P=8, seed=5)
+
+
+def prefill_flops(c) -> float:
+    N = c["N"]
+    pairs = N * (N + 1) // 2 if c["causal"] else N * N
+    return 4.0 * c["d"] * pairs * c["B"] * c["H"]
+
+
+def decode_bytes(c) -> float:
+    B, H, Hkv, L, d, P = c["B"], c["H"], c["Hkv"], c["L"], c["d"], c["P"]
+    kv = 2.0 * B * Hkv * L * d * 2          # K and V read once (GQA: not x H/Hkv)
+    qo = 2.0 * B * H * d * 2 + B * H * 4    # q read, O (bf16) and lse written
+    part = 2.0 * B * H * P * (d + 1) * 4    # per-ring-block fp32 partials written and read
+    return kv + qo + part
+
+
+def upload(x, dtype):
+    import numpy as np
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    return torch.from_numpy(x).to("cuda:0")
+
+
+def cpu_baseline(c, q, k, v, budget_s: float = 12.0) -> dict:
+    """The fp64 oracle, as it is, on a seeded sample of query rows."""
+    import numpy as np
+    import oracle
+    import synth
+    cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(c["seed"])
+    heads = [(0, h) for h in (0, c["H"] // 2)]
+    qf = synth.as_f32(q[:, :c["H"]], "bf16")
+    kf = synth.as_f32(k, "bf16")
+    vf = synth.as_f32(v, "bf16")
+    n_rows = 64
+    elapsed, flops, rows_done = 0.0, 0.0, 0
+    while True:
+        rows = np.sort(rng.integers(0, c["N"], n_rows))
+        t0 = time.perf_counter()
+        oracle.attention(qf, kf, vf, causal=True, rows=rows, heads=heads, threads=cores)
+        dt = time.perf_counter() - t0
+        elapsed += dt
+        flops += 4.0 * c["d"] * float((rows + 1).sum()) * len(heads)
+        rows_done += n_rows * len(heads)
+        if elapsed >= budget_s:
+            break
+        n_rows = int(min(4096, max(n_rows * 2, n_rows * (budget_s - elapsed) / max(dt, 1e-3) * 0.5)))
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows_done} query rows (heads 0 and {c['H'] // 2}, uniformly random positions, "
+                      f"causal prefix of each row) of the prefill workload, fp64, {elapsed:.1f} s",
+            "seconds": elapsed}
+
+
+def run_prefill(args) -> dict:
+    import torch
+    import blockwise_ring_attention_attn_amd as ra
+    import synth
+    c = PREFILL
+    q, k, v = synth.qkv(c["seed"], c["B"], c["H"], c["Hkv"], c["N"], c["d"], "bf16")
+    qd, kd, vd = upload(q, "bf16"), upload(k, "bf16"), upload(v, "bf16")
+    out = torch.empty_like(qd)
+    lse = torch.empty((c["B"], c["H"], c["N"]), dtype=torch.float32, device="cuda:0")
+    nb = ra.ring_attn_fwd_ws_bytes(c["B"], c["H"], c["Hkv"], c["N"], c["d"], c["P"], ra.RA_BF16)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ra.ring_attn_fwd(qd, kd, vd, P=c["P"], causal=c["causal"], layout=c["layout"], out=out, lse=lse,
+                         ws=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ra.prof_enable(True)
+    ra.prof_reset()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = ra.prof_read()
+    ra.prof_enable(False)
+    ms = ev0.elapsed_time(ev1) / args.steps
+    flops = prefill_flops(c)
+    tflops = flops / (ms * 1e-3) / 1e12
+    launches = prof["step_launches"]
+    kern_ms = prof["step_ms"] / max(1, launches)
+    achieved = prof["step_flops"] / (prof["step_ms"] * 1e-3) / 1e12 if prof["step_ms"] > 0 else 0.0
+    res = {
+        "value": tflops, "ms_per_step": ms, "wall_s": wall, "flops": flops,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "step_bf16_kernel<128>", "launches_per_step": launches / args.steps,
+                     "mean_launch_ms": kern_ms,
+                     "flops_per_launch": prof["step_flops"] / max(1, launches)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(c, q, k, v, args.cpu_seconds)
+    del qd, kd, vd, out, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_decode(args) -> dict:
+    import torch
+    import blockwise_ring_attention_attn_amd as ra
+    import synth
+    c = DECODE
+    q, k, v = synth.qkv(c["seed"], c["B"], c["H"], c["Hkv"], c["L"], c["d"], "bf16", Nq=1)
+    qd = upload(q, "bf16")
+    kd = upload(k, "bf16")
+    del k
+    vd = upload(v, "bf16")
+    del v
+    out = torch.empty_like(qd)
+    lse = torch.empty((c["B"], c["H"]), dtype=torch.float32, device="cuda:0")
+    nb = ra.load().ring_attn_decode_ws_bytes(c["B"], c["H"], c["Hkv"], c["L"], c["d"], c["P"])
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ra.ring_attn_decode(qd, kd, vd, P=c["P"], out=out, lse=lse, ws=ws, stream=stream)
+
+    for _ in range(max(2, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    ra.prof_enable(True)
+    ra.prof_reset()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(args.steps, 10)
+    ev0.record(stream)
+    for _ in range(n):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    prof = ra.prof_read()
+    ra.prof_enable(False)
+    ms = ev0.elapsed_time(ev1) / n
+    nbytes = decode_bytes(c)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    kern_achieved = prof["decode_bytes"] / (prof["decode_ms"] * 1e-3) / 1e9 if prof["decode_ms"] > 0 else 0.0
+    del qd, kd, vd, out, lse, ws
+    torch.cuda.empty_cache()
+    return {
+        "metric": "split-KV decode HBM GB/s", "value": gbs, "unit": "GB/s", "ms_per_step": ms, "steps": n,
+        "frac_hbm_peak": gbs / HBM_PEAK_GBS, "bytes": nbytes,
+        "config": {"workload": "decode: 16 sequences x 1 query token, H=32 / Hkv=8, L=262144, d=128, "
+                               "P=8 ring blocks, bf16", **c},
+        "roofline": {"bound": "hbm", "achieved": kern_achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": kern_achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "decode_partial_kernel<128>",
+                     "mean_launch_ms": prof["decode_ms"] / max(1, prof["decode_launches"]),
+                     "bytes_per_launch": prof["decode_bytes"] / max(1, prof["decode_launches"])},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the ring's P hosts are emulated on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    pre = run_prefill(args)
+    c = PREFILL
+    line = {
+        "metric": METRIC,
+        "value": pre["value"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal prefill ring: bf16 B=1 H=32 N=32768 d=128, contiguous layout, "
+                               "P=8 virtual hosts (all ring steps, KV staging on a second stream)",
+                   "global_batch": c["B"], "seq_len": c["N"], "parallelism": "1 GPU, P=8 virtual ring hosts",
+                   **c},
+        "pct_bf16_mfma_peak": 100.0 * pre["value"] / MFMA_BF16_PEAK_TFLOPS,
+        "algorithmic_flops_per_step": pre["flops"],
+        "roofline": pre["roofline"],
+    }
+    if "cpu_baseline" in pre:
+        line["cpu_baseline"] = pre["cpu_baseline"]
+    if not args.no_decode:
+        line["decode"] = run_decode(args)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
