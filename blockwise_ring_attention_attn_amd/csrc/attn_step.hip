@@ -28,9 +28,9 @@
 // and the output accumulator's rescale is a per-lane scalar.  P^T feeds the
 // second MFMA straight from registers: the contraction index is permuted to
 // the order the first MFMA left the keys in, and V^T is read from LDS in
-// that same order.  K tiles are stored row-major and V tiles transposed in
-// LDS, double-buffered: the next tile's global loads are in flight while the
-// current tile computes.
+// that same order with the gfx950 transposing LDS read.  K and V tiles are
+// stored row-major in LDS and triple-buffered: the global loads of tile
+// j + 2 are in flight while tile j computes.
 #include "ra_internal.h"
 
 namespace ra {
@@ -191,115 +191,120 @@ __device__ __forceinline__ void store_row(const StepArgs& A, int64_t idx, bool f
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel.  BM = 128 query rows (4 waves x 32), BN = 64 keys / tile.
+// bf16 MFMA kernel.
+//
+// Workgroup: 4 waves, BM = 128 query rows (32 per wave, one MFMA column
+// block), two workgroups per CU (two waves per SIMD, so one wave's softmax
+// overlaps the other's MFMAs).  Key/value tiles of BN = 64 rows go straight
+// from HBM into LDS with buffer_load_dwordx4 ... lds (each wave instruction
+// fills 1 KiB of LDS, lane l at byte 16 l; the buffer descriptor's bound
+// turns rows past the block into zeros), double-buffered: tile j + 1 is in
+// flight while tile j computes, one barrier per tile.
+//
+// LDS rows are unpadded (D * 2 bytes); 16-byte chunks are XOR-swizzled so
+// that every read phase touches all 32 banks:
+//   K row r:  logical chunk c sits in slot c ^ (r & 7)
+//   V row k:  logical chunk c sits in slot c ^ (2 (k & 3))
+// K fragments (A operand of S^T = K Q^T) are ds_read_b128 of one row each.
+// The V^T operand of O^T = V^T P^T comes from ds_read_b64_tr_b16: in each
+// 16-lane group, lane i receives element i%4 of the 8-byte pieces addressed
+// by lanes i/4 + 4 j (j = 0..3); pointing lane s at key 4 (s/32) + (s%16)/4
+// and dims 16 ((s/16)%2) + 4 (s%4) hands every lane 4 consecutive keys of its
+// own dim, in the key order the S^T registers already hold.
 // ---------------------------------------------------------------------------
+constexpr int kThreads = 256;
 constexpr int kBM = 128;
 constexpr int kBN = 64;
-constexpr int kThreads = 256;
 
 template <int D>
-struct Lds {
-  static constexpr int KP = D + 8;      // K row pitch (bf16 elements)
-  static constexpr int VP = kBN + 4;    // V^T row pitch (bf16 elements)
-  static constexpr int K_ELEMS = kBN * KP;
-  static constexpr int V_ELEMS = D * VP;
-  static constexpr int BUF = K_ELEMS + V_ELEMS;
-  static constexpr int BYTES = 2 * BUF * 2;
+struct Tile {
+  static constexpr int RB = D * 2;              // bytes per LDS row
+  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int BYTES = kBN * RB;        // one K (or V) tile
+  static constexpr int BUF = 2 * BYTES;         // K tile then V tile
+  static constexpr int LDS_BYTES = 2 * BUF;     // double buffer
+  static constexpr int INSTR = BYTES / 1024;    // 1 KiB load instructions per tile per tensor
+  static constexpr int PER_WAVE = INSTR / 4;
 };
 
-template <int D>
-struct KvRegs {
-  static constexpr int KCH = kBN * D / 8 / kThreads;          // 16-byte K chunks per thread
-  static constexpr int VUNITS = (kBN / 4) * (D / 8);          // 4-key x 8-dim units
-  static constexpr int VU = (VUNITS + kThreads - 1) / kThreads;
-  u32x4 k[KCH];
-  u32x4 v[VU][4];
-};
-
-template <int D>
-__device__ __forceinline__ void load_kv_tile(const StepArgs& A, const Work& w, int tile0,
-                                             KvRegs<D>& R) {
-  const int t = threadIdx.x;
-  const unsigned short* K = reinterpret_cast<const unsigned short*>(A.k);
-  const unsigned short* V = reinterpret_cast<const unsigned short*>(A.v);
-  constexpr int CPR = D / 8;  // chunks per row
-#pragma unroll
-  for (int u = 0; u < KvRegs<D>::KCH; ++u) {
-    const int c = t + u * kThreads;
-    const int row = c / CPR, col = c % CPR;
-    const int j = tile0 + row;
-    if (j < A.Lkv) {
-      R.k[u] = *reinterpret_cast<const u32x4*>(K + kv_row_index(A, w, j) * D + col * 8);
-    } else {
-      R.k[u] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < KvRegs<D>::VU; ++u) {
-    const int unit = t + u * kThreads;
-    if (unit < KvRegs<D>::VUNITS) {
-      const int dg = unit % CPR, kg = unit / CPR;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int j = tile0 + kg * 4 + kk;
-        if (j < A.Lkv) {
-          R.v[u][kk] = *reinterpret_cast<const u32x4*>(V + kv_row_index(A, w, j) * D + dg * 8);
-        } else {
-          R.v[u][kk] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-  }
+__device__ __forceinline__ u32x2 lds_read_tr(const unsigned char* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<unsigned char*>(p)));
+  return __builtin_bit_cast(u32x2, v);
 }
 
+__device__ __forceinline__ void wait_vmcnt0() {
+  // s_waitcnt vmcnt(0), leaving expcnt / lgkmcnt unconstrained
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// Issue the direct-to-LDS loads of one K/V tile.  `soff` is the byte offset
+// of the tile's first row inside the block's buffer descriptors.
 template <int D>
-__device__ __forceinline__ void store_kv_tile(unsigned short* lds_buf, const KvRegs<D>& R) {
-  const int t = threadIdx.x;
-  constexpr int CPR = D / 8;
-  unsigned short* Ks = lds_buf;
-  unsigned short* Vt = lds_buf + Lds<D>::K_ELEMS;
+__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                          unsigned char* buf, const int (&voff_k)[Tile<D>::PER_WAVE],
+                                          const int (&voff_v)[Tile<D>::PER_WAVE], int wave_u, unsigned soff) {
 #pragma unroll
-  for (int u = 0; u < KvRegs<D>::KCH; ++u) {
-    const int c = t + u * kThreads;
-    const int row = c / CPR, col = c % CPR;
-    *reinterpret_cast<u32x4*>(Ks + row * Lds<D>::KP + col * 8) = R.k[u];
-  }
-#pragma unroll
-  for (int u = 0; u < KvRegs<D>::VU; ++u) {
-    const int unit = t + u * kThreads;
-    if (unit < KvRegs<D>::VUNITS) {
-      const int dg = unit % CPR, kg = unit / CPR;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const unsigned sel = (i & 1) ? 0x07060302u : 0x05040100u;
-        const int dw = i >> 1;
-        u32x2 pr;
-        pr[0] = __builtin_amdgcn_perm(R.v[u][1][dw], R.v[u][0][dw], sel);
-        pr[1] = __builtin_amdgcn_perm(R.v[u][3][dw], R.v[u][2][dw], sel);
-        *reinterpret_cast<u32x2*>(Vt + (dg * 8 + i) * Lds<D>::VP + kg * 4) = pr;
-      }
-    }
+  for (int u = 0; u < Tile<D>::PER_WAVE; ++u) {
+    const int i = wave_u * Tile<D>::PER_WAVE + u;   // instruction index within the tile
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rk, (__attribute__((address_space(3))) void*)(buf + i * 1024), 16, voff_k[u], soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rv, (__attribute__((address_space(3))) void*)(buf + Tile<D>::BYTES + i * 1024), 16, voff_v[u], soff,
+        0, 0);
   }
 }
 
 template <int D, typename OutT>
 __global__ __launch_bounds__(kThreads, 2) void step_bf16_kernel(StepArgs A) {
-  extern __shared__ __align__(16) unsigned short lds[];
+  using T = Tile<D>;
+  extern __shared__ __align__(1024) unsigned char lds[];
   const Work w = decode_work(A);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5;       // which half of the wave
   const int col = lane & 31;        // query column owned by this lane
   const int64_t row_first = (int64_t)w.qtile * kBM;
   const int64_t row_last = (row_first + kBM < A.Lq ? row_first + kBM : A.Lq) - 1;
-  const int64_t my_row = row_first + wave * 32 + col;
+  const int64_t my_row = row_first + wave_u * 32 + col;
   const bool row_ok = my_row < A.Lq;
-
-  // Visible key range of this tile of queries.
-  const int64_t kv_end = key_limit(A, w, row_last) + 1;     // keys [0, kv_end) may be visible
-  const int64_t full_end = key_limit(A, w, row_first) + 1;  // keys [0, full_end) visible to all rows
-  const int64_t my_lim = key_limit(A, w, my_row < A.Lq ? my_row : row_last);
+  const int64_t my_lim = key_limit(A, w, row_ok ? my_row : row_last);
+  const int64_t kv_end = key_limit(A, w, row_last) + 1;
+  const int64_t full_end = key_limit(A, w, row_first) + 1;
   const int ntiles = (int)((kv_end + kBN - 1) / kBN);
+
+  // Buffer descriptors covering exactly the kv block's rows of this plane:
+  // row j sits at byte j * rstride * RB; rows j >= Lkv read as zero.
+  int64_t row0, rstride;
+  if (A.kv_mode == ROWS_COMPACT) {
+    row0 = 0;
+    rstride = 1;
+  } else {
+    const int rk = A.kv_mode == ROWS_HOST_Q ? w.q_rank : w.kv_rank;
+    row0 = A.layout == 0 ? (int64_t)rk * A.Lkv : rk;
+    rstride = A.layout == 0 ? 1 : A.P;
+  }
+  const int64_t plane_row = ((int64_t)w.b * A.Hkv + w.hkv) * A.kv_plane_rows + row0;
+  const unsigned nrec = (unsigned)(((int64_t)(A.Lkv - 1) * rstride + 1) * T::RB);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(A.k)) + plane_row * D, 0, nrec,
+      0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(A.v)) + plane_row * D, 0, nrec,
+      0x00020000);
+  const unsigned tile_bytes = (unsigned)(kBN * rstride * T::RB);
+  // Per-lane source offsets: lane l of load instruction i fills LDS slot
+  // (64 i + l) of the tile, i.e. row r = (64 i + l) / CPR, slot q = l % CPR,
+  // which holds logical chunk q ^ swizzle(r).
+  int voff_k[T::PER_WAVE], voff_v[T::PER_WAVE];
+#pragma unroll
+  for (int u = 0; u < T::PER_WAVE; ++u) {
+    const int pos = (wave_u * T::PER_WAVE + u) * 64 + lane;
+    const int r = pos / T::CPR, q = pos % T::CPR;
+    voff_k[u] = (int)(r * rstride * T::RB + 16 * (q ^ (r & 7)));
+    voff_v[u] = (int)(r * rstride * T::RB + 16 * (q ^ (2 * (r & 3))));
+  }
 
   // Resident query fragment: B operand of S^T = K Q^T (16 dims per MFMA).
   bf16x8 qf[D / 16];
@@ -314,46 +319,59 @@ __global__ __launch_bounds__(kThreads, 2) void step_bf16_kernel(StepArgs A) {
     }
   }
 
+  // LDS read addresses (bytes within a buffer).
+  // K: row kb*32 + col, logical chunk c = 2 ks + half, ks = 4 a + b:
+  //    slot = c ^ (col & 7) = 8 a + 2 (b ^ z) + y.
+  const int xk = col & 7;
+  const int yk = half ^ (xk & 1), zk = xk >> 1;
+  int kaddr[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) kaddr[b] = col * T::RB + 16 * (2 * (b ^ zk) + yk);
+  // V (transposing reads): lane s -> key 4 half + jp, jp = (s%16)/4, and dims
+  // 16 g + 4 (s%4), g = (s/16)%2, i.e. chunk 4 db + u, u = 2 g + (s%4)/2,
+  // byte 8 (s%2) inside it; slot = (4 db + u) ^ (2 jp) = 4 (db ^ jh) + (u ^ 2 jl).
+  const int jp = (lane & 15) >> 2, jh = jp >> 1, jl = jp & 1;
+  const int ug = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int vbase = T::BYTES + (4 * half + jp) * T::RB + 16 * (ug ^ (2 * jl)) + 8 * (lane & 1);
+  const int vaddr_even = vbase + 64 * jh;   // db even: db ^ jh = db + jh
+  const int vaddr_odd = vbase - 64 * jh;    // db odd:  db ^ jh = db - jh
+
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
   const float c = A.scale_log2;
 
-  KvRegs<D> R;
-  if (ntiles > 0) {
-    load_kv_tile<D>(A, w, 0, R);
-    store_kv_tile<D>(lds, R);
-  }
+  if (ntiles > 0) issue_tile<D>(rk, rv, lds, voff_k, voff_v, wave_u, 0u);
+  wait_vmcnt0();
   __syncthreads();
 
-  for (int jt = 0; jt < ntiles; ++jt) {
-    unsigned short* cur = lds + (jt & 1) * Lds<D>::BUF;
-    if (jt + 1 < ntiles) load_kv_tile<D>(A, w, (jt + 1) * kBN, R);
-
+  auto tile_body = [&](const unsigned char* cur, int jt) {
     // S^T = K Q^T for two blocks of 32 keys.
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
-      const unsigned short* kr = cur + (kb * 32 + col) * Lds<D>::KP + half * 8;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + ks * 16));
+        const unsigned char* p = cur + kaddr[ks & 3] + kb * 32 * T::RB + 128 * (ks >> 2);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
     }
 
-    // Mask: only tiles that reach past the all-visible prefix.
     const int64_t tile0 = (int64_t)jt * kBN;
     if (tile0 + kBN > full_end) {
+      // key tile0 + kb*32 + 8*(r/4) + 4*half + r%4 is visible iff its offset
+      // in the tile is <= my_lim - tile0; compare the compile-time part of
+      // the offset against one per-lane bound.
+      const int64_t rel = my_lim - tile0 - 4 * half;
+      const int bound = rel < -1 ? -1 : (rel > kBN ? kBN : (int)rel);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t j = tile0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (j > my_lim) s[kb][r] = kNegInf;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) > bound) s[kb][r] = kNegInf;
     }
 
     // Row max of this tile (raw scores), shared by both halves.
@@ -379,9 +397,9 @@ __global__ __launch_bounds__(kThreads, 2) void step_bf16_kernel(StepArgs A) {
     }
     const float m_use = m_run == kNegInf ? 0.f : m_run;
 
-    // P = exp2(S c - m): the row sum l takes the fp32 values, the PV
-    // product their bf16 rounding (the page's listing does the same: block
-    // sum from the fp32 exponentials, P cast to the V dtype for P V).
+    // P = exp2(S c - m): the row sum takes the fp32 values, the PV product
+    // their bf16 rounding (as the page's listing: block sum from the fp32
+    // exponentials, P cast to the V dtype for P V).
     bf16x8 pk[2][2];
     float lsum = 0.f;
 #pragma unroll
@@ -398,24 +416,32 @@ __global__ __launch_bounds__(kThreads, 2) void step_bf16_kernel(StepArgs A) {
 
     // O^T += V^T P^T.  Contraction index k = 8*half + e maps to key
     // 16*hc + 8*(e/4) + 4*half + e%4 of key block kb (the S^T register order).
-    const unsigned short* vt = cur + Lds<D>::K_ELEMS;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const unsigned short* vr = vt + (db * 32 + col) * Lds<D>::VP + 4 * half;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int hc = 0; hc < 2; ++hc)
 #pragma unroll
-        for (int hc = 0; hc < 2; ++hc) {
-          const int k0 = kb * 32 + hc * 16;
-          u32x2 lo = *reinterpret_cast<const u32x2*>(vr + k0);
-          u32x2 hi = *reinterpret_cast<const u32x2*>(vr + k0 + 8);
-          u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                             pk[kb][hc], oacc[db], 0, 0, 0);
+        for (int db = 0; db < D / 32; ++db) {
+          const unsigned char* p0 = cur + ((db & 1) ? vaddr_odd : vaddr_even) +
+                                    (kb * 32 + hc * 16) * T::RB + 64 * db;
+          const u32x2 lo = lds_read_tr(p0);
+          const u32x2 hi = lds_read_tr(p0 + 8 * T::RB);
+          const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pk[kb][hc],
+                                                             oacc[db], 0, 0, 0);
         }
-    }
+  };
 
-    if (jt + 1 < ntiles) store_kv_tile<D>(lds + ((jt + 1) & 1) * Lds<D>::BUF, R);
+  // Two tiles per trip so each buffer's LDS offset is a compile-time constant.
+  for (int jt = 0; jt < ntiles; jt += 2) {
+    if (jt + 1 < ntiles) issue_tile<D>(rk, rv, lds + T::BUF, voff_k, voff_v, wave_u, (unsigned)(jt + 1) * tile_bytes);
+    tile_body(lds, jt);
+    wait_vmcnt0();
+    __syncthreads();
+    if (jt + 1 >= ntiles) break;
+    if (jt + 2 < ntiles) issue_tile<D>(rk, rv, lds, voff_k, voff_v, wave_u, (unsigned)(jt + 2) * tile_bytes);
+    tile_body(lds + T::BUF, jt + 1);
+    wait_vmcnt0();
     __syncthreads();
   }
 
@@ -534,9 +560,9 @@ hipError_t launch_step_bf16(const StepArgs& a, int d, hipStream_t s) {
   const int g = grid_size(a);
   if (g <= 0) return hipSuccess;
   if (d == 128) {
-    hipLaunchKernelGGL((step_bf16_kernel<128, __bf16>), dim3(g), dim3(kThreads), Lds<128>::BYTES, s, a);
+    hipLaunchKernelGGL((step_bf16_kernel<128, __bf16>), dim3(g), dim3(kThreads), Tile<128>::LDS_BYTES, s, a);
   } else if (d == 64) {
-    hipLaunchKernelGGL((step_bf16_kernel<64, __bf16>), dim3(g), dim3(kThreads), Lds<64>::BYTES, s, a);
+    hipLaunchKernelGGL((step_bf16_kernel<64, __bf16>), dim3(g), dim3(kThreads), Tile<64>::LDS_BYTES, s, a);
   } else {
     return hipErrorInvalidValue;
   }
@@ -559,10 +585,10 @@ hipError_t launch_step_f32(const StepArgs& a, int d, hipStream_t s) {
 // The bf16 kernel needs more than the default 64 KiB of dynamic LDS.
 hipError_t step_kernel_setup() {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(step_bf16_kernel<128, __bf16>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::BYTES);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, Tile<128>::LDS_BYTES);
   if (e != hipSuccess) return e;
   return hipFuncSetAttribute(reinterpret_cast<const void*>(step_bf16_kernel<64, __bf16>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, Lds<64>::BYTES);
+                             hipFuncAttributeMaxDynamicSharedMemorySize, Tile<64>::LDS_BYTES);
 }
 
 }  // namespace ra

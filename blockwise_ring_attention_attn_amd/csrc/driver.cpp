@@ -208,9 +208,9 @@ StepPlan plan_step(int layout, int causal, int P, int s, int64_t Bl) {
   return p;
 }
 
+
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 size_t esize(ra_dtype t) { return t == RA_BF16 ? 2 : 4; }
-
 bool dtype_ok(int t) { return t == RA_F32 || t == RA_BF16; }
 bool layout_ok(int l) { return l == RA_CONTIGUOUS || l == RA_STRIPED; }
 
@@ -224,6 +224,9 @@ ra_status check_common(int B, int H, int Hkv, long long N, int d, int P, ra_dtyp
   if (N / P > (1LL << 30)) return fail(RA_EINVAL, "block length N/P too large");
   if (!dtype_ok(dtype)) return fail(RA_EINVAL, "unknown dtype %d", (int)dtype);
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(RA_EINVAL, "scale must be finite and > 0");
+  // The bf16 kernels address one (batch, kv head) plane with 32-bit buffer offsets.
+  if ((uint64_t)N * d * esize(dtype) >= (1ull << 31))
+    return fail(RA_EINVAL, "one kv head plane (N * d elements) must stay below 2 GiB");
   return RA_OK;
 }
 
@@ -526,6 +529,8 @@ ra_status ring_attn_step(const void* q_blk, ra_kv_block kv_blk, float* m, float*
     return fail(RA_EINVAL, "bad ring description P=%d q_rank=%d kv_rank=%d", md->P, md->q_rank, md->kv_rank);
   if (md->layout == RA_STRIPED && md->causal && md->Lq != md->Lkv)
     return fail(RA_EINVAL, "striped causal blocks must have Lq == Lkv");
+  if ((uint64_t)md->Lkv * md->d * esize(md->dtype) >= (1ull << 31))
+    return fail(RA_EINVAL, "one kv head block (Lkv * d elements) must stay below 2 GiB");
   if (!(md->scale > 0.f) || !std::isfinite(md->scale)) return fail(RA_EINVAL, "scale must be finite and > 0");
   const int BM = block_rows(md->dtype, md->d);
   const int64_t nqt = (md->Lq + BM - 1) / BM;
