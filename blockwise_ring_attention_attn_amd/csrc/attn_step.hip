@@ -31,6 +31,8 @@
 // that same order with the gfx950 transposing LDS read.  K and V tiles are
 // stored row-major in LDS and triple-buffered: the global loads of tile
 // j + 2 are in flight while tile j computes.
+#include <type_traits>
+
 #include "ra_internal.h"
 
 namespace ra {
@@ -202,9 +204,13 @@ __device__ __forceinline__ void store_row(const StepArgs& A, int64_t idx, bool f
 // flight while tile j computes, one barrier per tile.
 //
 // LDS rows are unpadded (D * 2 bytes); 16-byte chunks are XOR-swizzled so
-// that every read phase touches all 32 banks:
-//   K row r:  logical chunk c sits in slot c ^ (r & 7)
-//   V row k:  logical chunk c sits in slot c ^ (2 (k & 3))
+// that every read phase covers all 64 LDS banks (ds_read_b128 is served 16
+// lanes at a time, ds_read_b64_tr_b16 32 lanes at a time):
+//   K row r:  logical chunk c sits in slot c ^ kswz(r)
+//   V row k:  logical chunk c sits in slot c ^ vswz(k)
+// with kswz(r) = r & 15, vswz(k) = 4 (k & 3) for D = 128 (one row spans the
+// 64 banks) and kswz(r) = (r >> 1) & 7, vswz(k) = 4 ((k >> 1) & 1) for D = 64
+// (two rows span them).
 // K fragments (A operand of S^T = K Q^T) are ds_read_b128 of one row each.
 // The V^T operand of O^T = V^T P^T comes from ds_read_b64_tr_b16: in each
 // 16-lane group, lane i receives element i%4 of the 8-byte pieces addressed
@@ -212,20 +218,27 @@ __device__ __forceinline__ void store_row(const StepArgs& A, int64_t idx, bool f
 // and dims 16 ((s/16)%2) + 4 (s%4) hands every lane 4 consecutive keys of its
 // own dim, in the key order the S^T registers already hold.
 // ---------------------------------------------------------------------------
-constexpr int kThreads = 256;
-constexpr int kBM = 128;
+constexpr int kWaves = 4;                 // waves per workgroup (32 query rows each)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;
 constexpr int kBN = 64;
+constexpr int kWgPerCu = kWaves == 4 ? 2 : 1;
 
 template <int D>
 struct Tile {
   static constexpr int RB = D * 2;              // bytes per LDS row
   static constexpr int CPR = D / 8;             // 16-byte chunks per row
   static constexpr int BYTES = kBN * RB;        // one K (or V) tile
-  static constexpr int BUF = 2 * BYTES;         // K tile then V tile
-  static constexpr int LDS_BYTES = 2 * BUF;     // double buffer
+  static constexpr int LDS_BYTES = 4 * BYTES;   // K double buffer, then V double buffer
+  static constexpr int VOFF = 2 * BYTES;        // start of the V buffers
   static constexpr int INSTR = BYTES / 1024;    // 1 KiB load instructions per tile per tensor
-  static constexpr int PER_WAVE = INSTR / 4;
+  static constexpr int PER_WAVE = INSTR / kWaves;
 };
+
+template <int D>
+__device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int vswz(int k) { return D == 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); }
 
 __device__ __forceinline__ u32x2 lds_read_tr(const unsigned char* p) {
   typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -239,25 +252,22 @@ __device__ __forceinline__ void wait_vmcnt0() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-// Issue the direct-to-LDS loads of one K/V tile.  `soff` is the byte offset
-// of the tile's first row inside the block's buffer descriptors.
+// Issue the direct-to-LDS loads of one K (or V) tile: this wave's share of
+// the tile's 1 KiB load instructions.  `soff` is the byte offset of the
+// tile's first row inside the block's buffer descriptor.
 template <int D>
-__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                          unsigned char* buf, const int (&voff_k)[Tile<D>::PER_WAVE],
-                                          const int (&voff_v)[Tile<D>::PER_WAVE], int wave_u, unsigned soff) {
+__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rsrc, unsigned char* buf,
+                                          const int (&voff)[Tile<D>::PER_WAVE], int wave_u, unsigned soff) {
 #pragma unroll
   for (int u = 0; u < Tile<D>::PER_WAVE; ++u) {
     const int i = wave_u * Tile<D>::PER_WAVE + u;   // instruction index within the tile
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rk, (__attribute__((address_space(3))) void*)(buf + i * 1024), 16, voff_k[u], soff, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rv, (__attribute__((address_space(3))) void*)(buf + Tile<D>::BYTES + i * 1024), 16, voff_v[u], soff,
-        0, 0);
+        rsrc, (__attribute__((address_space(3))) void*)(buf + i * 1024), 16, voff[u], soff, 0, 0);
   }
 }
 
 template <int D, typename OutT>
-__global__ __launch_bounds__(kThreads, 2) void step_bf16_kernel(StepArgs A) {
+__global__ __launch_bounds__(kThreads, kWgPerCu) void step_bf16_kernel(StepArgs A) {
   using T = Tile<D>;
   extern __shared__ __align__(1024) unsigned char lds[];
   const Work w = decode_work(A);
@@ -273,6 +283,7 @@ __global__ __launch_bounds__(kThreads, 2) void step_bf16_kernel(StepArgs A) {
   const int64_t kv_end = key_limit(A, w, row_last) + 1;
   const int64_t full_end = key_limit(A, w, row_first) + 1;
   const int ntiles = (int)((kv_end + kBN - 1) / kBN);
+  const int lim32 = (int)my_lim;
 
   // Buffer descriptors covering exactly the kv block's rows of this plane:
   // row j sits at byte j * rstride * RB; rows j >= Lkv read as zero.
@@ -302,8 +313,8 @@ __global__ __launch_bounds__(kThreads, 2) void step_bf16_kernel(StepArgs A) {
   for (int u = 0; u < T::PER_WAVE; ++u) {
     const int pos = (wave_u * T::PER_WAVE + u) * 64 + lane;
     const int r = pos / T::CPR, q = pos % T::CPR;
-    voff_k[u] = (int)(r * rstride * T::RB + 16 * (q ^ (r & 7)));
-    voff_v[u] = (int)(r * rstride * T::RB + 16 * (q ^ (2 * (r & 3))));
+    voff_k[u] = (int)(r * rstride * T::RB + 16 * (q ^ kswz<D>(r)));
+    voff_v[u] = (int)(r * rstride * T::RB + 16 * (q ^ vswz<D>(r)));
   }
 
   // Resident query fragment: B operand of S^T = K Q^T (16 dims per MFMA).
@@ -320,21 +331,20 @@ __global__ __launch_bounds__(kThreads, 2) void step_bf16_kernel(StepArgs A) {
   }
 
   // LDS read addresses (bytes within a buffer).
-  // K: row kb*32 + col, logical chunk c = 2 ks + half, ks = 4 a + b:
-  //    slot = c ^ (col & 7) = 8 a + 2 (b ^ z) + y.
-  const int xk = col & 7;
-  const int yk = half ^ (xk & 1), zk = xk >> 1;
-  int kaddr[4];
+  // K: row kb*32 + col, logical chunk 2 ks + half; kswz(kb*32 + col) = kswz(col).
+  int kaddr[D / 16];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) kaddr[b] = col * T::RB + 16 * (2 * (b ^ zk) + yk);
-  // V (transposing reads): lane s -> key 4 half + jp, jp = (s%16)/4, and dims
-  // 16 g + 4 (s%4), g = (s/16)%2, i.e. chunk 4 db + u, u = 2 g + (s%4)/2,
-  // byte 8 (s%2) inside it; slot = (4 db + u) ^ (2 jp) = 4 (db ^ jh) + (u ^ 2 jl).
-  const int jp = (lane & 15) >> 2, jh = jp >> 1, jl = jp & 1;
+  for (int ks = 0; ks < D / 16; ++ks) kaddr[ks] = col * T::RB + 16 * ((2 * ks + half) ^ kswz<D>(col));
+  // V (transposing reads): lane s -> key 4 half + jp (+ 32 kb + 16 hc, + 8),
+  // jp = (s%16)/4, and dims 32 db + 16 g + 4 (s%4), g = (s/16)%2, i.e. chunk
+  // 4 db + u, u = 2 g + (s%4)/2, byte 8 (s%2) inside it; vswz of the key
+  // depends on jp only.
+  const int jp = (lane & 15) >> 2;
   const int ug = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int vbase = T::BYTES + (4 * half + jp) * T::RB + 16 * (ug ^ (2 * jl)) + 8 * (lane & 1);
-  const int vaddr_even = vbase + 64 * jh;   // db even: db ^ jh = db + jh
-  const int vaddr_odd = vbase - 64 * jh;    // db odd:  db ^ jh = db - jh
+  int vaddr[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+    vaddr[db] = (4 * half + jp) * T::RB + 16 * ((4 * db + ug) ^ vswz<D>(jp)) + 8 * (lane & 1);
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -342,39 +352,43 @@ __global__ __launch_bounds__(kThreads, 2) void step_bf16_kernel(StepArgs A) {
   float m_run = kNegInf, l_run = 0.f;
   const float c = A.scale_log2;
 
-  if (ntiles > 0) issue_tile<D>(rk, rv, lds, voff_k, voff_v, wave_u, 0u);
-  wait_vmcnt0();
-  __syncthreads();
+  // Software pipeline over key tiles: iteration j computes S(j+1) = K(j+1) Q^T
+  // on the MFMA pipe while the VALU turns S(j) into P(j), then O += V(j)^T P(j).
+  // K tiles therefore run one tile ahead of V tiles: during iteration j the
+  // loads of K(j+2) and V(j+1) are in flight, K(j+1) and V(j) are read.
+  unsigned char* kbuf0 = lds;
+  unsigned char* kbuf1 = lds + T::BYTES;
+  unsigned char* vbuf0 = lds + T::VOFF;
+  unsigned char* vbuf1 = lds + T::VOFF + T::BYTES;
 
-  auto tile_body = [&](const unsigned char* cur, int jt) {
-    // S^T = K Q^T for two blocks of 32 keys.
-    f32x16 s[2];
+  auto qk = [&](const unsigned char* kb_lds, f32x16 (&s)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const unsigned char* p = cur + kaddr[ks & 3] + kb * 32 * T::RB + 128 * (ks >> 2);
+        const unsigned char* p = kb_lds + kaddr[ks] + kb * 32 * T::RB;
         const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
     }
+  };
 
-    const int64_t tile0 = (int64_t)jt * kBN;
+  // Mask, row max and (lazy) rescale of tile jt's scores; returns the
+  // reference max to subtract.
+  auto prepare = [&](f32x16 (&s)[2], int jt) -> float {
+    const int tile0 = jt * kBN;
     if (tile0 + kBN > full_end) {
       // key tile0 + kb*32 + 8*(r/4) + 4*half + r%4 is visible iff its offset
       // in the tile is <= my_lim - tile0; compare the compile-time part of
-      // the offset against one per-lane bound.
-      const int64_t rel = my_lim - tile0 - 4 * half;
-      const int bound = rel < -1 ? -1 : (rel > kBN ? kBN : (int)rel);
+      // the offset against one per-lane 32-bit bound (block rows < 2^30).
+      const int bound = lim32 - tile0 - 4 * half;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (kb * 32 + 8 * (r >> 2) + (r & 3) > bound) s[kb][r] = kNegInf;
     }
-
-    // Row max of this tile (raw scores), shared by both halves.
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -382,8 +396,8 @@ __global__ __launch_bounds__(kThreads, 2) void step_bf16_kernel(StepArgs A) {
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = partner_max(mx);
     const float m_tile = mx * c;
-
-    // Online-softmax update with a lazily refreshed reference max.
+    // Lazily refreshed reference max: rescale only when the tile max exceeds
+    // it by more than kTau (base 2).
     const bool need = m_tile > m_run + kTau;
     if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
       const float m_new = fmaxf(m_run, m_tile);
@@ -395,13 +409,14 @@ __global__ __launch_bounds__(kThreads, 2) void step_bf16_kernel(StepArgs A) {
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       m_run = m_new;
     }
-    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    return m_run == kNegInf ? 0.f : m_run;
+  };
 
-    // P = exp2(S c - m): the row sum takes the fp32 values, the PV product
-    // their bf16 rounding (as the page's listing: block sum from the fp32
-    // exponentials, P cast to the V dtype for P V).
-    bf16x8 pk[2][2];
-    float lsum = 0.f;
+  // P = exp2(S c - m): the row sum takes the fp32 values, the PV product
+  // their bf16 rounding (as the page's listing: block sum from the fp32
+  // exponentials, P cast to the V dtype for P V).
+  auto softmax = [&](const f32x16 (&s)[2], float m_use, bf16x8 (&pk)[2][2]) {
+    float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -409,21 +424,62 @@ __global__ __launch_bounds__(kThreads, 2) void step_bf16_kernel(StepArgs A) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float p = fast_exp2(__builtin_fmaf(s[kb][hc * 8 + e], c, -m_use));
-          lsum += p;
+          if (e & 1) lsum1 += p; else lsum0 += p;
           pk[kb][hc][e] = (__bf16)p;
         }
-    l_run += lsum;
+    l_run += lsum0 + lsum1;
+  };
 
-    // O^T += V^T P^T.  Contraction index k = 8*half + e maps to key
-    // 16*hc + 8*(e/4) + 4*half + e%4 of key block kb (the S^T register order).
+  // S(j+1) = K(j+1) Q^T interleaved with P(j) = softmax(S(j)): the loop is
+  // cut into NSTEP steps (one MFMA each, K fragment read two steps ahead,
+  // 32 / NSTEP score elements of the current tile), fenced so the compiler
+  // keeps the MFMAs spread across the exponentials.
+  auto qk_softmax = [&](const unsigned char* kb_lds, f32x16 (&nxt)[2], const f32x16 (&cur)[2], float m_use,
+                        bf16x8 (&pk)[2][2]) {
+    constexpr int KS = D / 16;
+    constexpr int NSTEP = 2 * KS;            // (kb, ks) pairs
+    constexpr int EPS = 32 / NSTEP;          // score elements per step (2 or 4)
+    auto kread = [&](int i) -> bf16x8 {
+      const int kb = i / KS, ks = i % KS;
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kb_lds + kaddr[ks] + kb * 32 * T::RB));
+    };
+    nxt[0] = f32x16{};
+    nxt[1] = f32x16{};
+    bf16x8 kf[3];
+    kf[0] = kread(0);
+    kf[1] = kread(1);
+    float lsum0 = 0.f, lsum1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) {
+      if (i + 2 < NSTEP) kf[(i + 2) % 3] = kread(i + 2);
+      const int kb = i / KS, ks = i % KS;
+      nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[ks], nxt[kb], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < EPS; t += 2) {
+        const int el = i * EPS + t;          // element pair (el, el + 1) of the current tile
+        const int ckb = el / 16, r = el % 16;
+        const float p0 = fast_exp2(__builtin_fmaf(cur[ckb][r], c, -m_use));
+        const float p1 = fast_exp2(__builtin_fmaf(cur[ckb][r + 1], c, -m_use));
+        lsum0 += p0;
+        lsum1 += p1;
+        pk[ckb][r >> 3][r & 7] = (__bf16)p0;
+        pk[ckb][r >> 3][(r & 7) + 1] = (__bf16)p1;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += lsum0 + lsum1;
+  };
+
+  // O^T += V^T P^T.  Contraction index k = 8*half + e maps to key
+  // 16*hc + 8*(e/4) + 4*half + e%4 of key block kb (the S^T register order).
+  auto pv = [&](const unsigned char* vb_lds, const bf16x8 (&pk)[2][2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int hc = 0; hc < 2; ++hc)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const unsigned char* p0 = cur + ((db & 1) ? vaddr_odd : vaddr_even) +
-                                    (kb * 32 + hc * 16) * T::RB + 64 * db;
+          const unsigned char* p0 = vb_lds + vaddr[db] + (kb * 32 + hc * 16) * T::RB;
           const u32x2 lo = lds_read_tr(p0);
           const u32x2 hi = lds_read_tr(p0 + 8 * T::RB);
           const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
@@ -432,17 +488,52 @@ __global__ __launch_bounds__(kThreads, 2) void step_bf16_kernel(StepArgs A) {
         }
   };
 
-  // Two tiles per trip so each buffer's LDS offset is a compile-time constant.
-  for (int jt = 0; jt < ntiles; jt += 2) {
-    if (jt + 1 < ntiles) issue_tile<D>(rk, rv, lds + T::BUF, voff_k, voff_v, wave_u, (unsigned)(jt + 1) * tile_bytes);
-    tile_body(lds, jt);
+  f32x16 sa[2], sb[2];
+  if (ntiles > 0) {
+    issue_tile<D>(rk, kbuf0, voff_k, wave_u, 0u);
+    issue_tile<D>(rv, vbuf0, voff_v, wave_u, 0u);
+    if (ntiles > 1) issue_tile<D>(rk, kbuf1, voff_k, wave_u, tile_bytes);
     wait_vmcnt0();
     __syncthreads();
-    if (jt + 1 >= ntiles) break;
-    if (jt + 2 < ntiles) issue_tile<D>(rk, rv, lds, voff_k, voff_v, wave_u, (unsigned)(jt + 2) * tile_bytes);
-    tile_body(lds + T::BUF, jt + 1);
+    qk(kbuf0, sa);
+    __syncthreads();  // everyone is done with K(0) before K(2) overwrites it
+  }
+
+  // One pipeline stage: tile jt with scores `cur`, producing `nxt` for jt + 1
+  // (LAST: tile jt is the final tile, nothing to produce).  K(jt+1) lives in
+  // kb_next, V(jt) in vb_cur; K(jt+2) goes to kb_free and V(jt+1) to vb_free.
+  auto stage = [&](auto last_tag, int jt, f32x16 (&cur)[2], f32x16 (&nxt)[2], const unsigned char* kb_next,
+                   unsigned char* kb_free, const unsigned char* vb_cur, unsigned char* vb_free) {
+    constexpr bool LAST = decltype(last_tag)::value;
+    if (!LAST) {
+      if (jt + 2 < ntiles) issue_tile<D>(rk, kb_free, voff_k, wave_u, (unsigned)(jt + 2) * tile_bytes);
+      issue_tile<D>(rv, vb_free, voff_v, wave_u, (unsigned)(jt + 1) * tile_bytes);
+    }
+    const float m_use = prepare(cur, jt);
+    bf16x8 pk[2][2];
+    if (!LAST) {
+      qk_softmax(kb_next, nxt, cur, m_use, pk);
+    } else {
+      softmax(cur, m_use, pk);
+    }
+    pv(vb_cur, pk);
     wait_vmcnt0();
     __syncthreads();
+  };
+
+  using Mid = std::integral_constant<bool, false>;
+  using Last = std::integral_constant<bool, true>;
+  // Two tiles per trip so every buffer address is a compile-time offset.
+  int jt = 0;
+  for (; jt + 2 < ntiles; jt += 2) {
+    stage(Mid{}, jt, sa, sb, kbuf1, kbuf0, vbuf0, vbuf1);
+    stage(Mid{}, jt + 1, sb, sa, kbuf0, kbuf1, vbuf1, vbuf0);
+  }
+  if (jt + 1 < ntiles) {  // two tiles left: jt (buffer parity 0) and the last
+    stage(Mid{}, jt, sa, sb, kbuf1, kbuf0, vbuf0, vbuf1);
+    stage(Last{}, jt + 1, sb, sa, kbuf0, kbuf1, vbuf1, vbuf0);
+  } else if (jt < ntiles) {  // one tile left
+    stage(Last{}, jt, sa, sb, kbuf1, kbuf0, vbuf0, vbuf1);
   }
 
   // Combine the two halves' partial sums (they saw disjoint keys).

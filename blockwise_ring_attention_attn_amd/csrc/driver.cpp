@@ -279,17 +279,22 @@ hipError_t copy2d(void* dst, size_t dpitch, const void* src, size_t spitch, size
 }
 
 // dst <- src shifted by one host (host r receives host r-1's block), both in
-// natural row order [planes, N, d].
+// natural row order [planes, N, d].  Only the receiving hosts r in
+// [r_lo, P) are written (a contiguous causal ring never reads the staging
+// rows of hosts that have finished, see plan_step).
 hipError_t ring_shift(void* dst, const void* src, int layout, int64_t planes, int64_t N, int64_t Bl,
-                      int P, size_t row_bytes, hipStream_t s) {
+                      int P, int r_lo, size_t row_bytes, hipStream_t s) {
   char* D = static_cast<char*>(dst);
   const char* S = static_cast<const char*>(src);
   hipError_t e;
   if (layout == RA_CONTIGUOUS) {
     const size_t plane = (size_t)N * row_bytes;
-    // rows [Bl, N) <- [0, N - Bl);  rows [0, Bl) <- [N - Bl, N)
-    e = copy2d(D + Bl * row_bytes, plane, S, plane, (size_t)(N - Bl) * row_bytes, planes, s);
-    if (e != hipSuccess) return e;
+    // rows [max(r_lo, 1) Bl, N) <- the rows one block earlier
+    const int64_t lo = (r_lo > 1 ? r_lo : 1) * Bl;
+    e = copy2d(D + lo * row_bytes, plane, S + (lo - Bl) * row_bytes, plane, (size_t)(N - lo) * row_bytes,
+               planes, s);
+    if (e != hipSuccess || r_lo > 0) return e;
+    // host 0 receives from host P-1: rows [0, Bl) <- [N - Bl, N)
     return copy2d(D, plane, S + (N - Bl) * row_bytes, plane, (size_t)Bl * row_bytes, planes, s);
   }
   // striped: within every group of P consecutive rows, row r <- row r-1, row 0 <- row P-1
@@ -394,8 +399,12 @@ ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, 
       if (s >= 1) RA_HIP(hipStreamWaitEvent(ctx->copy, ctx->done[(s - 1) & 1], 0), "hipStreamWaitEvent");
       void* kd = wsb + W.off_stage[(s + 1) & 1];
       void* vd = wsb + W.off_stage[(s + 1) & 1] + W.kv_bytes;
-      RA_HIP(ring_shift(kd, kbuf(s), layout, (int64_t)B * Hkv, N, Bl, P, row_bytes, ctx->copy), "staging copy");
-      RA_HIP(ring_shift(vd, vbuf(s), layout, (int64_t)B * Hkv, N, Bl, P, row_bytes, ctx->copy), "staging copy");
+      // Receivers that still have work at step s + 1 (all hosts unless the
+      // ring is contiguous and causal, where hosts below s + 1 are done).
+      const StepPlan nxt = plan_step(layout, a.causal, P, s + 1, Bl);
+      const int r_lo = (layout == RA_CONTIGUOUS && a.causal) ? nxt.host_lo : 0;
+      RA_HIP(ring_shift(kd, kbuf(s), layout, (int64_t)B * Hkv, N, Bl, P, r_lo, row_bytes, ctx->copy), "staging copy");
+      RA_HIP(ring_shift(vd, vbuf(s), layout, (int64_t)B * Hkv, N, Bl, P, r_lo, row_bytes, ctx->copy), "staging copy");
       RA_HIP(hipEventRecord(ctx->copied[(s + 1) & 1], ctx->copy), "hipEventRecord");
     }
     // Compute stream: step s.
