@@ -121,11 +121,27 @@ __device__ __forceinline__ int64_t q_row_index(const StepArgs& A, const Work& w,
   return ((int64_t)w.b * A.H + w.h) * A.q_plane_rows + row;
 }
 
+// First row (within the k / v array) of this workgroup's kv block and the
+// row stride between consecutive keys of the block.
+__device__ __forceinline__ void kv_block_rows(const StepArgs& A, const Work& w, int64_t& first, int64_t& stride) {
+  const int64_t plane = (int64_t)w.b * A.Hkv + w.hkv;
+  if (A.kv_mode == ROWS_COMPACT) {
+    first = plane * A.kv_plane_rows;
+    stride = 1;
+  } else if (A.kv_mode == ROWS_HOST_MAJOR) {
+    first = ((int64_t)w.q_rank * A.B * A.Hkv + plane) * A.kv_plane_rows;
+    stride = 1;
+  } else {
+    const int rk = A.kv_mode == ROWS_HOST_Q ? w.q_rank : w.kv_rank;
+    first = plane * A.kv_plane_rows + (A.layout == 0 ? (int64_t)rk * A.Lkv : rk);
+    stride = A.layout == 0 ? 1 : A.P;
+  }
+}
+
 __device__ __forceinline__ int64_t kv_row_index(const StepArgs& A, const Work& w, int64_t j) {
-  int64_t row;
-  if (A.kv_mode == ROWS_COMPACT) row = j;
-  else row = host_row(A.layout, A.kv_mode == ROWS_HOST_Q ? w.q_rank : w.kv_rank, j, A.Lkv, A.P);
-  return ((int64_t)w.b * A.Hkv + w.hkv) * A.kv_plane_rows + row;
+  int64_t first, stride;
+  kv_block_rows(A, w, first, stride);
+  return first + j * stride;
 }
 
 // Epilogue.  The previous state of a row (earlier ring steps) is read once,
@@ -269,7 +285,6 @@ __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rsrc, unsigned
 template <int D, typename OutT>
 __global__ __launch_bounds__(kThreads, kWgPerCu) void step_bf16_kernel(StepArgs A) {
   using T = Tile<D>;
-  extern __shared__ __align__(1024) unsigned char lds[];
   const Work w = decode_work(A);
   const int lane = threadIdx.x & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -287,16 +302,8 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void step_bf16_kernel(StepArgs 
 
   // Buffer descriptors covering exactly the kv block's rows of this plane:
   // row j sits at byte j * rstride * RB; rows j >= Lkv read as zero.
-  int64_t row0, rstride;
-  if (A.kv_mode == ROWS_COMPACT) {
-    row0 = 0;
-    rstride = 1;
-  } else {
-    const int rk = A.kv_mode == ROWS_HOST_Q ? w.q_rank : w.kv_rank;
-    row0 = A.layout == 0 ? (int64_t)rk * A.Lkv : rk;
-    rstride = A.layout == 0 ? 1 : A.P;
-  }
-  const int64_t plane_row = ((int64_t)w.b * A.Hkv + w.hkv) * A.kv_plane_rows + row0;
+  int64_t plane_row, rstride;
+  kv_block_rows(A, w, plane_row, rstride);
   const unsigned nrec = (unsigned)(((int64_t)(A.Lkv - 1) * rstride + 1) * T::RB);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(A.k)) + plane_row * D, 0, nrec,
@@ -356,22 +363,26 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void step_bf16_kernel(StepArgs 
   // on the MFMA pipe while the VALU turns S(j) into P(j), then O += V(j)^T P(j).
   // K tiles therefore run one tile ahead of V tiles: during iteration j the
   // loads of K(j+2) and V(j+1) are in flight, K(j+1) and V(j) are read.
-  unsigned char* kbuf0 = lds;
-  unsigned char* kbuf1 = lds + T::BYTES;
-  unsigned char* vbuf0 = lds + T::VOFF;
-  unsigned char* vbuf1 = lds + T::VOFF + T::BYTES;
+  // Four separate LDS objects, so that reads of one buffer are not ordered
+  // behind direct-to-LDS loads that target another.
+  __shared__ __align__(1024) unsigned char kbuf0[T::BYTES];
+  __shared__ __align__(1024) unsigned char kbuf1[T::BYTES];
+  __shared__ __align__(1024) unsigned char vbuf0[T::BYTES];
+  __shared__ __align__(1024) unsigned char vbuf1[T::BYTES];
 
+  // The two key blocks' accumulator chains alternate, so consecutive MFMAs
+  // never depend on each other.
   auto qk = [&](const unsigned char* kb_lds, f32x16 (&s)[2]) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
+    for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
+      for (int kb = 0; kb < 2; ++kb) {
         const unsigned char* p = kb_lds + kaddr[ks] + kb * 32 * T::RB;
         const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
-    }
   };
 
   // Mask, row max and (lazy) rescale of tile jt's scores; returns the
@@ -439,8 +450,9 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void step_bf16_kernel(StepArgs 
     constexpr int KS = D / 16;
     constexpr int NSTEP = 2 * KS;            // (kb, ks) pairs
     constexpr int EPS = 32 / NSTEP;          // score elements per step (2 or 4)
+    // step i: key block i % 2, dim slice i / 2 (the two chains alternate)
     auto kread = [&](int i) -> bf16x8 {
-      const int kb = i / KS, ks = i % KS;
+      const int kb = i & 1, ks = i >> 1;
       return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kb_lds + kaddr[ks] + kb * 32 * T::RB));
     };
     nxt[0] = f32x16{};
@@ -452,7 +464,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void step_bf16_kernel(StepArgs 
 #pragma unroll
     for (int i = 0; i < NSTEP; ++i) {
       if (i + 2 < NSTEP) kf[(i + 2) % 3] = kread(i + 2);
-      const int kb = i / KS, ks = i % KS;
+      const int kb = i & 1, ks = i >> 1;
       nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[ks], nxt[kb], 0, 0, 0);
 #pragma unroll
       for (int t = 0; t < EPS; t += 2) {
@@ -651,9 +663,9 @@ hipError_t launch_step_bf16(const StepArgs& a, int d, hipStream_t s) {
   const int g = grid_size(a);
   if (g <= 0) return hipSuccess;
   if (d == 128) {
-    hipLaunchKernelGGL((step_bf16_kernel<128, __bf16>), dim3(g), dim3(kThreads), Tile<128>::LDS_BYTES, s, a);
+    hipLaunchKernelGGL((step_bf16_kernel<128, __bf16>), dim3(g), dim3(kThreads), 0, s, a);
   } else if (d == 64) {
-    hipLaunchKernelGGL((step_bf16_kernel<64, __bf16>), dim3(g), dim3(kThreads), Tile<64>::LDS_BYTES, s, a);
+    hipLaunchKernelGGL((step_bf16_kernel<64, __bf16>), dim3(g), dim3(kThreads), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -278,31 +278,44 @@ hipError_t copy2d(void* dst, size_t dpitch, const void* src, size_t spitch, size
   return hipMemcpy2DAsync(dst, dpitch, src, spitch, width, height, hipMemcpyDeviceToDevice, s);
 }
 
-// dst <- src shifted by one host (host r receives host r-1's block), both in
-// natural row order [planes, N, d].  Only the receiving hosts r in
-// [r_lo, P) are written (a contiguous causal ring never reads the staging
-// rows of hosts that have finished, see plan_step).
-hipError_t ring_shift(void* dst, const void* src, int layout, int64_t planes, int64_t N, int64_t Bl,
-                      int P, int r_lo, size_t row_bytes, hipStream_t s) {
+// Staging buffers of ring_attn_fwd are host-major: [P hosts][planes][Bl][d],
+// host r's current kv block contiguous at r * host_bytes.
+//
+// First hand-off: staging[r] <- host (r-1) mod P's block of the natural-order
+// array, for receivers r in [r_lo, P).
+hipError_t ring_gather_first(void* dst, const void* src, int layout, int64_t planes, int64_t N, int64_t Bl,
+                             int P, int r_lo, size_t row_bytes, hipStream_t s) {
   char* D = static_cast<char*>(dst);
   const char* S = static_cast<const char*>(src);
-  hipError_t e;
-  if (layout == RA_CONTIGUOUS) {
-    const size_t plane = (size_t)N * row_bytes;
-    // rows [max(r_lo, 1) Bl, N) <- the rows one block earlier
-    const int64_t lo = (r_lo > 1 ? r_lo : 1) * Bl;
-    e = copy2d(D + lo * row_bytes, plane, S + (lo - Bl) * row_bytes, plane, (size_t)(N - lo) * row_bytes,
-               planes, s);
-    if (e != hipSuccess || r_lo > 0) return e;
-    // host 0 receives from host P-1: rows [0, Bl) <- [N - Bl, N)
-    return copy2d(D, plane, S + (N - Bl) * row_bytes, plane, (size_t)Bl * row_bytes, planes, s);
+  const size_t host_bytes = (size_t)planes * Bl * row_bytes;
+  for (int r = r_lo; r < P; ++r) {
+    const int from = (r + P - 1) % P;
+    hipError_t e;
+    if (layout == RA_CONTIGUOUS) {
+      e = copy2d(D + r * host_bytes, (size_t)Bl * row_bytes, S + (size_t)from * Bl * row_bytes,
+                 (size_t)N * row_bytes, (size_t)Bl * row_bytes, planes, s);
+    } else {
+      e = copy2d(D + r * host_bytes, row_bytes, S + (size_t)from * row_bytes, (size_t)P * row_bytes, row_bytes,
+                 (size_t)planes * Bl, s);
+    }
+    if (e != hipSuccess) return e;
   }
-  // striped: within every group of P consecutive rows, row r <- row r-1, row 0 <- row P-1
-  const size_t grp = (size_t)P * row_bytes;
-  const size_t groups = (size_t)planes * Bl;
-  e = copy2d(D + row_bytes, grp, S, grp, (size_t)(P - 1) * row_bytes, groups, s);
-  if (e != hipSuccess) return e;
-  return copy2d(D, grp, S + (size_t)(P - 1) * row_bytes, grp, row_bytes, groups, s);
+  return hipSuccess;
+}
+
+// Later hand-offs: dst[r] <- src[r-1] for receivers r in [r_lo, P) (one
+// contiguous move), and dst[0] <- src[P-1] when host 0 receives.
+hipError_t ring_shift(void* dst, const void* src, int64_t planes, int64_t Bl, int P, int r_lo, size_t row_bytes,
+                      hipStream_t s) {
+  char* D = static_cast<char*>(dst);
+  const char* S = static_cast<const char*>(src);
+  const size_t host_bytes = (size_t)planes * Bl * row_bytes;
+  const int lo = r_lo > 1 ? r_lo : 1;
+  hipError_t e = hipSuccess;
+  if (lo < P) e = hipMemcpyAsync(D + lo * host_bytes, S + (lo - 1) * host_bytes, (P - lo) * host_bytes,
+                                 hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess || r_lo > 0) return e;
+  return hipMemcpyAsync(D, S + (size_t)(P - 1) * host_bytes, host_bytes, hipMemcpyDeviceToDevice, s);
 }
 
 // dst (compact [planes, Bl, d]) <- block `kv` of src (natural [planes, N, d]).
@@ -400,11 +413,18 @@ ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, 
       void* kd = wsb + W.off_stage[(s + 1) & 1];
       void* vd = wsb + W.off_stage[(s + 1) & 1] + W.kv_bytes;
       // Receivers that still have work at step s + 1 (all hosts unless the
-      // ring is contiguous and causal, where hosts below s + 1 are done).
+      // ring is contiguous and causal, where hosts below s + 1 are done;
+      // their staging slots are never read again).
       const StepPlan nxt = plan_step(layout, a.causal, P, s + 1, Bl);
       const int r_lo = (layout == RA_CONTIGUOUS && a.causal) ? nxt.host_lo : 0;
-      RA_HIP(ring_shift(kd, kbuf(s), layout, (int64_t)B * Hkv, N, Bl, P, r_lo, row_bytes, ctx->copy), "staging copy");
-      RA_HIP(ring_shift(vd, vbuf(s), layout, (int64_t)B * Hkv, N, Bl, P, r_lo, row_bytes, ctx->copy), "staging copy");
+      const int64_t planes = (int64_t)B * Hkv;
+      if (s == 0) {
+        RA_HIP(ring_gather_first(kd, k, layout, planes, N, Bl, P, r_lo, row_bytes, ctx->copy), "staging copy");
+        RA_HIP(ring_gather_first(vd, v, layout, planes, N, Bl, P, r_lo, row_bytes, ctx->copy), "staging copy");
+      } else {
+        RA_HIP(ring_shift(kd, kbuf(s), planes, Bl, P, r_lo, row_bytes, ctx->copy), "staging copy");
+        RA_HIP(ring_shift(vd, vbuf(s), planes, Bl, P, r_lo, row_bytes, ctx->copy), "staging copy");
+      }
       RA_HIP(hipEventRecord(ctx->copied[(s + 1) & 1], ctx->copy), "hipEventRecord");
     }
     // Compute stream: step s.
@@ -412,6 +432,8 @@ ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, 
     const StepPlan sp = plan_step(layout, a.causal, P, s, Bl);
     a.k = kbuf(s);
     a.v = vbuf(s);
+    a.kv_mode = s == 0 ? ROWS_HOST_Q : ROWS_HOST_MAJOR;
+    a.kv_plane_rows = s == 0 ? N : Bl;
     a.host_lo = sp.host_lo;
     a.n_hosts = sp.n_hosts;
     a.kv_shift = s;

@@ -11,6 +11,7 @@ enum RowMode : int {
   ROWS_COMPACT = 0,   // row = i                        (a compact block)
   ROWS_HOST_Q = 1,    // row = host_row(q_rank, i)      (natural order array)
   ROWS_HOST_KV = 2,   // row = host_row(kv_rank, i)     (natural order array)
+  ROWS_HOST_MAJOR = 3 // row = i of plane (q_rank * B + b) * Hkv + hkv (host-major staging)
 };
 
 // One launch of the fused block-attention step kernel.  A launch covers
