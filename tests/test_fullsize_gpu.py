@@ -1,0 +1,118 @@
+"""GPU parity at full workload sizes, in the launch configuration bench.py times.
+
+The HIP library runs the whole problem; the fp64 oracle recomputes a seeded
+sample of query rows (rows are independent, so the check is exact for those
+rows): the first and last rows of every virtual host block, rows around
+query-tile boundaries, and random rows.  Tolerances: bf16 max|dO| <= 1e-2,
+max|dlse| <= 1e-3.
+
+Workloads (all bf16, N(0, 1) inputs from the seeded generator):
+  prefill   B=1 H=32 N=32768 d=128 causal, contiguous, P=8
+  gqa       B=1 H=8 Hkv=2 N=131072 d=128 causal, striped, P=8
+  share     rank 7 of a P=8 ring over N=1,048,576: q 131072 tokens, H=4, causal
+  decode    B=16 H=32 Hkv=8 L=262144 d=128, P=8 ring blocks
+"""
+import math
+import time
+
+import numpy as np
+import pytest
+
+import blockwise_ring_attention_attn_amd as ra
+import oracle
+import synth
+from _util import assert_close, from_dev, host_vals, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(f"\n[fullsize] {msg}", flush=True)
+
+
+@pytest.mark.parametrize("name,seed,B,H,Hkv,N,d,P,layout,nh", [
+    ("prefill", 2, 1, 32, 32, 32768, 128, 8, "contiguous", 3),
+    ("gqa", 3, 1, 8, 2, 131072, 128, 8, "striped", 3),
+])
+def test_ring_fwd_fullsize(name, seed, B, H, Hkv, N, d, P, layout, nh):
+    import torch
+    _log(f"{name}: generating B={B} H={H}/{Hkv} N={N} d={d} P={P} {layout}")
+    t0 = time.time()
+    q, k, v = synth.qkv(seed, B, H, Hkv, N, d, "bf16")
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    _log(f"{name}: inputs ready in {time.time() - t0:.1f} s; running ring_attn_fwd")
+    out, lse = ra.ring_attn_fwd(qd, kd, vd, P=P, causal=True, layout=layout)
+    torch.cuda.synchronize()
+    rows = sample_rows(N, P, layout, 256, seed)
+    heads = sorted({0, H - 1} | set(int(x) for x in np.random.default_rng(seed).integers(0, H, nh)))
+    rows_t = torch.from_numpy(rows).to(out.device)
+    got_o = from_dev(out.index_select(2, rows_t))
+    got_l = from_dev(lse.index_select(2, rows_t))
+    del qd, kd, vd, out, lse
+    torch.cuda.empty_cache()
+    _log(f"{name}: oracle on {len(rows)} rows x {len(heads)} heads")
+    Ow, Lw = oracle.attention(host_vals(q, "bf16"), host_vals(k, "bf16"), host_vals(v, "bf16"),
+                              scale=1 / math.sqrt(d), causal=True, rows=rows, heads=[(0, h) for h in heads])
+    eo, el = assert_close(got_o[:, heads], got_l[:, heads], Ow[:, heads], Lw[:, heads], "bf16", name)
+    _log(f"{name}: max|dO|={eo:.2e} max|dlse|={el:.2e}")
+
+
+def test_share_fullsize_1M():
+    """Rank 7's share of a 1,048,576-token causal ring (P=8), H=4, d=128."""
+    import torch
+    B, H, Hkv, N, d, P, rank, seed = 1, 4, 4, 1 << 20, 128, 8, 7, 4
+    Bl = N // P
+    _log("share: generating q (rank 7 block) and k, v (1M tokens)")
+    q = synth.tensor(seed, synth.TENSOR_Q, B, H, Bl, d, "bf16")
+    k = synth.tensor(seed, synth.TENSOR_K, B, Hkv, N, d, "bf16")
+    v = synth.tensor(seed, synth.TENSOR_V, B, Hkv, N, d, "bf16")
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    _log("share: running ring_attn_fwd_share")
+    out, lse = ra.ring_attn_fwd_share(qd, kd, vd, P=P, rank=rank, causal=True, layout="contiguous")
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, 3), np.arange(Bl - 3, Bl), np.arange(127, 130),
+                                     np.random.default_rng(seed).integers(0, Bl, 40)]))
+    rows_t = torch.from_numpy(rows).to(out.device)
+    got_o = from_dev(out.index_select(2, rows_t))
+    got_l = from_dev(lse.index_select(2, rows_t))
+    del qd, kd, vd, out, lse
+    torch.cuda.empty_cache()
+    heads = [0, H - 1]
+    _log(f"share: oracle on {len(rows)} rows x {len(heads)} heads against {N} keys")
+    qpos = rank * Bl + np.arange(Bl)
+    Ow, Lw = oracle.attention(host_vals(q, "bf16"), host_vals(k, "bf16"), host_vals(v, "bf16"), causal=True,
+                              q_pos=qpos, rows=rows, heads=[(0, h) for h in heads])
+    eo, el = assert_close(got_o[:, heads], got_l[:, heads], Ow[:, heads], Lw[:, heads], "bf16", "share 1M")
+    _log(f"share: max|dO|={eo:.2e} max|dlse|={el:.2e}")
+
+
+def test_decode_fullsize():
+    """16 sequences x 1 token, H=32 / Hkv=8, L=262144, P=8 ring blocks."""
+    import torch
+    B, H, Hkv, L, d, P, seed = 16, 32, 8, 262144, 128, 8, 5
+    _log("decode: generating q and the 2 x 8.6 GB k, v cache")
+    t0 = time.time()
+    q = synth.tensor(seed, synth.TENSOR_Q, B, H, 1, d, "bf16")
+    qd = to_dev(q, "bf16")
+    k = synth.tensor(seed, synth.TENSOR_K, B, Hkv, L, d, "bf16")
+    kd = to_dev(k, "bf16")
+    del k
+    v = synth.tensor(seed, synth.TENSOR_V, B, Hkv, L, d, "bf16")
+    vd = to_dev(v, "bf16")
+    del v
+    _log(f"decode: inputs ready in {time.time() - t0:.1f} s; running ring_attn_decode")
+    out, lse = ra.ring_attn_decode(qd, kd, vd, P=P)
+    torch.cuda.synchronize()
+    got_o, got_l = from_dev(out), from_dev(lse)
+    del qd, kd, vd, out, lse
+    torch.cuda.empty_cache()
+    group = H // Hkv
+    pairs = [(0, 0), (0, H - 1), (B - 1, 5), (7, 17), (11, 30)]
+    for b, h in pairs:
+        g = h // group
+        kk = synth.as_f32(synth.slab_bits(seed, synth.TENSOR_K, b, g, L, d), "bf16")
+        vv = synth.as_f32(synth.slab_bits(seed, synth.TENSOR_V, b, g, L, d), "bf16")
+        qq = host_vals(q[b:b + 1, h:h + 1], "bf16")
+        Ow, Lw = oracle.decode(qq, kk[None, None], vv[None, None])
+        assert_close(got_o[b, h, 0], got_l[b, h], Ow[0, 0, 0], Lw[0, 0, 0], "bf16", f"decode b={b} h={h}")
+    _log(f"decode: {len(pairs)} (sequence, head) pairs match")
