@@ -17,6 +17,7 @@ resident in HBM.  Prints ONE JSON line:
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -33,6 +34,37 @@ METRIC = "causal ring-attn fwd TFLOP/s + % bf16 MFMA peak; split-KV decode HBM G
 
 PREFILL = dict(B=1, H=32, Hkv=32, N=32768, d=128, P=8, layout="contiguous", causal=True, seed=2)
 DECODE = dict(B=16, H=32, Hkv=8, L=262144, d=128, P=8, seed=5)
+
+
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "blockwise_ring_attention_attn_amd", "csrc")
+
+
+def source_sha(name: str) -> str:
+    return hashlib.sha256(open(os.path.join(CSRC, name), "rb").read()).hexdigest()
+
+
+def measured_traffic(kernel: str, source: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/traffic.json), or None if the kernel source changed since."""
+    try:
+        rec = json.load(open(os.path.join(PROFILES, "traffic.json")))[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_sha(source):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def calibration_copy(mib: int) -> None:
+    """A plain device-to-device copy of known size, for counter calibration."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def prefill_flops(c) -> float:
@@ -129,7 +161,8 @@ def run_prefill(args) -> dict:
     res = {
         "value": tflops, "ms_per_step": ms, "wall_s": wall, "flops": flops,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": measured_traffic("step_bf16_kernel<128>", "attn_step.hip"),
                      "kernel": "step_bf16_kernel<128>", "launches_per_step": launches / args.steps,
                      "mean_launch_ms": kern_ms,
                      "flops_per_launch": prof["step_flops"] / max(1, launches)},
@@ -187,7 +220,8 @@ def run_decode(args) -> dict:
         "config": {"workload": "decode: 16 sequences x 1 query token, H=32 / Hkv=8, L=262144, d=128, "
                                "P=8 ring blocks, bf16", **c},
         "roofline": {"bound": "hbm", "achieved": kern_achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": kern_achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": kern_achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("decode_partial_kernel<128>", "decode.hip"),
                      "kernel": "decode_partial_kernel<128>",
                      "mean_launch_ms": prof["decode_ms"] / max(1, prof["decode_launches"]),
                      "bytes_per_launch": prof["decode_bytes"] / max(1, prof["decode_launches"])},
@@ -202,6 +236,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only", choices=("prefill", "decode"), default=None,
+                    help="run one workload only (profiling runs)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first do a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -211,6 +249,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.calib_copy_mib:
+        calibration_copy(args.calib_copy_mib)
+    if args.only == "decode":
+        print(json.dumps(run_decode(args)), flush=True)
+        return
     pre = run_prefill(args)
     c = PREFILL
     line = {
@@ -236,7 +279,7 @@ def main():
     }
     if "cpu_baseline" in pre:
         line["cpu_baseline"] = pre["cpu_baseline"]
-    if not args.no_decode:
+    if not args.no_decode and args.only is None:
         line["decode"] = run_decode(args)
     print(json.dumps(line), flush=True)
 
