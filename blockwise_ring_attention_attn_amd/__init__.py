@@ -25,7 +25,7 @@ EXPORTS = (
     "ring_attn_fwd_share_ws_bytes", "ring_attn_fwd_share",
     "ring_attn_step", "ring_attn_finalize", "lse_merge",
     "ring_attn_decode_ws_bytes", "ring_attn_decode",
-    "ra_last_error", "ra_version", "ra_prof_enable", "ra_prof_reset", "ra_prof_read",
+    "ra_last_error", "ra_version", "ra_debug_set_delays", "ra_prof_enable", "ra_prof_reset", "ra_prof_read",
 )
 
 
@@ -82,6 +82,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.ra_last_error.restype = ctypes.c_char_p
     lib.ra_version.argtypes = []
     lib.ra_version.restype = ctypes.c_char_p
+    lib.ra_debug_set_delays.argtypes = [i, i]
+    lib.ra_debug_set_delays.restype = i
     lib.ra_prof_enable.argtypes = [i]
     lib.ra_prof_enable.restype = i
     lib.ra_prof_reset.argtypes = []
@@ -268,6 +270,11 @@ def ring_attn_decode(q, k, v, *, P: int, scale: float | None = None, out=None, l
     _check(lib.ring_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, L, d, P, scale,
                                 code, _stream(stream), _ptr(wst) if wst is not None else None, nb))
     return out, lse
+
+
+def debug_set_delays(compute_us: int = 0, copy_us: int = 0) -> None:
+    """Test hook: bounded spins before every step kernel / staging copy."""
+    _check(load().ra_debug_set_delays(int(compute_us), int(copy_us)))
 
 
 def prof_enable(on: bool = True) -> None:

@@ -71,6 +71,7 @@ struct DeviceCtx {
 
 std::mutex g_mu;
 DeviceCtx g_dev[kMaxDevices];
+int g_delay_compute_us = 0, g_delay_copy_us = 0;  // test hook (ra_debug_set_delays)
 
 ra_status get_ctx(DeviceCtx** out) {
   int dev = 0;
@@ -418,6 +419,7 @@ ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, 
       const StepPlan nxt = plan_step(layout, a.causal, P, s + 1, Bl);
       const int r_lo = (layout == RA_CONTIGUOUS && a.causal) ? nxt.host_lo : 0;
       const int64_t planes = (int64_t)B * Hkv;
+      RA_HIP(launch_spin(g_delay_copy_us, ctx->copy), "delay");
       if (s == 0) {
         RA_HIP(ring_gather_first(kd, k, layout, planes, N, Bl, P, r_lo, row_bytes, ctx->copy), "staging copy");
         RA_HIP(ring_gather_first(vd, v, layout, planes, N, Bl, P, r_lo, row_bytes, ctx->copy), "staging copy");
@@ -440,7 +442,10 @@ ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, 
     a.has_prev = s > 0 ? 1 : 0;
     a.fin_lo = sp.fin_lo;
     a.fin_hi = sp.fin_hi;
-    if (sp.n_hosts > 0) RA_HIP(launch_step(a, d, dtype, cs, step_flops(a, d)), "step kernel launch");
+    if (sp.n_hosts > 0) {
+      RA_HIP(launch_spin(g_delay_compute_us, cs), "delay");
+      RA_HIP(launch_step(a, d, dtype, cs, step_flops(a, d)), "step kernel launch");
+    }
     if (s + 2 < P) RA_HIP(hipEventRecord(ctx->done[s & 1], cs), "hipEventRecord");
   }
   return RA_OK;
@@ -513,6 +518,7 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
       if (i >= 1) RA_HIP(hipStreamWaitEvent(ctx->copy, ctx->done[(i - 1) & 1], 0), "hipStreamWaitEvent");
       void* kd = wsb + W.off_stage[(i + 1) & 1];
       void* vd = wsb + W.off_stage[(i + 1) & 1] + W.kv_bytes;
+      RA_HIP(launch_spin(g_delay_copy_us, ctx->copy), "delay");
       RA_HIP(gather_block(kd, k, layout, (int64_t)B * Hkv, N, Bl, P, kv1, row_bytes, ctx->copy), "staging copy");
       RA_HIP(gather_block(vd, v, layout, (int64_t)B * Hkv, N, Bl, P, kv1, row_bytes, ctx->copy), "staging copy");
       RA_HIP(hipEventRecord(ctx->copied[(i + 1) & 1], ctx->copy), "hipEventRecord");
@@ -533,6 +539,7 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
     a.has_prev = i > 0 ? 1 : 0;
     a.fin_lo = (i == n - 1) ? rank : 0;
     a.fin_hi = (i == n - 1) ? rank + 1 : 0;
+    RA_HIP(launch_spin(g_delay_compute_us, cs), "delay");
     RA_HIP(launch_step(a, d, dtype, cs, step_flops(a, d)), "step kernel launch");
     if (i + 2 < n) RA_HIP(hipEventRecord(ctx->done[i & 1], cs), "hipEventRecord");
   }
@@ -688,6 +695,15 @@ ra_status ring_attn_decode(const void* q, const void* k, const void* v, void* ou
     RA_HIP(launch_decode_partial(a, d, 1, cs), "decode partial launch");
   }
   RA_HIP(launch_decode_merge(a, d, 1, cs), "decode merge launch");
+  return RA_OK;
+}
+
+ra_status ra_debug_set_delays(int compute_us, int copy_us) {
+  if (compute_us < 0 || copy_us < 0 || compute_us > 100000 || copy_us > 100000)
+    return fail(RA_EINVAL, "delays must be in [0, 100000] us");
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_delay_compute_us = compute_us;
+  g_delay_copy_us = copy_us;
   return RA_OK;
 }
 

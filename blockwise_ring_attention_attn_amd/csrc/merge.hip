@@ -55,7 +55,28 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs A) {
   if (lane == 0) A.lse[row] = l > 0.f ? m + __builtin_amdgcn_logf(l) * kLn2 : kNegInf;
 }
 
+// Busy-waits for about `us` microseconds of the 100 MHz constant clock
+// (s_memrealtime).  The iteration count is bounded (each iteration takes well
+// over 1/64 us), so the kernel always ends.
+__global__ void spin_kernel(int us, unsigned* sink) {
+  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+  const unsigned long long ticks = (unsigned long long)us * 100ull;
+  const unsigned bound = (unsigned)us * 64u + 1024u;
+  unsigned n = 0;
+  for (unsigned it = 0; it < bound; ++it) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 >= ticks) break;
+    ++n;
+  }
+  if (n == 0xffffffffu) sink[0] = n;  // never true; keeps the loop
+}
+
 }  // namespace
+
+hipError_t launch_spin(int microseconds, hipStream_t s) {
+  if (microseconds <= 0) return hipSuccess;
+  hipLaunchKernelGGL(spin_kernel, dim3(1), dim3(1), 0, s, microseconds, nullptr);
+  return hipGetLastError();
+}
 
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;

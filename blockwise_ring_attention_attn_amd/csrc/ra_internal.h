@@ -79,5 +79,6 @@ hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, int out_bf16, hipStream_t s);
 hipError_t launch_decode_partial(const DecodeArgs& a, int d, int bf16, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs& a, int d, int bf16, hipStream_t s);
+hipError_t launch_spin(int microseconds, hipStream_t s);  // bounded busy wait (test hook)
 
 }  // namespace ra

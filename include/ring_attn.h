@@ -188,6 +188,13 @@ ra_status ring_attn_decode(const void* q, const void* k, const void* v, void* ou
  * ---------------------------------------------------------------------- */
 const char* ra_last_error(void);
 const char* ra_version(void);
+
+/* Test hook for the ring driver's stream ordering: when set, every later
+ * ring_attn_fwd / ring_attn_fwd_share call enqueues a bounded spin of about
+ * `compute_us` microseconds on the compute stream before each step kernel and
+ * of about `copy_us` on the copy stream before each staging copy (0 = none,
+ * at most 100000).  Results must not change; only the timeline does. */
+ra_status ra_debug_set_delays(int compute_us, int copy_us);
 ra_status ra_prof_enable(int on);
 ra_status ra_prof_reset(void);
 ra_status ra_prof_read(double* out6);
