@@ -15,9 +15,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libringattn.so")
 
 RA_OK, RA_EINVAL, RA_ENOMEM, RA_EHIP, RA_EUNSUPPORTED = 0, 1, 2, 3, 4
-RA_CONTIGUOUS, RA_STRIPED = 0, 1
+RA_CONTIGUOUS, RA_STRIPED, RA_ZIGZAG = 0, 1, 2
 RA_F32, RA_BF16 = 0, 1
-LAYOUTS = {"contiguous": RA_CONTIGUOUS, "striped": RA_STRIPED}
+LAYOUTS = {"contiguous": RA_CONTIGUOUS, "striped": RA_STRIPED, "zigzag": RA_ZIGZAG}
 
 # Every symbol declared in include/ring_attn.h.
 EXPORTS = (

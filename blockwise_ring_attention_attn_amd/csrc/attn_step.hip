@@ -49,8 +49,14 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;   // lazy-rescale threshold, base-2 units
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// Global token position of row i of host `rank`'s block (blk rows):
+// contiguous rank*blk + i; striped i*P + rank; zigzag: the block is chunks
+// rank and 2P-1-rank of 2P chunks of blk/2 tokens.
 __device__ __forceinline__ int64_t host_row(int layout, int rank, int64_t i, int blk, int P) {
-  return layout == 0 ? (int64_t)rank * blk + i : i * P + rank;
+  if (layout == 0) return (int64_t)rank * blk + i;
+  if (layout == 1) return i * P + rank;
+  const int64_t c = blk >> 1;
+  return i < c ? (int64_t)rank * c + i : (int64_t)(2 * P - 1 - rank) * c + (i - c);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -108,8 +114,19 @@ __device__ __forceinline__ int64_t key_limit(const StepArgs& A, const Work& w, i
     lim = A.Lkv - 1;
   } else if (A.layout == 0) {
     lim = (int64_t)w.q_rank * A.Lq + i - (int64_t)w.kv_rank * A.Lkv;
-  } else {
+  } else if (A.layout == 1) {
     lim = i - (w.kv_rank > w.q_rank ? 1 : 0);
+  } else {
+    // zigzag: the kv block's positions increase with the row index (its
+    // low chunk precedes its high chunk), so the visible keys are a prefix
+    // whose length counts the keys of each chunk at or before the query.
+    const int64_t c = A.Lkv >> 1;
+    const int64_t pos = host_row(2, w.q_rank, i, A.Lq, A.P);
+    int64_t na = pos - (int64_t)w.kv_rank * c + 1;
+    int64_t nb = pos - (int64_t)(2 * A.P - 1 - w.kv_rank) * c + 1;
+    na = na < 0 ? 0 : (na > c ? c : na);
+    nb = nb < 0 ? 0 : (nb > c ? c : nb);
+    lim = na + nb - 1;
   }
   if (lim > A.Lkv - 1) lim = A.Lkv - 1;
   if (lim < -1) lim = -1;
@@ -132,6 +149,8 @@ __device__ __forceinline__ void kv_block_rows(const StepArgs& A, const Work& w, 
     first = ((int64_t)w.q_rank * A.B * A.Hkv + plane) * A.kv_plane_rows;
     stride = 1;
   } else {
+    // natural-order source (contiguous or striped only; a zigzag block is
+    // two separate chunks and is always staged compactly first)
     const int rk = A.kv_mode == ROWS_HOST_Q ? w.q_rank : w.kv_rank;
     first = plane * A.kv_plane_rows + (A.layout == 0 ? (int64_t)rk * A.Lkv : rk);
     stride = A.layout == 0 ? 1 : A.P;

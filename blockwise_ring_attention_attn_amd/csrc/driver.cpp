@@ -151,11 +151,23 @@ int64_t clamp_prefix(int64_t x, int64_t M) {
   return M * (M + 1) / 2 + (x - M - 1) * M;
 }
 
+// Visible (query, key) pairs between two chunks of c tokens at global chunk
+// indices a (queries) and b (keys): all when b < a, the lower triangle with
+// the diagonal when b == a, none when b > a.
+int64_t chunk_pairs(int64_t a, int64_t b, int64_t c) {
+  return b < a ? c * c : (b == a ? c * (c + 1) / 2 : 0);
+}
+
 // Visible pairs between query block q_rank (Lq rows) and kv block kv_rank
 // (Lkv rows): query i sees keys j <= lim(i), lim(i) = i + c0 - 1.
 int64_t visible_pairs(int layout, int causal, int P, int q_rank, int kv_rank, int64_t Lq, int64_t Lkv) {
-  (void)P;
   if (!causal) return Lq * Lkv;
+  if (layout == RA_ZIGZAG) {
+    // blocks of two chunks each: q_rank and 2P-1-q_rank, kv_rank and 2P-1-kv_rank
+    const int64_t c = Lq / 2;
+    const int64_t qa = q_rank, qb = 2 * P - 1 - q_rank, ka = kv_rank, kb = 2 * P - 1 - kv_rank;
+    return chunk_pairs(qa, ka, c) + chunk_pairs(qa, kb, c) + chunk_pairs(qb, ka, c) + chunk_pairs(qb, kb, c);
+  }
   int64_t c0 = layout == RA_CONTIGUOUS ? (int64_t)q_rank * Lq - (int64_t)kv_rank * Lkv + 1
                                        : 1 - (kv_rank > q_rank ? 1 : 0);
   // sum_{i=0}^{Lq-1} clamp(i + c0, 0, Lkv)
@@ -213,7 +225,17 @@ StepPlan plan_step(int layout, int causal, int P, int s, int64_t Bl) {
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 size_t esize(ra_dtype t) { return t == RA_BF16 ? 2 : 4; }
 bool dtype_ok(int t) { return t == RA_F32 || t == RA_BF16; }
-bool layout_ok(int l) { return l == RA_CONTIGUOUS || l == RA_STRIPED; }
+bool layout_ok(int l) { return l == RA_CONTIGUOUS || l == RA_STRIPED || l == RA_ZIGZAG; }
+
+// Zigzag blocks are two chunks of N / (2P) tokens.  With one host the block
+// is the whole sequence in natural order, i.e. the contiguous layout.
+ra_status check_layout(int layout, long long N, int P) {
+  if (!layout_ok(layout)) return fail(RA_EINVAL, "unknown layout %d", layout);
+  if (layout == RA_ZIGZAG && N % (2LL * P))
+    return fail(RA_EINVAL, "zigzag layout needs N (%lld) to be a multiple of 2P (%d)", N, 2 * P);
+  return RA_OK;
+}
+int effective_layout(int layout, int P) { return (layout == RA_ZIGZAG && P == 1) ? RA_CONTIGUOUS : layout; }
 
 ra_status check_common(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype, float scale) {
   if (B < 1 || H < 1 || Hkv < 1) return fail(RA_EINVAL, "B, H, Hkv must be >= 1 (got %d, %d, %d)", B, H, Hkv);
@@ -328,8 +350,29 @@ hipError_t gather_block(void* dst, const void* src, int layout, int64_t planes, 
     return copy2d(D, (size_t)Bl * row_bytes, S + (size_t)kv * Bl * row_bytes, (size_t)N * row_bytes,
                   (size_t)Bl * row_bytes, planes, s);
   }
+  if (layout == RA_ZIGZAG) {
+    const int64_t c = Bl / 2;
+    const size_t cb = (size_t)c * row_bytes;
+    hipError_t e = copy2d(D, (size_t)Bl * row_bytes, S + (size_t)kv * cb, (size_t)N * row_bytes, cb, planes, s);
+    if (e != hipSuccess) return e;
+    return copy2d(D + cb, (size_t)Bl * row_bytes, S + (size_t)(2 * P - 1 - kv) * cb, (size_t)N * row_bytes, cb,
+                  planes, s);
+  }
   return copy2d(D, row_bytes, S + (size_t)kv * row_bytes, (size_t)P * row_bytes, row_bytes,
                 (size_t)planes * Bl, s);
+}
+
+// Host-major staging of every host's own block: dst[r] <- block r of src
+// (used by layouts whose blocks the kernel cannot read in place).
+hipError_t ring_gather_own(void* dst, const void* src, int layout, int64_t planes, int64_t N, int64_t Bl, int P,
+                           size_t row_bytes, hipStream_t s) {
+  char* D = static_cast<char*>(dst);
+  const size_t host_bytes = (size_t)planes * Bl * row_bytes;
+  for (int r = 0; r < P; ++r) {
+    hipError_t e = gather_block(D + r * host_bytes, src, layout, planes, N, Bl, P, r, row_bytes, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -359,7 +402,9 @@ ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, 
   if (!q || !k || !v || !out || !lse) return fail(RA_EINVAL, "null tensor pointer");
   ra_status st = check_common(B, H, Hkv, N, d, P, dtype, scale);
   if (st != RA_OK) return st;
-  if (!layout_ok(layout)) return fail(RA_EINVAL, "unknown layout %d", (int)layout);
+  if ((st = check_layout(layout, N, P)) != RA_OK) return st;
+  const int lay = effective_layout(layout, P);
+  const bool stage_own = lay == RA_ZIGZAG;  // blocks not readable in place: stage step 0 too
   const FwdWs W = fwd_ws_layout(B, H, Hkv, N, N, d, P, dtype);
   if (ws_bytes < W.total) return fail(RA_EINVAL, "workspace too small: need %zu bytes, got %zu", W.total, ws_bytes);
   if (W.total && !ws) return fail(RA_EINVAL, "null workspace");
@@ -384,7 +429,7 @@ ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, 
   a.B = B; a.H = H; a.Hkv = Hkv;
   a.Lq = (int)Bl; a.Lkv = (int)Bl;
   a.P = P;
-  a.layout = layout;
+  a.layout = lay;
   a.q_mode = ROWS_HOST_Q;
   a.kv_mode = ROWS_HOST_Q;
   a.causal = causal ? 1 : 0;
@@ -397,15 +442,24 @@ ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, 
   }
 
   auto kbuf = [&](int s) -> const void* {
-    return s == 0 ? k : static_cast<const void*>(wsb + W.off_stage[s & 1]);
+    return (s == 0 && !stage_own) ? k : static_cast<const void*>(wsb + W.off_stage[s & 1]);
   };
   auto vbuf = [&](int s) -> const void* {
-    return s == 0 ? v : static_cast<const void*>(wsb + W.off_stage[s & 1] + W.kv_bytes);
+    return (s == 0 && !stage_own) ? v : static_cast<const void*>(wsb + W.off_stage[s & 1] + W.kv_bytes);
   };
+  const int64_t planes = (int64_t)B * Hkv;
 
   if (P > 1) {
     RA_HIP(hipEventRecord(ctx->fork, cs), "hipEventRecord");
     RA_HIP(hipStreamWaitEvent(ctx->copy, ctx->fork, 0), "hipStreamWaitEvent");
+  }
+  if (stage_own) {
+    // Every host's own block into staging buffer 0 before step 0.
+    RA_HIP(launch_spin(g_delay_copy_us, ctx->copy), "delay");
+    RA_HIP(ring_gather_own(wsb + W.off_stage[0], k, lay, planes, N, Bl, P, row_bytes, ctx->copy), "staging copy");
+    RA_HIP(ring_gather_own(wsb + W.off_stage[0] + W.kv_bytes, v, lay, planes, N, Bl, P, row_bytes, ctx->copy),
+           "staging copy");
+    RA_HIP(hipEventRecord(ctx->copied[0], ctx->copy), "hipEventRecord");
   }
   for (int s = 0; s < P; ++s) {
     // Copy stream: stage the blocks of step s + 1 while step s computes.
@@ -416,13 +470,12 @@ ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, 
       // Receivers that still have work at step s + 1 (all hosts unless the
       // ring is contiguous and causal, where hosts below s + 1 are done;
       // their staging slots are never read again).
-      const StepPlan nxt = plan_step(layout, a.causal, P, s + 1, Bl);
-      const int r_lo = (layout == RA_CONTIGUOUS && a.causal) ? nxt.host_lo : 0;
-      const int64_t planes = (int64_t)B * Hkv;
+      const StepPlan nxt = plan_step(lay, a.causal, P, s + 1, Bl);
+      const int r_lo = (lay == RA_CONTIGUOUS && a.causal) ? nxt.host_lo : 0;
       RA_HIP(launch_spin(g_delay_copy_us, ctx->copy), "delay");
-      if (s == 0) {
-        RA_HIP(ring_gather_first(kd, k, layout, planes, N, Bl, P, r_lo, row_bytes, ctx->copy), "staging copy");
-        RA_HIP(ring_gather_first(vd, v, layout, planes, N, Bl, P, r_lo, row_bytes, ctx->copy), "staging copy");
+      if (s == 0 && !stage_own) {
+        RA_HIP(ring_gather_first(kd, k, lay, planes, N, Bl, P, r_lo, row_bytes, ctx->copy), "staging copy");
+        RA_HIP(ring_gather_first(vd, v, lay, planes, N, Bl, P, r_lo, row_bytes, ctx->copy), "staging copy");
       } else {
         RA_HIP(ring_shift(kd, kbuf(s), planes, Bl, P, r_lo, row_bytes, ctx->copy), "staging copy");
         RA_HIP(ring_shift(vd, vbuf(s), planes, Bl, P, r_lo, row_bytes, ctx->copy), "staging copy");
@@ -430,12 +483,13 @@ ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, 
       RA_HIP(hipEventRecord(ctx->copied[(s + 1) & 1], ctx->copy), "hipEventRecord");
     }
     // Compute stream: step s.
-    if (s >= 1) RA_HIP(hipStreamWaitEvent(cs, ctx->copied[s & 1], 0), "hipStreamWaitEvent");
-    const StepPlan sp = plan_step(layout, a.causal, P, s, Bl);
+    if (s >= 1 || stage_own) RA_HIP(hipStreamWaitEvent(cs, ctx->copied[s & 1], 0), "hipStreamWaitEvent");
+    const StepPlan sp = plan_step(lay, a.causal, P, s, Bl);
+    const bool in_place = s == 0 && !stage_own;
     a.k = kbuf(s);
     a.v = vbuf(s);
-    a.kv_mode = s == 0 ? ROWS_HOST_Q : ROWS_HOST_MAJOR;
-    a.kv_plane_rows = s == 0 ? N : Bl;
+    a.kv_mode = in_place ? ROWS_HOST_Q : ROWS_HOST_MAJOR;
+    a.kv_plane_rows = in_place ? N : Bl;
     a.host_lo = sp.host_lo;
     a.n_hosts = sp.n_hosts;
     a.kv_shift = s;
@@ -459,7 +513,9 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
   if (!q || !k || !v || !out || !lse) return fail(RA_EINVAL, "null tensor pointer");
   ra_status st = check_common(B, H, Hkv, N, d, P, dtype, scale);
   if (st != RA_OK) return st;
-  if (!layout_ok(layout)) return fail(RA_EINVAL, "unknown layout %d", (int)layout);
+  if ((st = check_layout(layout, N, P)) != RA_OK) return st;
+  const int lay = effective_layout(layout, P);
+  const bool stage_first = lay == RA_ZIGZAG;  // the first block is not readable in place
   if (rank < 0 || rank >= P) return fail(RA_EINVAL, "rank %d out of [0, %d)", rank, P);
   const int64_t Bl = N / P;
   const FwdWs W = fwd_ws_layout(B, H, Hkv, Bl, Bl, d, P, dtype);
@@ -480,7 +536,7 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
   std::vector<int> steps;
   for (int s = 0; s < P; ++s) {
     const int kv = ((rank - s) % P + P) % P;
-    if (pair_active(layout, causal ? 1 : 0, P, rank, kv, Bl, Bl)) steps.push_back(s);
+    if (pair_active(lay, causal ? 1 : 0, P, rank, kv, Bl, Bl)) steps.push_back(s);
   }
 
   StepArgs a{};
@@ -491,7 +547,7 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
   a.B = B; a.H = H; a.Hkv = Hkv;
   a.Lq = (int)Bl; a.Lkv = (int)Bl;
   a.P = P;
-  a.layout = layout;
+  a.layout = lay;
   a.q_mode = ROWS_COMPACT;
   a.causal = causal ? 1 : 0;
   a.n_qtiles = (int)nqt;
@@ -504,12 +560,22 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
     a.o = reinterpret_cast<float*>(wsb + W.off_o);
   }
   const int n = (int)steps.size();
-  if (n > 1) {
+  const int64_t planes = (int64_t)B * Hkv;
+  if (n > 1 || (n > 0 && stage_first)) {
     RA_HIP(hipEventRecord(ctx->fork, cs), "hipEventRecord");
     RA_HIP(hipStreamWaitEvent(ctx->copy, ctx->fork, 0), "hipStreamWaitEvent");
   }
+  if (n > 0 && stage_first) {
+    const int kv0 = ((rank - steps[0]) % P + P) % P;
+    RA_HIP(launch_spin(g_delay_copy_us, ctx->copy), "delay");
+    RA_HIP(gather_block(wsb + W.off_stage[0], k, lay, planes, N, Bl, P, kv0, row_bytes, ctx->copy), "staging copy");
+    RA_HIP(gather_block(wsb + W.off_stage[0] + W.kv_bytes, v, lay, planes, N, Bl, P, kv0, row_bytes, ctx->copy),
+           "staging copy");
+    RA_HIP(hipEventRecord(ctx->copied[0], ctx->copy), "hipEventRecord");
+  }
   // Step index i uses staging buffer i & 1 (i >= 1); the first step reads
-  // its block in place from the natural-order k / v.
+  // its block in place from the natural-order k / v (contiguous, striped)
+  // or from staging buffer 0 (zigzag).
   for (int i = 0; i < n; ++i) {
     const int s = steps[i];
     if (i + 1 < n) {
@@ -519,12 +585,12 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
       void* kd = wsb + W.off_stage[(i + 1) & 1];
       void* vd = wsb + W.off_stage[(i + 1) & 1] + W.kv_bytes;
       RA_HIP(launch_spin(g_delay_copy_us, ctx->copy), "delay");
-      RA_HIP(gather_block(kd, k, layout, (int64_t)B * Hkv, N, Bl, P, kv1, row_bytes, ctx->copy), "staging copy");
-      RA_HIP(gather_block(vd, v, layout, (int64_t)B * Hkv, N, Bl, P, kv1, row_bytes, ctx->copy), "staging copy");
+      RA_HIP(gather_block(kd, k, lay, planes, N, Bl, P, kv1, row_bytes, ctx->copy), "staging copy");
+      RA_HIP(gather_block(vd, v, lay, planes, N, Bl, P, kv1, row_bytes, ctx->copy), "staging copy");
       RA_HIP(hipEventRecord(ctx->copied[(i + 1) & 1], ctx->copy), "hipEventRecord");
     }
-    if (i >= 1) RA_HIP(hipStreamWaitEvent(cs, ctx->copied[i & 1], 0), "hipStreamWaitEvent");
-    if (i == 0) {
+    if (i >= 1 || stage_first) RA_HIP(hipStreamWaitEvent(cs, ctx->copied[i & 1], 0), "hipStreamWaitEvent");
+    if (i == 0 && !stage_first) {
       a.k = k;
       a.v = v;
       a.kv_mode = ROWS_HOST_KV;
@@ -562,6 +628,8 @@ ra_status ring_attn_step(const void* q_blk, ra_kv_block kv_blk, float* m, float*
     return fail(RA_EINVAL, "block lengths must be in [1, 2^30]");
   if (!dtype_ok(md->dtype)) return fail(RA_EINVAL, "unknown dtype %d", (int)md->dtype);
   if (!layout_ok(md->layout)) return fail(RA_EINVAL, "unknown layout %d", (int)md->layout);
+  if (md->layout == RA_ZIGZAG && md->causal && (md->Lq != md->Lkv || md->Lq % 2))
+    return fail(RA_EINVAL, "zigzag causal blocks must have Lq == Lkv and an even length");
   if (md->P < 1 || md->P > kMaxP || md->q_rank < 0 || md->q_rank >= md->P || md->kv_rank < 0 ||
       md->kv_rank >= md->P)
     return fail(RA_EINVAL, "bad ring description P=%d q_rank=%d kv_rank=%d", md->P, md->q_rank, md->kv_rank);

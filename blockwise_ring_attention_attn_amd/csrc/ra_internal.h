@@ -31,7 +31,7 @@ struct StepArgs {
   int B, H, Hkv;
   int Lq, Lkv;            // rows per host block (query / key)
   int P;
-  int layout;             // 0 contiguous, 1 striped
+  int layout;             // 0 contiguous, 1 striped, 2 zigzag
   int host_lo, n_hosts;
   int kv_shift;           // kv_rank = (q_rank - kv_shift) mod P
   int q_mode;             // RowMode for q / out / state (COMPACT or HOST_Q)

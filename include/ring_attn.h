@@ -44,10 +44,15 @@ extern "C" {
 typedef enum { RA_OK = 0, RA_EINVAL = 1, RA_ENOMEM = 2, RA_EHIP = 3, RA_EUNSUPPORTED = 4 } ra_status;
 
 /* Which tokens each of the P virtual hosts owns ([TKG] §2 sequence sharding,
- * §7 round-robin striping):
+ * §7 round-robin striping; [CML] "İddia ve Gerçeklik" names striped and
+ * zigzag schedules as the cures for the causal load imbalance):
  *   RA_CONTIGUOUS: host r owns tokens r*Bl .. r*Bl + Bl - 1   (Bl = N / P)
- *   RA_STRIPED:    host r owns tokens r, r + P, r + 2P, ...                */
-typedef enum { RA_CONTIGUOUS = 0, RA_STRIPED = 1 } ra_layout;
+ *   RA_STRIPED:    host r owns tokens r, r + P, r + 2P, ...
+ *   RA_ZIGZAG:     the sequence is cut into 2P chunks of C = N / (2P) tokens
+ *                  and host r owns chunks r and 2P-1-r, in that order
+ *                  (rows 0..C-1 of its block are tokens r*C .., rows C..2C-1
+ *                  are tokens (2P-1-r)*C ..).  Needs N % (2P) == 0.      */
+typedef enum { RA_CONTIGUOUS = 0, RA_STRIPED = 1, RA_ZIGZAG = 2 } ra_layout;
 
 /* Element type of q, k, v and out.  RA_BF16: bfloat16 inputs, bf16 MFMA
  * products with fp32 accumulation.  RA_F32: float32 throughout.          */
@@ -71,7 +76,9 @@ typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
  * positions ([TKG] §7); 0 = no mask.  layout only decides which tokens each
  * host owns; inputs and outputs stay in natural order, so the result does
  * not depend on layout or P (up to rounding).  scale: usually 1/sqrt(d)
- * ([TKG] §3 equation S).  Requires N % P == 0 and 1 <= P <= 64.
+ * ([TKG] §3 equation S).  Requires N % P == 0 (N % 2P == 0 for RA_ZIGZAG)
+ * and 1 <= P <= 64.  With RA_ZIGZAG every host's block is first gathered
+ * into the staging buffer (it is two separate chunks of the sequence).
  * ws: at least ring_attn_fwd_ws_bytes(...) bytes.
  * ---------------------------------------------------------------------- */
 size_t ring_attn_fwd_ws_bytes(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype);
@@ -87,7 +94,8 @@ ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, 
  * stream while the current one computes ([TKG] §2, §5).
  *
  * q, out [B, H, N/P, d] hold the rank's Nq = N/P query tokens (in the order
- * the layout gives them: contiguous r*Bl + i, striped i*P + r); lse is
+ * the layout gives them: contiguous r*Bl + i, striped i*P + r, zigzag chunk
+ * r then chunk 2P-1-r); lse is
  * [B, H, N/P].  k, v [B, Hkv, N, d] hold the whole sequence in natural
  * order (the blocks the other hosts would send).  ws: at least
  * ring_attn_fwd_share_ws_bytes(...) bytes.
@@ -116,8 +124,11 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
  *
  * Positions for the causal mask come from mask_desc: contiguous
  * pos_q(i) = q_rank*Lq + i, pos_k(j) = kv_rank*Lkv + j; striped
- * pos_q(i) = i*P + q_rank, pos_k(j) = j*P + kv_rank.  A query row with no
- * visible key in the block leaves its state unchanged.
+ * pos_q(i) = i*P + q_rank, pos_k(j) = j*P + kv_rank (needs Lq == Lkv when
+ * causal); zigzag with C = Lq/2: pos_q(i) = q_rank*C + i for i < C, else
+ * (2P-1-q_rank)*C + i - C, likewise for keys (needs Lq == Lkv, even, when
+ * causal).  A query row with no visible key in the block leaves its state
+ * unchanged.
  * ---------------------------------------------------------------------- */
 typedef struct { const void* k; const void* v; } ra_kv_block;
 typedef struct {

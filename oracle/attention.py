@@ -63,7 +63,11 @@ def host_positions(N: int, P: int, layout: str) -> list[np.ndarray]:
 
     [TKG] §2: each host holds B = N / P tokens.  "contiguous": host r holds
     tokens r*B .. r*B + B - 1.  "striped" ([TKG] §7, round-robin): host r
-    holds tokens r, r + P, r + 2P, ...
+    holds tokens r, r + P, r + 2P, ...  "zigzag" ([CML] "İddia ve Gerçeklik"
+    names zigzag schedules beside striped ones; the pages give no formula,
+    so this is the plain reading): the sequence is cut into 2P equal chunks
+    and host r holds chunk r followed by chunk 2P-1-r, pairing an early
+    chunk with a late one.
     """
     if N % P:
         raise ValueError("N must be a multiple of P")
@@ -72,6 +76,13 @@ def host_positions(N: int, P: int, layout: str) -> list[np.ndarray]:
         return [np.arange(r * Bl, (r + 1) * Bl, dtype=np.int64) for r in range(P)]
     if layout == "striped":
         return [np.arange(r, N, P, dtype=np.int64) for r in range(P)]
+    if layout == "zigzag":
+        if N % (2 * P):
+            raise ValueError("zigzag needs N to be a multiple of 2P")
+        C = N // (2 * P)
+        return [np.concatenate([np.arange(r * C, (r + 1) * C, dtype=np.int64),
+                                np.arange((2 * P - 1 - r) * C, (2 * P - r) * C, dtype=np.int64)])
+                for r in range(P)]
     raise ValueError(f"unknown layout {layout!r}")
 
 

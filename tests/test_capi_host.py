@@ -69,6 +69,7 @@ def _fwd(lib, **kw):
     (dict(ws=None), "null workspace"),
     (dict(ws=255), "aligned"),
     (dict(layout=7), "layout"),
+    (dict(layout=2, N=68), "multiple of 2P"),
     (dict(dtype=9), "dtype"),
     (dict(scale=0.0), "scale"),
     (dict(scale=float("nan")), "scale"),
@@ -85,6 +86,9 @@ def test_step_rejects_invalid(lib):
     assert lib.ring_attn_step(1, ra.ra_kv_block(1, 1), 1, 1, 1, None, None) == ra.RA_EINVAL
     md = ra.ra_mask_desc(1, 2, 1, 64, 16, 8, 0.125, ra.RA_BF16, 1, 1, 4, 1, 0)  # striped causal Lq != Lkv
     assert lib.ring_attn_step(1, ra.ra_kv_block(1, 1), 1, 1, 1, ctypes.byref(md), None) == ra.RA_EINVAL
+    md = ra.ra_mask_desc(1, 2, 1, 64, 15, 15, 0.125, ra.RA_BF16, 1, 2, 4, 1, 0)  # zigzag causal, odd length
+    assert lib.ring_attn_step(1, ra.ra_kv_block(1, 1), 1, 1, 1, ctypes.byref(md), None) == ra.RA_EINVAL
+    assert b"zigzag" in lib.ra_last_error()
 
 
 def test_merge_decode_reject_invalid(lib):

@@ -23,7 +23,7 @@ def _inputs(seed, B, H, Hkv, N, d):
     return to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
 
 
-@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
 @pytest.mark.parametrize("delays", [(2000, 0), (0, 2000)])
 def test_fwd_stream_order_under_delays(layout, delays):
     qd, kd, vd = _inputs(21, 1, 4, 2, 8 * 256, 128)
@@ -38,23 +38,25 @@ def test_fwd_stream_order_under_delays(layout, delays):
     assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1])
 
 
+@pytest.mark.parametrize("layout,causal", [("contiguous", False), ("zigzag", True)])
 @pytest.mark.parametrize("delays", [(2000, 0), (0, 2000)])
-def test_share_stream_order_under_delays(delays):
+def test_share_stream_order_under_delays(layout, causal, delays):
     import torch
     B, H, Hkv, N, d, P, rank = 1, 4, 4, 8 * 256, 128, 8, 5
     q, k, v = synth.qkv(22, B, H, Hkv, N, d, "bf16", Nq=N // P)
     qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
-    ref = [from_dev(t) for t in ra.ring_attn_fwd_share(qd, kd, vd, P=P, rank=rank, causal=False)]
+    kw = dict(P=P, rank=rank, causal=causal, layout=layout)
+    ref = [from_dev(t) for t in ra.ring_attn_fwd_share(qd, kd, vd, **kw)]
     try:
         ra.debug_set_delays(*delays)
-        got = [from_dev(t) for t in ra.ring_attn_fwd_share(qd, kd, vd, P=P, rank=rank, causal=False)]
+        got = [from_dev(t) for t in ra.ring_attn_fwd_share(qd, kd, vd, **kw)]
     finally:
         ra.debug_set_delays(0, 0)
     torch.cuda.synchronize()
     assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1])
 
 
-@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
 def test_fwd_ignores_stale_workspace(layout):
     """A workspace full of NaN bytes gives bitwise the same result as a zeroed one."""
     import torch

@@ -289,7 +289,7 @@ def _ring_recurrence(q, k, v, scale, causal, P, layout, order):
 
 
 @pytest.mark.parametrize("P", [1, 2, 4, 8])
-@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ring_recurrence_reaches_oracle(P, layout, causal):
     rng = np.random.default_rng([P, int(causal), len(layout)])
@@ -347,12 +347,20 @@ def test_step_partial_empty_rows():
 # 8. Layout and work counts, pinned to the pages' figures.
 # --------------------------------------------------------------------------
 def test_host_positions_partition():
-    for layout in ("contiguous", "striped"):
+    for layout in ("contiguous", "striped", "zigzag"):
         pos = oracle.host_positions(24, 4, layout)
         allp = np.sort(np.concatenate(pos))
         np.testing.assert_array_equal(allp, np.arange(24))
+        # positions inside a block increase with the row (the kernels rely on it)
+        for p in pos:
+            assert np.all(np.diff(p) > 0)
     assert list(oracle.host_positions(8, 4, "striped")[1]) == [1, 5]
     assert list(oracle.host_positions(8, 4, "contiguous")[1]) == [2, 3]
+    # zigzag, 2P = 4 chunks of 2: host 0 pairs the first and last chunk
+    assert list(oracle.host_positions(8, 2, "zigzag")[0]) == [0, 1, 6, 7]
+    assert list(oracle.host_positions(8, 2, "zigzag")[1]) == [2, 3, 4, 5]
+    with pytest.raises(ValueError):
+        oracle.host_positions(12, 4, "zigzag")
 
 
 @pytest.mark.parametrize("P,N", [(4, 32), (8, 64), (8, 256)])
@@ -370,6 +378,14 @@ def test_pair_counts_closed_forms(P, N):
     # striped: every host gets the same total share of the causal triangle ([TKG] §7)
     rows = st.sum(axis=1)
     assert rows.max() - rows.min() <= P * Bl
+    # zigzag: 2C^2 + C on the diagonal block, 2C^2 on every other block, so
+    # every host's share is exactly the same
+    C = N // (2 * P)
+    zz = oracle.pair_counts(N, P, "zigzag", causal=True)
+    for rq, rk in itertools.product(range(P), repeat=2):
+        assert zz[rq, rk] == (2 * C * C + C if rk == rq else 2 * C * C)
+    assert zz.sum() == N * (N + 1) // 2
+    assert len(set(zz.sum(axis=1))) == 1
 
 
 def test_pages_printed_figures():

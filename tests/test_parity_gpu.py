@@ -49,11 +49,25 @@ def test_fp32_small(d, causal, layout):
     _fwd_and_check(7, 1, 2, 1, 4 * 75, d, 4, causal, layout, "f32")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp32_small_zigzag(d, causal):
+    """Zigzag: 2P = 8 chunks of 75 tokens (ragged against every tile size)."""
+    _fwd_and_check(7, 1, 2, 1, 8 * 75, d, 4, causal, "zigzag", "f32")
+
+
 @pytest.mark.parametrize("N,P", [(8, 8), (24, 8), (8 * 130, 8), (4 * 257, 4), (3 * 384, 3), (700, 1)])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("layout", ["contiguous", "striped"])
 def test_bf16_causal_ragged(N, P, d, layout):
     _fwd_and_check(2, 1, 4, 2, N, d, P, True, layout, "bf16")
+
+
+# zigzag needs N % 2P == 0; chunks of 1, 3, 130, 257 and 384 tokens, and P = 1
+@pytest.mark.parametrize("N,P", [(16, 8), (48, 8), (16 * 130, 8), (8 * 257, 4), (6 * 384, 3), (700, 1)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_causal_ragged_zigzag(N, P, d):
+    _fwd_and_check(2, 1, 4, 2, N, d, P, True, "zigzag", "bf16")
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -62,12 +76,13 @@ def test_bf16_batched_gqa(causal):
 
 
 def test_bf16_layout_and_P_invariance():
-    """Same inputs: contiguous P=8, striped P=8, striped P=2 and P=1 agree
-    with each other within twice the tolerance and each with the oracle."""
+    """Same inputs: contiguous P=8, striped P=8 and P=2, P=1, zigzag P=8 and
+    P=2 agree with each other within twice the tolerance."""
     dtype, N, d = "bf16", 8 * 256, 128
     q, k, v = _case(4, 1, 2, 2, N, d, dtype)
     outs = []
-    for layout, P in (("contiguous", 8), ("striped", 8), ("striped", 2), ("contiguous", 1)):
+    for layout, P in (("contiguous", 8), ("striped", 8), ("striped", 2), ("contiguous", 1), ("zigzag", 8),
+                      ("zigzag", 2)):
         o, l = ra.ring_attn_fwd(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), P=P, causal=True,
                                 layout=layout)
         outs.append((from_dev(o), from_dev(l)))
@@ -94,7 +109,7 @@ def test_deterministic_bitwise():
     assert np.array_equal(from_dev(r1[1]), from_dev(r2[1]))
 
 
-@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_share_matches_oracle(layout, dtype):
     """One host's share: q holds host `rank`'s tokens, k, v the whole sequence."""
@@ -112,7 +127,7 @@ def test_share_matches_oracle(layout, dtype):
         assert_close(from_dev(o), from_dev(l), Ow, Lw, dtype, f"share rank={rank} {layout}")
 
 
-@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_step_state_against_oracle(layout, dtype):
     """ring_attn_step on one (q block, kv block) pair, then on a second kv
