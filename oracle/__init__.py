@@ -13,3 +13,4 @@ from .attention import (  # noqa: F401
     step_partial,
     pair_counts,
 )
+from .backward import attention_bwd  # noqa: F401
