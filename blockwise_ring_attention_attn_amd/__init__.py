@@ -25,6 +25,7 @@ EXPORTS = (
     "ring_attn_fwd_share_ws_bytes", "ring_attn_fwd_share",
     "ring_attn_step", "ring_attn_finalize", "lse_merge",
     "ring_attn_decode_ws_bytes", "ring_attn_decode",
+    "ring_attn_bwd_ws_bytes", "ring_attn_bwd",
     "ra_last_error", "ra_version", "ra_debug_set_delays", "ra_prof_enable", "ra_prof_reset", "ra_prof_read",
 )
 
@@ -78,6 +79,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.ring_attn_decode_ws_bytes.restype = st
     lib.ring_attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, ll, i, i, f, i, vp, vp, st]
     lib.ring_attn_decode.restype = i
+    lib.ring_attn_bwd_ws_bytes.argtypes = [i, i, i, ll, i, i, i]
+    lib.ring_attn_bwd_ws_bytes.restype = st
+    lib.ring_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, ll, i, i, i, i, f, i, vp, vp, st]
+    lib.ring_attn_bwd.restype = i
     lib.ra_last_error.argtypes = []
     lib.ra_last_error.restype = ctypes.c_char_p
     lib.ra_version.argtypes = []
@@ -197,6 +202,40 @@ def ring_attn_fwd_share(q, k, v, *, P: int, rank: int, causal: bool, layout: str
                                    rank, int(bool(causal)), LAYOUTS[layout], scale, code, _stream(stream),
                                    _ptr(wst) if wst is not None else None, nb))
     return out, lse
+
+
+def ring_attn_bwd(q, k, v, out, dout, lse, *, P: int, causal: bool, layout: str = "contiguous",
+                  scale: float | None = None, dq=None, dk=None, dv=None, ws=None, stream=None):
+    """Gradients of ring_attn_fwd by recomputation over a reverse ring.
+
+    q, out, dout [B, H, N, d]; k, v [B, Hkv, N, d] (bf16); lse [B, H, N] fp32
+    from the forward.  Returns (dq, dk, dv) shaped like q, k, v.
+    """
+    torch = _torch()
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout"), (lse, "lse")):
+        _need(t, n)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    code = _dtype_code(q)
+    if any(t.dtype != q.dtype for t in (k, v, out, dout)):
+        raise TypeError("q, k, v, out, dout must share a dtype")
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d):
+        raise ValueError("k, v must be [B, Hkv, N, d]")
+    if tuple(out.shape) != (B, H, N, d) or tuple(dout.shape) != (B, H, N, d) or tuple(lse.shape) != (B, H, N):
+        raise ValueError("out, dout must be [B, H, N, d] and lse [B, H, N]")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    nb = lib.ring_attn_bwd_ws_bytes(B, H, Hkv, N, d, P, code)
+    wst = _workspace(nb, q.device, ws)
+    _check(lib.ring_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                             _ptr(dv), B, H, Hkv, N, d, P, int(bool(causal)), LAYOUTS[layout], scale, code,
+                             _stream(stream), _ptr(wst) if wst is not None else None, nb))
+    return dq, dk, dv
 
 
 def init_state(B, H, Lq, d, device):

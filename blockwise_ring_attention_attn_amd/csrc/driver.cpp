@@ -616,6 +616,112 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
   return RA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Backward by recomputation ([TKG] §7, "활성화 체크포인팅과 메모리 재연산"):
+// the forward's lse (= m + ln l) and the queries stay put; at step s host r
+// recomputes its attention against kv block (r + s) mod P (the kv blocks
+// travel the other way round the ring) and adds that pair's dQ, dK, dV.
+// On one GPU the dK / dV accumulators that would travel with their kv block
+// stay at the block's rows; each kv block meets exactly one host per step,
+// so the kernels of one step never write the same rows.
+// ---------------------------------------------------------------------------
+struct BwdWs {
+  size_t off_delta, off_dq, off_dk, off_dv, total;
+};
+
+static BwdWs bwd_ws_layout(int B, int H, int Hkv, long long N, int d) {
+  BwdWs w{};
+  size_t off = 0;
+  w.off_delta = off; off += align_up((size_t)B * H * N * 4);
+  w.off_dq = off; off += align_up((size_t)B * H * N * d * 4);
+  w.off_dk = off; off += align_up((size_t)B * Hkv * N * d * 4);
+  w.off_dv = off; off += align_up((size_t)B * Hkv * N * d * 4);
+  w.total = off;
+  return w;
+}
+
+size_t ring_attn_bwd_ws_bytes(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype) {
+  (void)dtype;
+  if (B < 1 || H < 1 || Hkv < 1 || P < 1 || N < 1 || N % P) return 0;
+  return bwd_ws_layout(B, H, Hkv, N, d).total;
+}
+
+ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, long long N, int d,
+                        int P, int causal, ra_layout layout, float scale, ra_dtype dtype, void* stream, void* ws,
+                        size_t ws_bytes) {
+  g_err.clear();
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv) return fail(RA_EINVAL, "null tensor pointer");
+  ra_status st = check_common(B, H, Hkv, N, d, P, dtype, scale);
+  if (st != RA_OK) return st;
+  if ((st = check_layout(layout, N, P)) != RA_OK) return st;
+  if (dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "ring_attn_bwd supports bf16 only");
+  const BwdWs W = bwd_ws_layout(B, H, Hkv, N, d);
+  if (ws_bytes < W.total) return fail(RA_EINVAL, "workspace too small: need %zu bytes, got %zu", W.total, ws_bytes);
+  if (!ws) return fail(RA_EINVAL, "null workspace");
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(RA_EINVAL, "workspace must be 256-byte aligned");
+  const int64_t Bl = N / P;
+  const int64_t nqt = (Bl + bwd_dq_rows() - 1) / bwd_dq_rows();
+  const int64_t nkt = (Bl + bwd_dkdv_rows() - 1) / bwd_dkdv_rows();
+  if ((int64_t)P * B * H * nqt > 0x7fffffffLL || (int64_t)P * B * Hkv * nkt > 0x7fffffffLL)
+    return fail(RA_EINVAL, "problem too large for one launch");
+  const int lay = effective_layout(layout, P);
+  hipStream_t cs = static_cast<hipStream_t>(stream);
+  char* wsb = static_cast<char*>(ws);
+
+  BwdArgs a{};
+  a.s.q = q;
+  a.s.k = k;
+  a.s.v = v;
+  a.s.q_plane_rows = N;
+  a.s.kv_plane_rows = N;
+  a.s.B = B; a.s.H = H; a.s.Hkv = Hkv;
+  a.s.Lq = (int)Bl; a.s.Lkv = (int)Bl;
+  a.s.P = P;
+  a.s.layout = lay;
+  a.s.q_mode = ROWS_HOST_Q;
+  a.s.kv_mode = ROWS_HOST_KV;
+  a.s.causal = causal ? 1 : 0;
+  a.s.n_qtiles = (int)nqt;
+  a.s.scale_log2 = scale * 1.4426950408889634f;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = reinterpret_cast<float*>(wsb + W.off_delta);
+  a.dq_acc = reinterpret_cast<float*>(wsb + W.off_dq);
+  a.dk_acc = reinterpret_cast<float*>(wsb + W.off_dk);
+  a.dv_acc = reinterpret_cast<float*>(wsb + W.off_dv);
+  a.n_tok = N;
+  a.scale = scale;
+  a.n_kvtiles = (int)nkt;
+
+  const int64_t nq = (int64_t)B * H * N * d, nkv = (int64_t)B * Hkv * N * d;
+  RA_HIP(launch_fill_zero(a.dq_acc, nq, cs), "fill launch");
+  RA_HIP(launch_fill_zero(a.dk_acc, nkv, cs), "fill launch");
+  RA_HIP(launch_fill_zero(a.dv_acc, nkv, cs), "fill launch");
+  RA_HIP(launch_bwd_prep(out, dout, const_cast<float*>(a.delta), (int64_t)B * H * N, d, cs), "prep launch");
+  for (int s = 0; s < P; ++s) {
+    // hosts with visible work against kv block (r + s) mod P
+    int lo = -1, hi = -1;
+    for (int r = 0; r < P; ++r) {
+      const int kv = (r + s) % P;
+      if (pair_active(lay, a.s.causal, P, r, kv, Bl, Bl)) {
+        if (lo < 0) lo = r;
+        hi = r;
+      }
+    }
+    if (lo < 0) continue;
+    a.s.host_lo = lo;
+    a.s.n_hosts = hi - lo + 1;
+    a.s.kv_shift = -s;
+    RA_HIP(launch_bwd_dkdv(a, d, cs), "dK/dV kernel launch");
+    RA_HIP(launch_bwd_dq(a, d, cs), "dQ kernel launch");
+  }
+  RA_HIP(launch_to_bf16(a.dq_acc, dq, nq, cs), "convert launch");
+  RA_HIP(launch_to_bf16(a.dk_acc, dk, nkv, cs), "convert launch");
+  RA_HIP(launch_to_bf16(a.dv_acc, dv, nkv, cs), "convert launch");
+  return RA_OK;
+}
+
 ra_status ring_attn_step(const void* q_blk, ra_kv_block kv_blk, float* m, float* l, float* o,
                          const ra_mask_desc* md, void* stream) {
   g_err.clear();

@@ -44,6 +44,24 @@ struct StepArgs {
   float scale_log2;       // scale * log2(e)
 };
 
+// One backward ring step (bf16): the fields of `s` describe the (query
+// host, kv block) pairs exactly as for the forward step, with q / k / v read
+// in natural token order (q_mode = ROWS_HOST_Q, per-row kv addressing).
+// The kernels add this step's contributions into fp32 accumulators in
+// natural row order.
+struct BwdArgs {
+  StepArgs s;
+  const void* dout;       // [B, H, N, d], same rows as q
+  const float* lse;       // [B, H, N] natural-log lse of the forward
+  const float* delta;     // [B, H, N] rowsum(dO * O)
+  float* dq_acc;          // [B, H, N, d]
+  float* dk_acc;          // [B, Hkv, N, d]
+  float* dv_acc;          // [B, Hkv, N, d]
+  int64_t n_tok;          // N (rows per plane of every natural-order array)
+  float scale;
+  int n_kvtiles;          // ceil(Lkv / rows per dK/dV workgroup)
+};
+
 struct MergeArgs {
   float* o_a; float* lse_a; const float* o_b; const float* lse_b;
   int64_t rows; int d;
@@ -80,5 +98,15 @@ hipError_t launch_finalize(const FinalizeArgs& a, int out_bf16, hipStream_t s);
 hipError_t launch_decode_partial(const DecodeArgs& a, int d, int bf16, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs& a, int d, int bf16, hipStream_t s);
 hipError_t launch_spin(int microseconds, hipStream_t s);  // bounded busy wait (test hook)
+
+// Backward (bf16): delta = rowsum(dO * O); zero fill; dK/dV and dQ step
+// kernels; fp32 accumulator -> bf16 conversion.
+int bwd_dq_rows();     // query rows per dQ workgroup
+int bwd_dkdv_rows();   // keys per dK/dV workgroup
+hipError_t launch_bwd_prep(const void* out, const void* dout, float* delta, int64_t rows, int d, hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+hipError_t launch_to_bf16(const float* src, void* dst, int64_t n, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdArgs& a, int d, hipStream_t s);
 
 }  // namespace ra

@@ -182,6 +182,33 @@ ra_status ring_attn_decode(const void* q, const void* k, const void* v, void* ou
                            ra_dtype dtype, void* stream, void* ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------
+ * ring_attn_bwd -- gradients of ring_attn_fwd by recomputation over a
+ * reverse ring ([TKG] §7, "활성화 체크포인팅과 메모리 재연산": keep the
+ * queries and the row statistics, send the key/value blocks the other way
+ * round the ring and recompute the attention map where it is needed).
+ *
+ * At ring step s = 0..P-1 host r pairs with kv block (r + s) mod P and, tile
+ * by tile, recomputes S = scale Q K^T and P = exp(S - lse), then adds
+ *   dV += P^T dO,  dK += scale dS^T Q,  dQ += scale dS K,
+ *   dS = P * (dO V^T - delta),  delta_i = dO_i . O_i
+ * (the chain rule applied to the forward definition).
+ *
+ * q, out, dout, dq [B, H, N, d]; k, v, dk, dv [B, Hkv, N, d]; lse [B, H, N]
+ * float32 as written by ring_attn_fwd for the same inputs (out and lse are
+ * the forward's results); all in natural token order, element type bf16
+ * (RA_F32 returns RA_EUNSUPPORTED).  With grouped-query attention dk, dv
+ * sum the contributions of every query head of the group.  causal, layout,
+ * scale, P: as for ring_attn_fwd; the result does not depend on layout or P
+ * up to rounding.  dq, dk, dv are overwritten.  ws: at least
+ * ring_attn_bwd_ws_bytes(...) bytes (fp32 accumulators and delta).
+ * ---------------------------------------------------------------------- */
+size_t ring_attn_bwd_ws_bytes(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype);
+ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, long long N, int d,
+                        int P, int causal, ra_layout layout, float scale, ra_dtype dtype, void* stream, void* ws,
+                        size_t ws_bytes);
+
+/* ------------------------------------------------------------------------
  * Diagnostics.
  * ra_last_error: message of the last failed call on this thread ("" if none).
  * ra_version: library version string.

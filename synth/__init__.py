@@ -18,6 +18,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 TENSOR_Q, TENSOR_K, TENSOR_V = 0, 1, 2
+TENSOR_DOUT = 3   # upstream gradient of the output (backward tests)
 
 
 def _threads() -> int:
