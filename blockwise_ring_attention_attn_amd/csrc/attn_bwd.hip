@@ -11,7 +11,8 @@
 //
 // One ring step pairs query host r with kv block (r + s) mod P.  For every
 // such pair the kernels recompute, tile by tile,
-//   S = scale Q K^T,  P = exp(S - lse)      (lse = m + ln l of the forward)
+//   S = scale Q K^T,  P = exp(S - lse)      (lse = m + ln l of the forward,
+//                                            taken in base 2 as lse2)
 //   dP = dO V^T,      dS = P (dP - delta)   (delta_i = dO_i . O_i)
 // and add
 //   dV += P^T dO,  dK += scale dS^T Q       (bwd_dkdv_kernel, one key tile
@@ -65,11 +66,46 @@ struct RowTile {
   static constexpr int PER_THREAD = kRows * CPR / kThreads;
 };
 
+// Token position of row i of host `rank`'s block (blk rows) for a layout
+// fixed at compile time (0 contiguous, 1 striped, 2 zigzag); positions fit
+// in 32 bits (blocks are at most 2^30 rows and N / P == blk).
+template <int LAYOUT>
+__device__ __forceinline__ int lrow(int rank, int i, int blk, int P) {
+  if constexpr (LAYOUT == 0) {
+    return rank * blk + i;
+  } else if constexpr (LAYOUT == 1) {
+    return i * P + rank;
+  } else {
+    const int c = blk >> 1;
+    return i < c ? rank * c + i : (2 * P - 1 - rank) * c + (i - c);
+  }
+}
+
+// Largest visible key (index in the kv block) of query row i, clamped to
+// [-1, Lkv - 1]: the same limit as the forward's, for a compile-time layout.
+template <int LAYOUT>
+__device__ __forceinline__ int llim(const StepArgs& A, int q_rank, int kv_rank, int i) {
+  if (!A.causal) return A.Lkv - 1;
+  int lim;
+  if constexpr (LAYOUT == 0) {
+    lim = q_rank * A.Lq + i - kv_rank * A.Lkv;
+  } else if constexpr (LAYOUT == 1) {
+    lim = i - (kv_rank > q_rank ? 1 : 0);
+  } else {
+    const int c = A.Lkv >> 1;
+    const int pos = lrow<2>(q_rank, i, A.Lq, A.P);
+    const int na = min(max(pos - kv_rank * c + 1, 0), c);
+    const int nb = min(max(pos - (2 * A.P - 1 - kv_rank) * c + 1, 0), c);
+    lim = na + nb - 1;
+  }
+  return min(max(lim, -1), A.Lkv - 1);
+}
+
 // Natural-order row of host `rank`'s block row i in plane `plane` of an
 // array with n_tok rows per plane.
-__device__ __forceinline__ int64_t nat_row(const StepArgs& A, int64_t plane, int64_t n_tok, int rank, int64_t i,
-                                           int blk) {
-  return plane * n_tok + host_row(A.layout, rank, i, blk, A.P);
+template <int LAYOUT>
+__device__ __forceinline__ int64_t nat_row(const StepArgs& A, int64_t plane, int64_t n_tok, int rank, int i, int blk) {
+  return plane * n_tok + lrow<LAYOUT>(rank, i, blk, A.P);
 }
 
 // Global -> register prefetch and register -> LDS store of one 32-row tile
@@ -80,14 +116,14 @@ struct TileRegs {
 };
 
 template <int D, typename RowFn>
-__device__ __forceinline__ void tile_fetch(TileRegs<D>& t, const unsigned short* base, int64_t row0, int valid,
+__device__ __forceinline__ void tile_fetch(TileRegs<D>& t, const unsigned short* base, int row0, int valid,
                                            RowFn&& row_of) {
   using T = RowTile<D>;
 #pragma unroll
   for (int u = 0; u < T::PER_THREAD; ++u) {
     const int ch = u * kThreads + threadIdx.x;
     const int r = ch / T::CPR, c = ch % T::CPR;
-    const int64_t i = row0 + r;
+    const int i = row0 + r;
     t.v[u] = i < valid ? *reinterpret_cast<const u32x4*>(base + row_of(i) * D + 8 * c) : u32x4{0u, 0u, 0u, 0u};
   }
 }
@@ -185,7 +221,7 @@ __device__ __forceinline__ void add_block(float* dst_row, const f32x16& acc, int
 // sweeps, for every query head of the kv head's group, the 32-row query
 // tiles that see any of its keys.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int LAYOUT>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   using T = RowTile<D>;
   constexpr int KS = D / 16, NDB = D / 32;
@@ -214,25 +250,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   const float c = A.scale_log2;
 
   // this lane's key and the wave's key range
-  const int64_t key0 = (int64_t)kt * kDkdvKeys;
-  const int64_t my_key = key0 + wave * 32 + col;
+  const int key0 = kt * kDkdvKeys;
+  const int my_key = key0 + wave * 32 + col;
   const bool key_ok = my_key < A.Lkv;
   const int64_t kv_plane = (int64_t)w.b * A.Hkv + w.hkv;
-  const int64_t key_row = key_ok ? nat_row(A, kv_plane, G.n_tok, w.kv_rank, my_key, A.Lkv) : 0;
-  const int64_t wave_last = (key0 + wave * 32 + 31 < A.Lkv ? key0 + wave * 32 + 31 : A.Lkv - 1);
+  const int64_t key_row = key_ok ? nat_row<LAYOUT>(A, kv_plane, G.n_tok, w.kv_rank, my_key, A.Lkv) : 0;
 
   bf16x8 kf[KS], vf[KS];
   load_row_frags<D>(kf, reinterpret_cast<const unsigned short*>(A.k), key_row, key_ok, half);
   load_row_frags<D>(vf, reinterpret_cast<const unsigned short*>(A.v), key_row, key_ok, half);
 
-  // first query row that sees any key of the workgroup (key_limit is
+  // first query row that sees any key of the workgroup (the limit is
   // non-decreasing in the row)
   int i0 = 0;
   if (A.causal) {
     int lo = 0, hi = A.Lq;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (key_limit(A, w, mid) >= key0) hi = mid; else lo = mid + 1;
+      if (llim<LAYOUT>(A, w.q_rank, w.kv_rank, mid) >= key0) hi = mid; else lo = mid + 1;
     }
     i0 = lo;
   }
@@ -244,114 +279,193 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dvT[db] = dkT[db] = f32x16{};
 
-  __shared__ __align__(1024) unsigned char qbuf[2][T::BYTES];
-  __shared__ __align__(1024) unsigned char obuf[2][T::BYTES];
-  __shared__ __align__(16) float lse2s[2][kRows];
-  __shared__ __align__(16) float dels[2][kRows];
-  __shared__ __align__(16) int lims[2][kRows];
+  // Four LDS slots for the streamed (Q, dO, lse, delta, limit) tiles.  Tile
+  // t+3 is loaded straight into LDS (buffer_load ... lds, no registers)
+  // while tile t is consumed, so each load has two tiles of time to land;
+  // during tile t the MFMAs read tile t (dV, dK) and tile t+1 (next S, dP).
+  constexpr int NSLOT = 4, LOOK = 3;
+  constexpr int ROWS_PER_INSTR = 1024 / T::RB;        // tile rows per 1 KiB load instruction
+  constexpr int INSTR = T::BYTES / 1024;              // per tensor per tile
+  constexpr int PER_WAVE = INSTR / 4;                 // per wave
+  constexpr int LOADS = 2 * PER_WAVE + 2;             // vector loads per wave per tile (Q, dO, lse, delta)
+  static_assert(PER_WAVE >= 1 && INSTR % 4 == 0, "tile must split over the four waves");
+  __shared__ __align__(1024) unsigned char qbuf[NSLOT][T::BYTES];
+  __shared__ __align__(1024) unsigned char obuf[NSLOT][T::BYTES];
+  // lse / delta: wave w loads rows 8 w .. 8 w + 7 with 4-byte lanes; every
+  // lane of the load owns a float of the wave's 64-float area (lanes 8..63
+  // read out of range and write zeros there)
+  __shared__ __align__(16) float lseb[NSLOT][4][64];
+  __shared__ __align__(16) float delb[NSLOT][4][64];
+  __shared__ __align__(16) int lims[NSLOT][kRows];
   const LdsOffsets<D> off(lane);
-  const unsigned short* Qb = reinterpret_cast<const unsigned short*>(A.q);
-  const unsigned short* Ob = reinterpret_cast<const unsigned short*>(G.dout);
+  const int64_t plane_elems = G.n_tok * D;
+  const unsigned rec_rows = (unsigned)(G.n_tok * T::RB);   // bytes of one (b, h) plane
+  const unsigned rec_vec = (unsigned)(G.n_tok * 4);
 
-  // iteration it: head g*group + it / nqt, query tile qt0 + it % nqt
-  auto tile_of = [&](int it, int& h, int64_t& row0) {
-    h = w.hkv * group + it / nqt;
-    row0 = (int64_t)(qt0 + it % nqt) * kRows;
-  };
-  TileRegs<D> rq, ro;
-  float pre_lse = 0.f, pre_del = 0.f;
-  int pre_lim = -1;
-  auto fetch = [&](int it) {
-    int h;
-    int64_t row0;
-    tile_of(it, h, row0);
+  // tile it: head hkv*group + it / nqt, query tile qt0 + it % nqt.  Lane
+  // l of load instruction i fills LDS slot 64 i + l of the tile: row
+  // ROWS_PER_INSTR i + l / CPR, chunk slot l % CPR holding logical chunk
+  // (l % CPR) ^ dswz(row).  Rows past the block read as zeros (offset out
+  // of the buffer's range).
+  auto issue = [&](int it, int slot) __attribute__((always_inline)) {
+    const int h = w.hkv * group + it / nqt;
+    const int row0 = (qt0 + it % nqt) * kRows;
     const int64_t qplane = (int64_t)w.b * A.H + h;
-    auto rowf = [&](int64_t i) { return nat_row(A, qplane, G.n_tok, w.q_rank, i, A.Lq); };
-    tile_fetch<D>(rq, Qb, row0, A.Lq, rowf);
-    tile_fetch<D>(ro, Ob, row0, A.Lq, rowf);
-    if (threadIdx.x < kRows) {
-      const int64_t i = row0 + threadIdx.x;
-      if (i < A.Lq) {
-        const int64_t r = rowf(i);
-        const float l = G.lse[r];
-        pre_lse = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;   // no visible key: P = 0
-        pre_del = G.delta[r];
-        pre_lim = (int)key_limit(A, w, i);
-      } else {
-        pre_lse = __builtin_huge_valf();   // no such query: P = 0
-        pre_del = 0.f;
-        pre_lim = -1;
-      }
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(A.q)) + qplane * plane_elems, 0,
+        rec_rows, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(G.dout)) + qplane * plane_elems, 0,
+        rec_rows, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const int ins = wave * PER_WAVE + u;
+      const int r = ins * ROWS_PER_INSTR + lane / T::CPR;
+      const int q = lane % T::CPR;
+      const int i = row0 + r;
+      const int voff = i < A.Lq ? lrow<LAYOUT>(w.q_rank, i, A.Lq, A.P) * T::RB + 16 * (q ^ dswz<D>(r)) : (int)rec_rows;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)(qbuf[slot] + ins * 1024),
+                                               16, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (__attribute__((address_space(3))) void*)(obuf[slot] + ins * 1024),
+                                               16, voff, 0, 0, 0);
     }
-  };
-  auto stash = [&](int buf) {
-    tile_store<D>(rq, qbuf[buf]);
-    tile_store<D>(ro, obuf[buf]);
+    // lse and delta: wave w loads rows 8 w .. 8 w + 7 (lanes 0..7)
+    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(G.lse2) + qplane * G.n_tok, 0, rec_vec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(G.delta) + qplane * G.n_tok, 0, rec_vec, 0x00020000);
+    {
+      const int i = row0 + 8 * wave + lane;
+      const int voff = (lane < 8 && i < A.Lq) ? lrow<LAYOUT>(w.q_rank, i, A.Lq, A.P) * 4 : (int)rec_vec;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)(&lseb[slot][wave][0]),
+                                               4, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (__attribute__((address_space(3))) void*)(&delb[slot][wave][0]),
+                                               4, voff, 0, 0, 0);
+    }
     if (threadIdx.x < kRows) {
-      lse2s[buf][threadIdx.x] = pre_lse;
-      dels[buf][threadIdx.x] = pre_del;
-      lims[buf][threadIdx.x] = pre_lim;
+      const int i = row0 + threadIdx.x;
+      lims[slot][threadIdx.x] = i < A.Lq ? llim<LAYOUT>(A, w.q_rank, w.kv_rank, i) : -1;
     }
   };
 
+  // S and dP of a tile: [32 queries x 32 keys], one key per lane column;
+  // register r holds query 8 (r / 4) + 4 half + r % 4 of the tile.
+  f32x16 sc = f32x16{}, dpc = f32x16{};
   if (total > 0) {
-    fetch(0);
-    stash(0);
-    if (total > 1) fetch(1);
+#pragma unroll
+    for (int it = 0; it < LOOK; ++it)
+      if (it < total) issue(it, it);
+    wait_vmcnt0();
     __syncthreads();
-  }
-  for (int it = 0; it < total; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < total) {
-      stash(buf ^ 1);                 // tile it+1 (its buffer was freed by the last barrier)
-      if (it + 2 < total) fetch(it + 2);
-    }
-    const unsigned char* qt = qbuf[buf];
-    const unsigned char* ot = obuf[buf];
-    // S = Q K^T and dP = dO V^T, [32 queries x 32 keys], one key per lane column
-    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(qt, off, ks), kf[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(ot, off, ks), vf[ks], dp, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(qbuf[0], off, ks), kf[ks], sc, 0, 0, 0);
+      dpc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(obuf[0], off, ks), vf[ks], dpc, 0, 0, 0);
     }
-    // register r holds query 8 (r / 4) + 4 half + r % 4 of the tile
-    const bool masked = A.causal && lims[buf][0] < wave_last;
-    f32x16 pf, dsf;
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int q0 = 8 * g4 + 4 * half;
-      const float4 l4 = *reinterpret_cast<const float4*>(&lse2s[buf][q0]);
-      const float4 d4 = *reinterpret_cast<const float4*>(&dels[buf][q0]);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-      int lm[4] = {0, 0, 0, 0};
-      if (masked) {
-        const int4 m4 = *reinterpret_cast<const int4*>(&lims[buf][q0]);
-        lm[0] = m4.x; lm[1] = m4.y; lm[2] = m4.z; lm[3] = m4.w;
+  }
+
+  // One tile, cut into one-MFMA steps fenced with sched_barrier:
+  //   phase A: S(t+1), dP(t+1) (16 MFMAs, when MORE) while the VALU turns
+  //            S(t), dP(t) into P(t) and dS(t), one element per step;
+  //   phase B: dV^T += dO^T P(t), dK^T += Q^T dS(t) (16 MFMAs).
+  auto body = [&](auto slot_tag, auto more_tag, int t) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_tag)::value;          // t % NSLOT
+    constexpr int SN = (SL + 1) % NSLOT;                   // slot of tile t+1
+    constexpr int SF = (SL + LOOK) % NSLOT;                // slot of tile t+3 (free: it held t-1)
+    constexpr bool MORE = decltype(more_tag)::value;       // t + 1 < total
+    const bool ahead = t + LOOK < total;
+    if (ahead) issue(t + LOOK, SF);
+    // The causal limit is applied to every element (a row's limit is at
+    // least every key of an unmasked tile, so the test is a no-op there);
+    // testing per element keeps the phase free of branches.
+    f32x16 sn = f32x16{}, dpn = f32x16{}, pf, dsf;
+    bf16x8 fa[2];
+    if constexpr (MORE) fa[0] = read_rowfrag<D>(qbuf[SN], off, 0);
+    float lv[4], dv[4];
+    int lm[4];
+    static_for<2 * KS>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (MORE) {
+        // operand of step i + 1: dO fragment i/2 after a Q fragment, else Q fragment i/2 + 1
+        if constexpr (i + 1 < 2 * KS)
+          fa[(i + 1) & 1] = ((i + 1) & 1) ? read_rowfrag<D>(obuf[SN], off, (i + 1) >> 1)
+                                          : read_rowfrag<D>(qbuf[SN], off, (i + 1) >> 1);
+        if constexpr ((i & 1) == 0)
+          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0], kf[i >> 1], sn, 0, 0, 0);
+        else
+          dpn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1], vf[i >> 1], dpn, 0, 0, 0);
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g4 + e;
-        float p = fast_exp2(__builtin_fmaf(s[r], c, -lv[e]));
-        if (masked && my_key > lm[e]) p = 0.f;
-        pf[r] = p;
-        dsf[r] = p * (dp[r] - dv[e]);
-      }
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS (contraction over the tile's queries)
+      // VALU: the 16 elements spread over the 2 KS steps
+      static_for<16>([&](auto rc) __attribute__((always_inline)) {
+        constexpr int r = decltype(rc)::value;
+        if constexpr (r * 2 * KS / 16 == i) {
+          if constexpr ((r & 3) == 0) {
+            const int q0 = 8 * (r >> 2) + 4 * half;   // rows q0 .. q0 + 3 (loaded by wave r / 4)
+            const float4 l4 = *reinterpret_cast<const float4*>(&lseb[SL][r >> 2][4 * half]);
+            const float4 d4 = *reinterpret_cast<const float4*>(&delb[SL][r >> 2][4 * half]);
+            const int4 m4 = *reinterpret_cast<const int4*>(&lims[SL][q0]);
+            lv[0] = l4.x; lv[1] = l4.y; lv[2] = l4.z; lv[3] = l4.w;
+            dv[0] = d4.x; dv[1] = d4.y; dv[2] = d4.z; dv[3] = d4.w;
+            lm[0] = m4.x; lm[1] = m4.y; lm[2] = m4.z; lm[3] = m4.w;
+          }
+          float p = fast_exp2(__builtin_fmaf(sc[r], c, -lv[r & 3]));
+          p = my_key > lm[r & 3] ? 0.f : p;
+          pf[r] = p;
+          dsf[r] = p * (dpc[r] - dv[r & 3]);
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int hc = 0; hc < 2; ++hc) {
-      const bf16x8 pb = pack8(pf, 8 * hc);
-      const bf16x8 db8 = pack8(dsf, 8 * hc);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_trfrag<D>(ot, off, db, hc), pb, dvT[db], 0, 0, 0);
-        dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_trfrag<D>(qt, off, db, hc), db8, dkT[db], 0, 0, 0);
-      }
+      pb[hc] = pack8(pf, 8 * hc);
+      dsb[hc] = pack8(dsf, 8 * hc);
     }
+    // phase B: step j uses (db, hc) = ((j / 2) % NDB, (j / 2) / NDB), dV on
+    // even steps, dK on odd ones; fragments read two steps ahead
+    constexpr int NB = 4 * NDB;
+    auto tfrag = [&](int j) __attribute__((always_inline)) -> bf16x8 {
+      const int db = (j >> 1) % NDB, hc = (j >> 1) / NDB;
+      return (j & 1) ? read_trfrag<D>(qbuf[SL], off, db, hc) : read_trfrag<D>(obuf[SL], off, db, hc);
+    };
+    bf16x8 fb[3];
+    fb[0] = tfrag(0);
+    fb[1] = tfrag(1);
+    static_for<NB>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int db = (j >> 1) % NDB, hc = (j >> 1) / NDB;
+      if constexpr (j + 2 < NB) fb[(j + 2) % 3] = tfrag(j + 2);
+      if constexpr ((j & 1) == 0)
+        dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j % 3], pb[hc], dvT[db], 0, 0, 0);
+      else
+        dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j % 3], dsb[hc], dkT[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    sc = sn;
+    dpc = dpn;
+    // tile t+2 must have landed before the next tile reads it: only tile
+    // t+3's loads (issued above) may still be in flight
+    if (ahead) wait_vmcnt<LOADS>(); else wait_vmcnt0();
     __syncthreads();
+  };
+
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+  auto slot = [](auto n) { return std::integral_constant<int, decltype(n)::value>{}; };
+  int t = 0;
+  for (; t + NSLOT < total; t += NSLOT) {
+    static_for<NSLOT>([&](auto k) __attribute__((always_inline)) { body(slot(k), Yes{}, t + decltype(k)::value); });
   }
+  // 1..NSLOT tiles left (t % NSLOT == 0): all but the last have a successor
+  const int left = total - t;
+  static_for<NSLOT>([&](auto k) __attribute__((always_inline)) {
+    constexpr int kk = decltype(k)::value;
+    if (kk < left) {
+      if (kk + 1 < left) body(slot(k), Yes{}, t + kk);
+      else body(slot(k), No{}, t + kk);
+    }
+  });
   if (!key_ok || total == 0) return;
   float* dk_row = G.dk_acc + key_row * D;
   float* dv_row = G.dv_acc + key_row * D;
@@ -366,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
 // dQ: one workgroup per (query host, batch, query head, 128-row query tile),
 // sweeping the visible 32-key tiles of the paired kv block.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int LAYOUT>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
   using T = RowTile<D>;
   constexpr int KS = D / 16, NDB = D / 32;
@@ -376,23 +490,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, col = lane & 31;
   const float c = A.scale_log2;
-  const int64_t row_first = (int64_t)w.qtile * kDqRows;
-  const int64_t row_last = (row_first + kDqRows < A.Lq ? row_first + kDqRows : A.Lq) - 1;
-  const int64_t wave_first = row_first + wave * 32 < row_last ? row_first + wave * 32 : row_last;
-  const int64_t my_row = row_first + wave * 32 + col;
+  const int row_first = w.qtile * kDqRows;
+  const int row_last = (row_first + kDqRows < A.Lq ? row_first + kDqRows : A.Lq) - 1;
+  const int wave_first = row_first + wave * 32 < row_last ? row_first + wave * 32 : row_last;
+  const int my_row = row_first + wave * 32 + col;
   const bool row_ok = my_row < A.Lq;
-  const int lim32 = (int)key_limit(A, w, row_ok ? my_row : row_last);
-  const int64_t kv_end = key_limit(A, w, row_last) + 1;
-  const int64_t full_end = key_limit(A, w, wave_first) + 1;
+  const int lim32 = llim<LAYOUT>(A, w.q_rank, w.kv_rank, row_ok ? my_row : row_last);
+  const int kv_end = llim<LAYOUT>(A, w.q_rank, w.kv_rank, row_last) + 1;
+  const int full_end = llim<LAYOUT>(A, w.q_rank, w.kv_rank, wave_first) + 1;
   const int ntiles = (int)((kv_end + kRows - 1) / kRows);
 
   const int64_t qplane = (int64_t)w.b * A.H + w.h;
-  const int64_t qrow = row_ok ? nat_row(A, qplane, G.n_tok, w.q_rank, my_row, A.Lq) : 0;
+  const int64_t qrow = row_ok ? nat_row<LAYOUT>(A, qplane, G.n_tok, w.q_rank, my_row, A.Lq) : 0;
   bf16x8 qf[KS], of[KS];
   load_row_frags<D>(qf, reinterpret_cast<const unsigned short*>(A.q), qrow, row_ok, half);
   load_row_frags<D>(of, reinterpret_cast<const unsigned short*>(G.dout), qrow, row_ok, half);
-  const float lse_in = row_ok ? G.lse[qrow] : kNegInf;
-  const float lse2 = lse_in == kNegInf ? __builtin_huge_valf() : lse_in * kLog2e;   // no visible key: P = 0
+  const float lse2 = row_ok ? G.lse2[qrow] : __builtin_huge_valf();   // past the block: P = 0
   const float del = row_ok ? G.delta[qrow] : 0.f;
 
   f32x16 dqT[NDB];
@@ -405,11 +518,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
   const unsigned short* Kb = reinterpret_cast<const unsigned short*>(A.k);
   const unsigned short* Vb = reinterpret_cast<const unsigned short*>(A.v);
   const int64_t kv_plane = (int64_t)w.b * A.Hkv + w.hkv;
-  auto rowf = [&](int64_t j) { return nat_row(A, kv_plane, G.n_tok, w.kv_rank, j, A.Lkv); };
+  auto rowf = [&](int j) { return nat_row<LAYOUT>(A, kv_plane, G.n_tok, w.kv_rank, j, A.Lkv); };
   TileRegs<D> rk, rv;
   auto fetch = [&](int t) {
-    tile_fetch<D>(rk, Kb, (int64_t)t * kRows, A.Lkv, rowf);
-    tile_fetch<D>(rv, Vb, (int64_t)t * kRows, A.Lkv, rowf);
+    tile_fetch<D>(rk, Kb, t * kRows, A.Lkv, rowf);
+    tile_fetch<D>(rv, Vb, t * kRows, A.Lkv, rowf);
   };
   auto stash = [&](int buf) {
     tile_store<D>(rk, kbuf[buf]);
@@ -463,9 +576,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
   for (int db = 0; db < NDB; ++db) add_block(dq_row, dqT[db], db, half, G.scale);
 }
 
-// delta_i = sum_c dO_ic O_ic (one wavefront per row), bf16 inputs.
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* out, const __bf16* dout, float* delta,
-                                                        int64_t rows, int d) {
+// delta_i = sum_c dO_ic O_ic (one wavefront per row, bf16 inputs) and the
+// base-2 lse the kernels subtract: lse2_i = lse_i log2(e), +inf for a row
+// without visible keys (so that its P is 0).
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* out, const __bf16* dout, const float* lse,
+                                                        float* delta, float* lse2, int64_t rows, int d) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
@@ -473,7 +588,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* out, const 
   for (int cc = lane; cc < d; cc += 64) acc += (float)out[row * d + cc] * (float)dout[row * d + cc];
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-  if (lane == 0) delta[row] = acc;
+  if (lane == 0) {
+    delta[row] = acc;
+    const float l = lse[row];
+    lse2[row] = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
+  }
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
@@ -495,10 +614,12 @@ unsigned elementwise_grid(int64_t n) {
 int bwd_dq_rows() { return kDqRows; }
 int bwd_dkdv_rows() { return kDkdvKeys; }
 
-hipError_t launch_bwd_prep(const void* out, const void* dout, float* delta, int64_t rows, int d, hipStream_t s) {
+hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, float* delta, float* lse2,
+                           int64_t rows, int d, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
-                     reinterpret_cast<const __bf16*>(out), reinterpret_cast<const __bf16*>(dout), delta, rows, d);
+                     reinterpret_cast<const __bf16*>(out), reinterpret_cast<const __bf16*>(dout), lse, delta, lse2,
+                     rows, d);
   return hipGetLastError();
 }
 
@@ -515,22 +636,52 @@ hipError_t launch_to_bf16(const float* src, void* dst, int64_t n, hipStream_t s)
   return hipGetLastError();
 }
 
+template <int D, int L>
+hipError_t launch_dkdv_t(const BwdArgs& a, unsigned g, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, L>), dim3(g), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, int L>
+hipError_t launch_dq_t(const BwdArgs& a, unsigned g, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_dq_kernel<D, L>), dim3(g), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dkdv_d(const BwdArgs& a, unsigned g, hipStream_t s) {
+  switch (a.s.layout) {
+    case 0: return launch_dkdv_t<D, 0>(a, g, s);
+    case 1: return launch_dkdv_t<D, 1>(a, g, s);
+    case 2: return launch_dkdv_t<D, 2>(a, g, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t launch_dq_d(const BwdArgs& a, unsigned g, hipStream_t s) {
+  switch (a.s.layout) {
+    case 0: return launch_dq_t<D, 0>(a, g, s);
+    case 1: return launch_dq_t<D, 1>(a, g, s);
+    case 2: return launch_dq_t<D, 2>(a, g, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, hipStream_t s) {
   const int64_t g = (int64_t)a.s.n_hosts * a.s.B * a.s.Hkv * a.n_kvtiles;
   if (g <= 0) return hipSuccess;
-  if (d == 128) hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)g), dim3(kThreads), 0, s, a);
-  else if (d == 64) hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)g), dim3(kThreads), 0, s, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (d == 128) return launch_dkdv_d<128>(a, (unsigned)g, s);
+  if (d == 64) return launch_dkdv_d<64>(a, (unsigned)g, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int d, hipStream_t s) {
   const int64_t g = (int64_t)a.s.n_hosts * a.s.B * a.s.H * a.s.n_qtiles;
   if (g <= 0) return hipSuccess;
-  if (d == 128) hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)g), dim3(kThreads), 0, s, a);
-  else if (d == 64) hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)g), dim3(kThreads), 0, s, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (d == 128) return launch_dq_d<128>(a, (unsigned)g, s);
+  if (d == 64) return launch_dq_d<64>(a, (unsigned)g, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace ra

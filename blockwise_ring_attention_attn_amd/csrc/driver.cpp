@@ -626,13 +626,14 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
 // so the kernels of one step never write the same rows.
 // ---------------------------------------------------------------------------
 struct BwdWs {
-  size_t off_delta, off_dq, off_dk, off_dv, total;
+  size_t off_delta, off_lse2, off_dq, off_dk, off_dv, total;
 };
 
 static BwdWs bwd_ws_layout(int B, int H, int Hkv, long long N, int d) {
   BwdWs w{};
   size_t off = 0;
   w.off_delta = off; off += align_up((size_t)B * H * N * 4);
+  w.off_lse2 = off; off += align_up((size_t)B * H * N * 4);
   w.off_dq = off; off += align_up((size_t)B * H * N * d * 4);
   w.off_dk = off; off += align_up((size_t)B * Hkv * N * d * 4);
   w.off_dv = off; off += align_up((size_t)B * Hkv * N * d * 4);
@@ -685,7 +686,7 @@ ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void*
   a.s.n_qtiles = (int)nqt;
   a.s.scale_log2 = scale * 1.4426950408889634f;
   a.dout = dout;
-  a.lse = lse;
+  a.lse2 = reinterpret_cast<float*>(wsb + W.off_lse2);
   a.delta = reinterpret_cast<float*>(wsb + W.off_delta);
   a.dq_acc = reinterpret_cast<float*>(wsb + W.off_dq);
   a.dk_acc = reinterpret_cast<float*>(wsb + W.off_dk);
@@ -698,7 +699,9 @@ ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void*
   RA_HIP(launch_fill_zero(a.dq_acc, nq, cs), "fill launch");
   RA_HIP(launch_fill_zero(a.dk_acc, nkv, cs), "fill launch");
   RA_HIP(launch_fill_zero(a.dv_acc, nkv, cs), "fill launch");
-  RA_HIP(launch_bwd_prep(out, dout, const_cast<float*>(a.delta), (int64_t)B * H * N, d, cs), "prep launch");
+  RA_HIP(launch_bwd_prep(out, dout, lse, const_cast<float*>(a.delta), const_cast<float*>(a.lse2), (int64_t)B * H * N,
+                         d, cs),
+         "prep launch");
   for (int s = 0; s < P; ++s) {
     // hosts with visible work against kv block (r + s) mod P
     int lo = -1, hi = -1;

@@ -148,6 +148,14 @@ __device__ __forceinline__ u32x2 lds_read_tr(const unsigned char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// s_waitcnt vmcnt(N) (at most N vector-memory loads of this wave still in
+// flight), leaving expcnt / lgkmcnt unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 __device__ __forceinline__ void wait_vmcnt0() {
   // s_waitcnt vmcnt(0), leaving expcnt / lgkmcnt unconstrained
   __builtin_amdgcn_s_waitcnt(0x0F70);

@@ -52,7 +52,7 @@ struct StepArgs {
 struct BwdArgs {
   StepArgs s;
   const void* dout;       // [B, H, N, d], same rows as q
-  const float* lse;       // [B, H, N] natural-log lse of the forward
+  const float* lse2;      // [B, H, N] lse of the forward times log2(e) (+inf: no visible key)
   const float* delta;     // [B, H, N] rowsum(dO * O)
   float* dq_acc;          // [B, H, N, d]
   float* dk_acc;          // [B, Hkv, N, d]
@@ -103,7 +103,8 @@ hipError_t launch_spin(int microseconds, hipStream_t s);  // bounded busy wait (
 // kernels; fp32 accumulator -> bf16 conversion.
 int bwd_dq_rows();     // query rows per dQ workgroup
 int bwd_dkdv_rows();   // keys per dK/dV workgroup
-hipError_t launch_bwd_prep(const void* out, const void* dout, float* delta, int64_t rows, int d, hipStream_t s);
+hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, float* delta, float* lse2,
+                           int64_t rows, int d, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 hipError_t launch_to_bf16(const float* src, void* dst, int64_t n, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, hipStream_t s);
