@@ -108,37 +108,6 @@ __device__ __forceinline__ int64_t nat_row(const StepArgs& A, int64_t plane, int
   return plane * n_tok + lrow<LAYOUT>(rank, i, blk, A.P);
 }
 
-// Global -> register prefetch and register -> LDS store of one 32-row tile
-// of a natural-order bf16 array; rows at or beyond `valid` read as zero.
-template <int D>
-struct TileRegs {
-  u32x4 v[RowTile<D>::PER_THREAD];
-};
-
-template <int D, typename RowFn>
-__device__ __forceinline__ void tile_fetch(TileRegs<D>& t, const unsigned short* base, int row0, int valid,
-                                           RowFn&& row_of) {
-  using T = RowTile<D>;
-#pragma unroll
-  for (int u = 0; u < T::PER_THREAD; ++u) {
-    const int ch = u * kThreads + threadIdx.x;
-    const int r = ch / T::CPR, c = ch % T::CPR;
-    const int i = row0 + r;
-    t.v[u] = i < valid ? *reinterpret_cast<const u32x4*>(base + row_of(i) * D + 8 * c) : u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void tile_store(const TileRegs<D>& t, unsigned char* lds) {
-  using T = RowTile<D>;
-#pragma unroll
-  for (int u = 0; u < T::PER_THREAD; ++u) {
-    const int ch = u * kThreads + threadIdx.x;
-    const int r = ch / T::CPR, c = ch % T::CPR;
-    *reinterpret_cast<u32x4*>(lds + r * T::RB + 16 * (c ^ dswz<D>(r))) = t.v[u];
-  }
-}
-
 // Per-lane LDS offsets.  Row-fragment reads (A operand, lane l: row l % 32,
 // dims 16 ks + 8 (l / 32) .. + 7): roff[ks].  Transposing reads for the
 // contraction over the tile's rows (A operand, lane l: dim 32 db + l % 32,
@@ -492,12 +461,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
   const float c = A.scale_log2;
   const int row_first = w.qtile * kDqRows;
   const int row_last = (row_first + kDqRows < A.Lq ? row_first + kDqRows : A.Lq) - 1;
-  const int wave_first = row_first + wave * 32 < row_last ? row_first + wave * 32 : row_last;
   const int my_row = row_first + wave * 32 + col;
   const bool row_ok = my_row < A.Lq;
   const int lim32 = llim<LAYOUT>(A, w.q_rank, w.kv_rank, row_ok ? my_row : row_last);
   const int kv_end = llim<LAYOUT>(A, w.q_rank, w.kv_rank, row_last) + 1;
-  const int full_end = llim<LAYOUT>(A, w.q_rank, w.kv_rank, wave_first) + 1;
   const int ntiles = (int)((kv_end + kRows - 1) / kRows);
 
   const int64_t qplane = (int64_t)w.b * A.H + w.h;
@@ -512,55 +479,77 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqT[db] = f32x16{};
 
-  __shared__ __align__(1024) unsigned char kbuf[2][T::BYTES];
-  __shared__ __align__(1024) unsigned char vbuf[2][T::BYTES];
+  // Four LDS slots for the K / V tiles; tile t+3 is loaded straight into
+  // LDS while tile t computes (two tiles of time for each load to land).
+  constexpr int NSLOT = 4, LOOK = 3;
+  constexpr int ROWS_PER_INSTR = 1024 / T::RB;
+  constexpr int INSTR = T::BYTES / 1024;
+  constexpr int PER_WAVE = INSTR / 4;
+  constexpr int LOADS = 2 * PER_WAVE;   // vector loads per wave per tile
+  static_assert(PER_WAVE >= 1 && INSTR % 4 == 0, "tile must split over the four waves");
+  __shared__ __align__(1024) unsigned char kbuf[NSLOT][T::BYTES];
+  __shared__ __align__(1024) unsigned char vbuf[NSLOT][T::BYTES];
   const LdsOffsets<D> off(lane);
-  const unsigned short* Kb = reinterpret_cast<const unsigned short*>(A.k);
-  const unsigned short* Vb = reinterpret_cast<const unsigned short*>(A.v);
   const int64_t kv_plane = (int64_t)w.b * A.Hkv + w.hkv;
-  auto rowf = [&](int j) { return nat_row<LAYOUT>(A, kv_plane, G.n_tok, w.kv_rank, j, A.Lkv); };
-  TileRegs<D> rk, rv;
-  auto fetch = [&](int t) {
-    tile_fetch<D>(rk, Kb, t * kRows, A.Lkv, rowf);
-    tile_fetch<D>(rv, Vb, t * kRows, A.Lkv, rowf);
-  };
-  auto stash = [&](int buf) {
-    tile_store<D>(rk, kbuf[buf]);
-    tile_store<D>(rv, vbuf[buf]);
+  const unsigned rec_rows = (unsigned)(G.n_tok * T::RB);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(A.k)) + kv_plane * G.n_tok * D, 0, rec_rows,
+      0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(A.v)) + kv_plane * G.n_tok * D, 0, rec_rows,
+      0x00020000);
+  // Lane l of load instruction i fills LDS slot 64 i + l of the tile: row
+  // ROWS_PER_INSTR i + l / CPR, chunk slot l % CPR holding logical chunk
+  // (l % CPR) ^ dswz(row); keys past the block read as zeros.
+  auto issue = [&](int t, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const int ins = wave * PER_WAVE + u;
+      const int r = ins * ROWS_PER_INSTR + lane / T::CPR;
+      const int q = lane % T::CPR;
+      const int j = t * kRows + r;
+      const int voff = j < A.Lkv ? lrow<LAYOUT>(w.kv_rank, j, A.Lkv, A.P) * T::RB + 16 * (q ^ dswz<D>(r)) : (int)rec_rows;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kbuf[slot] + ins * 1024),
+                                               16, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vbuf[slot] + ins * 1024),
+                                               16, voff, 0, 0, 0);
+    }
   };
 
   if (ntiles > 0) {
-    fetch(0);
-    stash(0);
-    if (ntiles > 1) fetch(1);
-    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < LOOK; ++t)
+      if (t < ntiles) issue(t, t);
   }
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) {
-      stash(buf ^ 1);
-      if (t + 2 < ntiles) fetch(t + 2);
-    }
-    const unsigned char* kt = kbuf[buf];
-    const unsigned char* vt = vbuf[buf];
-    // S^T = K Q^T and dP^T = V dO^T, [32 keys x 32 queries], one query per lane column
+  // tile t: S^T = K Q^T and dP^T = V dO^T ([32 keys x 32 queries], one query
+  // per lane column; register r holds key 32 t + 8 (r / 4) + 4 half + r % 4),
+  // dS^T, then dQ^T += K^T dS^T (contraction over the tile's keys)
+  auto body = [&](auto slot_tag, int t) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_tag)::value;
+    constexpr int SF = (SL + LOOK) % NSLOT;
+    // tile t must have landed: only the loads of tiles t+1, t+2 may remain
+    if (t + 2 < ntiles) wait_vmcnt<2 * LOADS>();
+    else if (t + 1 < ntiles) wait_vmcnt<LOADS>();
+    else wait_vmcnt0();
+    __syncthreads();
+    if (t + LOOK < ntiles) issue(t + LOOK, SF);   // its slot held tile t-1, done before the barrier
+    const unsigned char* kt = kbuf[SL];
+    const unsigned char* vt = vbuf[SL];
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(kt, off, ks), qf[ks], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(vt, off, ks), of[ks], dp, 0, 0, 0);
     }
-    // register r holds key t*32 + 8 (r / 4) + 4 half + r % 4
-    const bool masked = t * kRows + kRows > full_end;
+    // causal limit per element, branch free (a no-op on unmasked tiles)
     const int bound = lim32 - t * kRows - 4 * half;
     f32x16 dsf;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float p = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
-      if (masked && 8 * (r >> 2) + (r & 3) > bound) p = 0.f;
+      p = 8 * (r >> 2) + (r & 3) > bound ? 0.f : p;
       dsf[r] = p * (dp[r] - del);
     }
-    // dQ^T += K^T dS^T (contraction over the tile's keys)
 #pragma unroll
     for (int hc = 0; hc < 2; ++hc) {
       const bf16x8 db8 = pack8(dsf, 8 * hc);
@@ -568,8 +557,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
       for (int db = 0; db < NDB; ++db)
         dqT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_trfrag<D>(kt, off, db, hc), db8, dqT[db], 0, 0, 0);
     }
-    __syncthreads();
-  }
+  };
+  int t = 0;
+  for (; t + NSLOT <= ntiles; t += NSLOT)
+    static_for<NSLOT>([&](auto k) __attribute__((always_inline)) {
+      body(std::integral_constant<int, decltype(k)::value>{}, t + decltype(k)::value);
+    });
+  static_for<NSLOT - 1>([&](auto k) __attribute__((always_inline)) {
+    if (t + decltype(k)::value < ntiles) body(std::integral_constant<int, decltype(k)::value>{}, t + decltype(k)::value);
+  });
   if (!row_ok || ntiles == 0) return;
   float* dq_row = G.dq_acc + qrow * D;
 #pragma unroll
