@@ -13,6 +13,10 @@ resident in HBM.  Prints ONE JSON line:
   cpu_baseline the fp64 oracle on a bounded row sample of the same workload
   decode       split-KV decode (16 sequences, H=32/Hkv=8, L=262144, d=128,
                P=8): algorithmic HBM GB/s, with its kernel's roofline
+  backward     ring_attn_bwd on the prefill workload (reverse ring,
+               recomputation): TFLOP/s at 10 d FLOPs per unmasked pair per
+               query head (the five products QK^T, dO V^T, P^T dO, dS K,
+               dS^T Q)
 """
 from __future__ import annotations
 
@@ -174,6 +178,45 @@ def run_prefill(args) -> dict:
     return res
 
 
+def run_backward(args) -> dict:
+    import torch
+    import blockwise_ring_attention_attn_amd as ra
+    import synth
+    c = PREFILL
+    q, k, v = synth.qkv(c["seed"], c["B"], c["H"], c["Hkv"], c["N"], c["d"], "bf16")
+    do = synth.tensor(c["seed"], synth.TENSOR_DOUT, c["B"], c["H"], c["N"], c["d"], "bf16")
+    qd, kd, vd, dod = upload(q, "bf16"), upload(k, "bf16"), upload(v, "bf16"), upload(do, "bf16")
+    del q, k, v, do
+    stream = torch.cuda.current_stream()
+    out, lse = ra.ring_attn_fwd(qd, kd, vd, P=c["P"], causal=c["causal"], layout=c["layout"], stream=stream)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    nb = ra.load().ring_attn_bwd_ws_bytes(c["B"], c["H"], c["Hkv"], c["N"], c["d"], c["P"], ra.RA_BF16)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda:0")
+
+    def step():
+        ra.ring_attn_bwd(qd, kd, vd, out, dod, lse, P=c["P"], causal=c["causal"], layout=c["layout"], dq=dq, dk=dk,
+                         dv=dv, ws=ws, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    n = max(3, args.steps // 4)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(n):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / n
+    flops = 2.5 * prefill_flops(c)
+    tflops = flops / (ms * 1e-3) / 1e12
+    del qd, kd, vd, dod, out, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return {"metric": "causal ring-attn bwd TFLOP/s (10 d per unmasked pair)", "value": tflops, "unit": "TFLOP/s",
+            "ms_per_step": ms, "steps": n, "flops_per_step": flops,
+            "pct_bf16_mfma_peak": 100.0 * tflops / MFMA_BF16_PEAK_TFLOPS,
+            "config": {"workload": "backward of the prefill workload (same shapes, upstream gradient seeded)"}}
+
+
 def run_decode(args) -> dict:
     import torch
     import blockwise_ring_attention_attn_amd as ra
@@ -235,8 +278,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=("prefill", "decode"), default=None,
+    ap.add_argument("--only", choices=("prefill", "decode", "backward"), default=None,
                     help="run one workload only (profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first do a plain device copy of this many MiB (counter calibration)")
@@ -253,6 +297,9 @@ def main():
         calibration_copy(args.calib_copy_mib)
     if args.only == "decode":
         print(json.dumps(run_decode(args)), flush=True)
+        return
+    if args.only == "backward":
+        print(json.dumps(run_backward(args)), flush=True)
         return
     pre = run_prefill(args)
     c = PREFILL
@@ -281,6 +328,8 @@ def main():
         line["cpu_baseline"] = pre["cpu_baseline"]
     if not args.no_decode and args.only is None:
         line["decode"] = run_decode(args)
+    if not args.no_backward and args.only is None:
+        line["backward"] = run_backward(args)
     print(json.dumps(line), flush=True)
 
 

@@ -41,8 +41,9 @@ namespace {
 
 using namespace dev;
 
-// Epilogue.  The previous state of a row (earlier ring steps) is read once,
-// the merge weights are formed once per row, every group of 4 dims is merged
+// Epilogue.  Where a launch merges with the state of earlier ring steps at
+// the end (the fp32 kernel), the previous state of a row is read once, the
+// merge weights are formed once per row, every group of 4 dims is merged
 // and written, and only then are the row scalars (m, l or lse) written.
 struct RowMerge {
   float ca, cb;      // weights of the stored state and of this launch's partial
@@ -68,9 +69,9 @@ __device__ __forceinline__ RowMerge row_merge(const StepArgs& A, int64_t idx, fl
 
 template <typename OutT>
 __device__ __forceinline__ void store_dims4(const StepArgs& A, int64_t idx, int dim, int D, bool fin,
-                                            const RowMerge& rm, const float o[4]) {
+                                            const RowMerge& rm, const float o[4], bool merge) {
   float oo[4] = {rm.cb * o[0], rm.cb * o[1], rm.cb * o[2], rm.cb * o[3]};
-  if (A.has_prev) {
+  if (merge) {
     const float4 op = *reinterpret_cast<const float4*>(A.o + idx * D + dim);
     oo[0] += rm.ca * op.x;
     oo[1] += rm.ca * op.y;
@@ -238,10 +239,30 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void step_bf16_kernel(StepArgs 
   for (int db = 0; db < D / 32; ++db)
     vaddr[db] = (4 * half + jp) * T::RB + 16 * ((4 * db + ug) ^ vswz<D>(jp)) + 8 * (lane & 1);
 
+  // Online-softmax state: resumed from the stored (m, l, o) of the earlier
+  // ring steps, so the epilogue only stores.  The stored o and l are
+  // relative to the stored m; l lives in half 0 (each half sums its own
+  // keys and the halves are added at the end).
   f32x16 oacc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
+  if (A.has_prev && row_ok) {
+    const int64_t idx = q_row_index(A, w, my_row);
+    m_run = A.m[idx] * kLog2e;
+    l_run = half == 0 ? A.l[idx] : 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 x = *reinterpret_cast<const float4*>(A.o + idx * D + db * 32 + 8 * g + 4 * half);
+        oacc[db][4 * g] = x.x;
+        oacc[db][4 * g + 1] = x.y;
+        oacc[db][4 * g + 2] = x.z;
+        oacc[db][4 * g + 3] = x.w;
+      }
+  } else {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+  }
   const float c = A.scale_log2;
 
   // Software pipeline over key tiles: iteration j computes S(j+1) = K(j+1) Q^T
@@ -438,13 +459,13 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void step_bf16_kernel(StepArgs 
   if (!row_ok) return;
   const bool fin = w.q_rank >= A.fin_lo && w.q_rank < A.fin_hi;
   const int64_t idx = q_row_index(A, w, my_row);
-  const RowMerge rm = row_merge(A, idx, m_run, l_tot);
+  const RowMerge rm{0.f, 1.f, m_run, l_tot};   // the state already includes earlier steps
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const float o4[4] = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
-      store_dims4<OutT>(A, idx, db * 32 + 8 * g + 4 * half, D, fin, rm, o4);
+      store_dims4<OutT>(A, idx, db * 32 + 8 * g + 4 * half, D, fin, rm, o4, false);
     }
   if (half == 0) store_row(A, idx, fin, rm);
 }
@@ -530,7 +551,7 @@ __global__ __launch_bounds__(kF32BM) void step_f32_kernel(StepArgs A) {
 #pragma unroll
   for (int c2 = 0; c2 < D; c2 += 4) {
     const float o4[4] = {o[c2], o[c2 + 1], o[c2 + 2], o[c2 + 3]};
-    store_dims4<float>(A, idx, c2, D, fin, rm, o4);
+    store_dims4<float>(A, idx, c2, D, fin, rm, o4, A.has_prev);
   }
   store_row(A, idx, fin, rm);
 }
