@@ -48,10 +48,11 @@ using namespace dev;
 struct RowMerge {
   float ca, cb;      // weights of the stored state and of this launch's partial
   float m_new, l_new;
+  float l_norm;      // divisor of the output at finalization
 };
 
 __device__ __forceinline__ RowMerge row_merge(const StepArgs& A, int64_t idx, float m2, float l) {
-  RowMerge r{0.f, 1.f, m2, l};
+  RowMerge r{0.f, 1.f, m2, l, l};
   if (A.has_prev) {
     const float mp = A.m[idx] * kLog2e;
     const float lp = A.l[idx];
@@ -63,6 +64,7 @@ __device__ __forceinline__ RowMerge row_merge(const StepArgs& A, int64_t idx, fl
       r.cb = fast_exp2(m2 - r.m_new);
     }
     r.l_new = r.ca * lp + r.cb * l;
+    r.l_norm = r.l_new;
   }
   return r;
 }
@@ -79,7 +81,7 @@ __device__ __forceinline__ void store_dims4(const StepArgs& A, int64_t idx, int 
     oo[3] += rm.ca * op.w;
   }
   if (fin) {
-    const float inv = rm.l_new > 0.f ? 1.f / rm.l_new : 0.f;
+    const float inv = rm.l_norm > 0.f ? 1.f / rm.l_norm : 0.f;
     OutT* out = reinterpret_cast<OutT*>(A.out) + idx * D + dim;
     if constexpr (sizeof(OutT) == 2) {
       bf16x2 p0, p1;
@@ -109,13 +111,28 @@ __device__ __forceinline__ void store_row(const StepArgs& A, int64_t idx, bool f
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel.
 //
-// Workgroup: 4 waves, BM = 128 query rows (32 per wave, one MFMA column
-// block), two workgroups per CU (two waves per SIMD, so one wave's softmax
-// overlaps the other's MFMAs).  Key/value tiles of BN = 64 rows go straight
-// from HBM into LDS with buffer_load_dwordx4 ... lds (each wave instruction
-// fills 1 KiB of LDS, lane l at byte 16 l; the buffer descriptor's bound
-// turns rows past the block into zeros), double-buffered: tile j + 1 is in
-// flight while tile j computes, one barrier per tile.
+// Workgroup: 8 waves, BM = 256 query rows (32 per wave), one workgroup per
+// CU.  The waves form two groups of four: group 0 owns rows 0..127 of the
+// tile, group 1 rows 128..255.  Waves w and w + 4 run on the same SIMD, so
+// every SIMD holds one wave of each group.  The work of one key tile is cut
+// into two phases:
+//   MFMA phase M(j):    S(j) = K(j) Q^T and O += V(j-1)^T P(j-1)  (matrix pipe)
+//   softmax phase X(j): mask, row max, lazy rescale, P(j) = exp2(S c - m),
+//                       row sums, bf16 packing                     (VALU)
+// Group 1 runs one phase behind group 0 and every phase ends at a workgroup
+// barrier, so on each SIMD one wave's MFMAs overlap the other wave's
+// exponentials instead of waiting for them.
+//
+// Key/value tiles of BN = 64 rows go straight from HBM into LDS with
+// buffer_load_dwordx4 ... lds (each wave instruction fills 1 KiB of LDS,
+// lane l at byte 16 l; the buffer descriptor's bound turns rows past the
+// block into zeros).  Three buffers per tensor, tile t in buffer t % 3.
+// Group 1 issues every tile load: K(j+3) and V(j+2) at the start of its
+// softmax phase X(j), and it waits for them at the end of X(j+1), before
+// the barrier.  Every wave's first LDS reads of M(j+1) are issued at the end
+// of X(j) and stay in flight across the barrier (the barrier does not wait
+// for LDS reads; the buffers they read are not reloaded until both groups
+// have finished M(j+1)).
 //
 // LDS rows are unpadded (D * 2 bytes); 16-byte chunks are XOR-swizzled so
 // that every read phase covers all 64 LDS banks (ds_read_b128 is served 16
@@ -132,21 +149,21 @@ __device__ __forceinline__ void store_row(const StepArgs& A, int64_t idx, bool f
 // and dims 16 ((s/16)%2) + 4 (s%4) hands every lane 4 consecutive keys of its
 // own dim, in the key order the S^T registers already hold.
 // ---------------------------------------------------------------------------
-constexpr int kWaves = 4;                 // waves per workgroup (32 query rows each)
+constexpr int kWaves = 8;                 // two groups of four waves, 32 query rows each
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;
+constexpr int kGroupRows = 128;
+constexpr int kBM = 2 * kGroupRows;
 constexpr int kBN = 64;
-constexpr int kWgPerCu = kWaves == 4 ? 2 : 1;
 
 template <int D>
 struct Tile {
   static constexpr int RB = D * 2;              // bytes per LDS row
   static constexpr int CPR = D / 8;             // 16-byte chunks per row
   static constexpr int BYTES = kBN * RB;        // one K (or V) tile
-  static constexpr int LDS_BYTES = 4 * BYTES;   // K double buffer, then V double buffer
-  static constexpr int VOFF = 2 * BYTES;        // start of the V buffers
   static constexpr int INSTR = BYTES / 1024;    // 1 KiB load instructions per tile per tensor
-  static constexpr int PER_WAVE = INSTR / kWaves;
+  static constexpr int PER_WAVE = INSTR / 4;    // issued by the four waves of group 1
+  static constexpr int NDB = D / 32;            // 32-dim output blocks
+  static constexpr int NSTEP = 2 * (D / 16);    // S MFMAs per tile (= PV MFMAs per tile)
 };
 
 template <int D>
@@ -159,31 +176,53 @@ __device__ __forceinline__ int vswz(int k) { return D == 128 ? 4 * (k & 3) : 4 *
 // tile's first row inside the block's buffer descriptor.
 template <int D>
 __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rsrc, unsigned char* buf,
-                                          const int (&voff)[Tile<D>::PER_WAVE], int wave_u, unsigned soff) {
+                                          const int (&voff)[Tile<D>::PER_WAVE], int wl, unsigned soff) {
 #pragma unroll
   for (int u = 0; u < Tile<D>::PER_WAVE; ++u) {
-    const int i = wave_u * Tile<D>::PER_WAVE + u;   // instruction index within the tile
+    const int i = wl * Tile<D>::PER_WAVE + u;   // instruction index within the tile
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc, (__attribute__((address_space(3))) void*)(buf + i * 1024), 16, voff[u], soff, 0, 0);
   }
 }
 
+// Workgroup barrier between phases.  It neither waits for this wave's LDS
+// reads nor lets the compiler move memory accesses or instructions across.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int D, typename OutT>
-__global__ __launch_bounds__(kThreads, kWgPerCu) void step_bf16_kernel(StepArgs A) {
+__global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
   using T = Tile<D>;
+  constexpr int NSTEP = T::NSTEP;
+  constexpr int PF = 3;                 // MFMA steps whose operands are read ahead
   const Work w = decode_work(A);
   const int lane = threadIdx.x & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int half = lane >> 5;       // which half of the wave
-  const int col = lane & 31;        // query column owned by this lane
+  const int grp = wave_u >> 2;          // 0: rows 0..127 of the tile, 1: rows 128..255
+  const int wl = wave_u & 3;
+  const int half = lane >> 5;           // which half of the wave
+  const int col = lane & 31;            // query column owned by this lane
   const int64_t row_first = (int64_t)w.qtile * kBM;
-  const int64_t row_last = (row_first + kBM < A.Lq ? row_first + kBM : A.Lq) - 1;
-  const int64_t my_row = row_first + wave_u * 32 + col;
+  const int64_t wg_last = (row_first + kBM < A.Lq ? row_first + kBM : A.Lq) - 1;
+  const int64_t g_first = row_first + grp * kGroupRows;
+  const bool grp_ok = g_first < A.Lq;
+  const int64_t g_last = grp_ok ? ((g_first + kGroupRows < A.Lq ? g_first + kGroupRows : A.Lq) - 1) : wg_last;
+  const int64_t my_row = g_first + wl * 32 + col;
   const bool row_ok = my_row < A.Lq;
-  const int64_t my_lim = key_limit(A, w, row_ok ? my_row : row_last);
-  const int64_t kv_end = key_limit(A, w, row_last) + 1;
-  const int64_t full_end = key_limit(A, w, row_first) + 1;
+  const int64_t my_lim = key_limit(A, w, row_ok ? my_row : g_last);
+  const int64_t kv_end = key_limit(A, w, wg_last) + 1;
   const int ntiles = (int)((kv_end + kBN - 1) / kBN);
+  // Group 1 loads every tile of the workgroup, so it runs through all of
+  // them (its rows see the most keys); group 0 stops after its own last
+  // visible tile.
+  const int n_own = (int)((key_limit(A, w, g_last) + 1 + kBN - 1) / kBN);
+  const int n_g = grp == 1 ? ntiles : (n_own < ntiles ? n_own : ntiles);
+  const int64_t full_end = key_limit(A, w, grp_ok ? g_first : g_last) + 1;
   const int lim32 = (int)my_lim;
 
   // Buffer descriptors covering exactly the kv block's rows of this plane:
@@ -198,16 +237,44 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void step_bf16_kernel(StepArgs 
       const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(A.v)) + plane_row * D, 0, nrec,
       0x00020000);
   const unsigned tile_bytes = (unsigned)(kBN * rstride * T::RB);
-  // Per-lane source offsets: lane l of load instruction i fills LDS slot
-  // (64 i + l) of the tile, i.e. row r = (64 i + l) / CPR, slot q = l % CPR,
-  // which holds logical chunk q ^ swizzle(r).
+  // Per-lane source offsets (group 1): lane l of load instruction i fills
+  // LDS slot (64 i + l) of the tile, i.e. row r = (64 i + l) / CPR, slot
+  // q = l % CPR, which holds logical chunk q ^ swizzle(r).
   int voff_k[T::PER_WAVE], voff_v[T::PER_WAVE];
 #pragma unroll
   for (int u = 0; u < T::PER_WAVE; ++u) {
-    const int pos = (wave_u * T::PER_WAVE + u) * 64 + lane;
+    const int pos = (wl * T::PER_WAVE + u) * 64 + lane;
     const int r = pos / T::CPR, q = pos % T::CPR;
     voff_k[u] = (int)(r * rstride * T::RB + 16 * (q ^ kswz<D>(r)));
     voff_v[u] = (int)(r * rstride * T::RB + 16 * (q ^ vswz<D>(r)));
+  }
+
+  __shared__ __align__(1024) unsigned char kb0[T::BYTES];
+  __shared__ __align__(1024) unsigned char kb1[T::BYTES];
+  __shared__ __align__(1024) unsigned char kb2[T::BYTES];
+  __shared__ __align__(1024) unsigned char vb0[T::BYTES];
+  __shared__ __align__(1024) unsigned char vb1[T::BYTES];
+  __shared__ __align__(1024) unsigned char vb2[T::BYTES];
+  // Six separate LDS objects, selected at compile time, so that reads of
+  // one buffer are never ordered behind direct-to-LDS loads into another.
+  auto kbuf = [&](auto I) -> unsigned char* {
+    constexpr int i = decltype(I)::value % 3;
+    if constexpr (i == 0) return kb0;
+    else if constexpr (i == 1) return kb1;
+    else return kb2;
+  };
+  auto vbuf = [&](auto I) -> unsigned char* {
+    constexpr int i = decltype(I)::value % 3;
+    if constexpr (i == 0) return vb0;
+    else if constexpr (i == 1) return vb1;
+    else return vb2;
+  };
+
+  // Tiles K(0), V(0), K(1) first; their loads overlap the query and state loads.
+  if (grp == 1 && ntiles > 0) {
+    issue_tile<D>(rk, kb0, voff_k, wl, 0u);
+    issue_tile<D>(rv, vb0, voff_v, wl, 0u);
+    if (ntiles > 1) issue_tile<D>(rk, kb1, voff_k, wl, tile_bytes);
   }
 
   // Resident query fragment: B operand of S^T = K Q^T (16 dims per MFMA).
@@ -234,23 +301,29 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void step_bf16_kernel(StepArgs 
   // depends on jp only.
   const int jp = (lane & 15) >> 2;
   const int ug = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  int vaddr[D / 32];
+  int vaddr[T::NDB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < T::NDB; ++db)
     vaddr[db] = (4 * half + jp) * T::RB + 16 * ((4 * db + ug) ^ vswz<D>(jp)) + 8 * (lane & 1);
 
   // Online-softmax state: resumed from the stored (m, l, o) of the earlier
   // ring steps, so the epilogue only stores.  The stored o and l are
   // relative to the stored m; l lives in half 0 (each half sums its own
   // keys and the halves are added at the end).
-  f32x16 oacc[D / 32];
-  float m_run = kNegInf, l_run = 0.f;
+  // Two row sums: l_run of the fp32 weights (for lse) and lb_run of their
+  // bf16 roundings, the weights the P V product actually applies; the
+  // output is normalized by lb, so its error depends on how much the values
+  // differ, not on their size.  A stored state keeps o scaled to o l / lb,
+  // i.e. o / l is that normalized output.
+  f32x16 oacc[T::NDB];
+  float m_run = kNegInf, l_run = 0.f, lb_run = 0.f;
   if (A.has_prev && row_ok) {
     const int64_t idx = q_row_index(A, w, my_row);
     m_run = A.m[idx] * kLog2e;
     l_run = half == 0 ? A.l[idx] : 0.f;
+    lb_run = l_run;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < T::NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float4 x = *reinterpret_cast<const float4*>(A.o + idx * D + db * 32 + 8 * g + 4 * half);
@@ -261,50 +334,101 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void step_bf16_kernel(StepArgs 
       }
   } else {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+    for (int db = 0; db < T::NDB; ++db) oacc[db] = f32x16{};
   }
   const float c = A.scale_log2;
+  wait_vmcnt0();
+  __syncthreads();  // K(0), V(0), K(1) are in LDS
 
-  // Software pipeline over key tiles: iteration j computes S(j+1) = K(j+1) Q^T
-  // on the MFMA pipe while the VALU turns S(j) into P(j), then O += V(j)^T P(j).
-  // K tiles therefore run one tile ahead of V tiles: during iteration j the
-  // loads of K(j+2) and V(j+1) are in flight, K(j+1) and V(j) are read.
-  // Four separate LDS objects, so that reads of one buffer are not ordered
-  // behind direct-to-LDS loads that target another.
-  __shared__ __align__(1024) unsigned char kbuf0[T::BYTES];
-  __shared__ __align__(1024) unsigned char kbuf1[T::BYTES];
-  __shared__ __align__(1024) unsigned char vbuf0[T::BYTES];
-  __shared__ __align__(1024) unsigned char vbuf1[T::BYTES];
+  f32x16 s[2];        // S^T of the tile between its MFMA and softmax phases
+  bf16x8 pk[2][2];    // P^T of the tile between its softmax phase and the next MFMA phase
+  bf16x8 kf[PF];      // K fragments of the first MFMA steps, read ahead
+  u32x4 vf[PF];       // V^T fragments of the first MFMA steps, read ahead
 
-  // The two key blocks' accumulator chains alternate, so consecutive MFMAs
-  // never depend on each other.
-  auto qk = [&](const unsigned char* kb_lds, f32x16 (&s)[2]) {
-    s[0] = f32x16{};
-    s[1] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const unsigned char* p = kb_lds + kaddr[ks] + kb * 32 * T::RB;
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+  // MFMA step t: S MFMA on key block t & 1, dim slice t >> 1; PV MFMA on
+  // output block db = t % NDB, key half hc = (t / NDB) % 2, key block
+  // t / (2 NDB).  Consecutive MFMAs never feed each other.
+  auto kread = [&](const unsigned char* kb, int t) -> bf16x8 {
+    return __builtin_bit_cast(bf16x8,
+                              *reinterpret_cast<const u32x4*>(kb + kaddr[t >> 1] + (t & 1) * 32 * T::RB));
+  };
+  // Contraction index k = 8*half + e of the PV MFMA maps to key
+  // 16*hc + 8*(e/4) + 4*half + e%4 of its key block (the S^T register order).
+  auto vread = [&](const unsigned char* vb, int t) -> u32x4 {
+    const int db = t % T::NDB, hc = (t / T::NDB) & 1, kbv = t / (2 * T::NDB);
+    const unsigned char* p0 = vb + vaddr[db] + (kbv * 32 + hc * 16) * T::RB;
+    const u32x2 lo = lds_read_tr(p0);
+    const u32x2 hi = lds_read_tr(p0 + 8 * T::RB);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+
+  // MFMA phase; steps 0..PF-1 use the fragments read ahead.  With the PV
+  // product it also sums the bf16 weights into lb (v_dot2_f32_bf16 of each
+  // packed pair with (1, 1), four chains), using VALU slots the matrix
+  // pipe leaves free.
+  auto mphase = [&](auto do_s_tag, auto do_pv_tag, const unsigned char* kb, const unsigned char* vb) {
+    constexpr bool DO_S = decltype(do_s_tag)::value;
+    constexpr bool DO_PV = decltype(do_pv_tag)::value;
+    constexpr int NPAIR = 16;                        // packed pairs of P per tile
+    constexpr int PAIRS_PER_STEP = NPAIR / NSTEP;    // 1 (d = 128) or 2 (d = 64)
+    float lbs[4] = {0.f, 0.f, 0.f, 0.f};
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+    // The wave in its MFMA phase wins instruction issue over the other
+    // group's wave on the same SIMD (otherwise the older wave would).
+    __builtin_amdgcn_s_setprio(1);
+    if constexpr (DO_S) {
+      s[0] = f32x16{};
+      s[1] = f32x16{};
+    }
+    static_for<NSTEP>([&](auto T_) __attribute__((always_inline)) {
+      constexpr int t = decltype(T_)::value;
+      if constexpr (DO_S) {
+        const bf16x8 a = kf[t % PF];
+        if constexpr (t + PF < NSTEP) kf[t % PF] = kread(kb, t + PF);
+        s[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t >> 1], s[t & 1], 0, 0, 0);
       }
+      if constexpr (DO_PV) {
+        constexpr int db = t % T::NDB, hc = (t / T::NDB) & 1, kbv = t / (2 * T::NDB);
+        const u32x4 b = vf[t % PF];
+        if constexpr (t + PF < NSTEP) vf[t % PF] = vread(vb, t + PF);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b), pk[kbv][hc],
+                                                           oacc[db], 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < PAIRS_PER_STEP; ++q) {
+          const int pr = t * PAIRS_PER_STEP + q;       // pair index: (kb, hc, element pair)
+          const bf16x2 pair = {pk[pr >> 3][(pr >> 2) & 1][2 * (pr & 3)], pk[pr >> 3][(pr >> 2) & 1][2 * (pr & 3) + 1]};
+          lbs[pr & 3] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lbs[pr & 3], false);
+          asm volatile("" : "+v"(lbs[pr & 3]));   // stays at this step (not sunk into the next phase)
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (DO_PV) {
+      lb_run += (lbs[0] + lbs[1]) + (lbs[2] + lbs[3]);
+      asm volatile("" : "+v"(lb_run));
+    }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Mask, row max and (lazy) rescale of tile jt's scores; returns the
   // reference max to subtract.
-  auto prepare = [&](f32x16 (&s)[2], int jt) -> float {
+  auto prepare = [&](int jt) -> float {
     const int tile0 = jt * kBN;
     if (tile0 + kBN > full_end) {
       // key tile0 + kb*32 + 8*(r/4) + 4*half + r%4 is visible iff its offset
       // in the tile is <= my_lim - tile0; compare the compile-time part of
       // the offset against one per-lane 32-bit bound (block rows < 2^30).
+      // (One compare into VCC and one select per element, written out so the
+      // compiler does not hold a lane mask per element in scalar registers.)
       const int bound = lim32 - tile0 - 4 * half;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (kb * 32 + 8 * (r >> 2) + (r & 3) > bound) s[kb][r] = kNegInf;
+          asm volatile("v_cmp_lt_i32 vcc, %1, %2\n\tv_cndmask_b32 %0, %0, %3, vcc"
+                       : "+v"(s[kb][r])
+                       : "v"(bound), "n"(kb * 32 + 8 * (r >> 2) + (r & 3)), "v"(kNegInf)
+                       : "vcc");
     }
     float mx = kNegInf;
 #pragma unroll
@@ -320,8 +444,9 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void step_bf16_kernel(StepArgs 
       const float m_new = fmaxf(m_run, m_tile);
       const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run - m_new);
       l_run *= alpha;
+      lb_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < T::NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       m_run = m_new;
@@ -329,10 +454,10 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void step_bf16_kernel(StepArgs 
     return m_run == kNegInf ? 0.f : m_run;
   };
 
-  // P = exp2(S c - m): the row sum takes the fp32 values, the PV product
-  // their bf16 rounding (as the page's listing: block sum from the fp32
-  // exponentials, P cast to the V dtype for P V).
-  auto softmax = [&](const f32x16 (&s)[2], float m_use, bf16x8 (&pk)[2][2]) {
+  // P = exp2(S c - m): l sums the fp32 values, the PV product takes their
+  // bf16 rounding (P cast to the V dtype, as the page's listing does); the
+  // MFMA phase that consumes them also adds them into lb.
+  auto softmax = [&](float m_use) {
     float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -345,123 +470,118 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void step_bf16_kernel(StepArgs 
           pk[kb][hc][e] = (__bf16)p;
         }
     l_run += lsum0 + lsum1;
+    asm volatile("" : "+v"(l_run));  // the sum finishes in this phase
   };
 
-  // S(j+1) = K(j+1) Q^T interleaved with P(j) = softmax(S(j)): the loop is
-  // cut into NSTEP steps (one MFMA each, K fragment read two steps ahead,
-  // 32 / NSTEP score elements of the current tile), fenced so the compiler
-  // keeps the MFMAs spread across the exponentials.
-  auto qk_softmax = [&](const unsigned char* kb_lds, f32x16 (&nxt)[2], const f32x16 (&cur)[2], float m_use,
-                        bf16x8 (&pk)[2][2]) {
-    constexpr int KS = D / 16;
-    constexpr int NSTEP = 2 * KS;            // (kb, ks) pairs
-    constexpr int EPS = 32 / NSTEP;          // score elements per step (2 or 4)
-    // step i: key block i % 2, dim slice i / 2 (the two chains alternate)
-    auto kread = [&](int i) -> bf16x8 {
-      const int kb = i & 1, ks = i >> 1;
-      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kb_lds + kaddr[ks] + kb * 32 * T::RB));
-    };
-    nxt[0] = f32x16{};
-    nxt[1] = f32x16{};
-    bf16x8 kf[3];
-    kf[0] = kread(0);
-    kf[1] = kread(1);
-    float lsum0 = 0.f, lsum1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < NSTEP; ++i) {
-      if (i + 2 < NSTEP) kf[(i + 2) % 3] = kread(i + 2);
-      const int kb = i & 1, ks = i >> 1;
-      nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[ks], nxt[kb], 0, 0, 0);
-#pragma unroll
-      for (int t = 0; t < EPS; t += 2) {
-        const int el = i * EPS + t;          // element pair (el, el + 1) of the current tile
-        const int ckb = el / 16, r = el % 16;
-        const float p0 = fast_exp2(__builtin_fmaf(cur[ckb][r], c, -m_use));
-        const float p1 = fast_exp2(__builtin_fmaf(cur[ckb][r + 1], c, -m_use));
-        lsum0 += p0;
-        lsum1 += p1;
-        pk[ckb][r >> 3][r & 7] = (__bf16)p0;
-        pk[ckb][r >> 3][(r & 7) + 1] = (__bf16)p1;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    l_run += lsum0 + lsum1;
-  };
-
-  // O^T += V^T P^T.  Contraction index k = 8*half + e maps to key
-  // 16*hc + 8*(e/4) + 4*half + e%4 of key block kb (the S^T register order).
-  auto pv = [&](const unsigned char* vb_lds, const bf16x8 (&pk)[2][2]) {
+  // Softmax phase X(j) (j % 3 == JM): group 1 first issues the loads of
+  // K(j+3) (into K(j)'s buffer, free since both groups finished M(j)) and
+  // V(j+2) (into V(j-1)'s buffer), and at the end waits for the loads it
+  // issued in X(j-1); then every wave reads ahead the first fragments of
+  // M(j+1): K(j+1) unless j + 1 is the group's last MFMA phase, and V(j).
+  auto xphase = [&](auto JM_, int j) {
+    using JM = decltype(JM_);
+    const bool ld_v = grp == 1 && j + 2 < ntiles;
+    const bool ld_k = grp == 1 && j + 3 < ntiles;
+    if (ld_v) issue_tile<D>(rv, vbuf(std::integral_constant<int, JM::value + 2>{}), voff_v, wl,
+                            (unsigned)(j + 2) * tile_bytes);
+    if (ld_k) issue_tile<D>(rk, kbuf(JM{}), voff_k, wl, (unsigned)(j + 3) * tile_bytes);
+    const float m_use = prepare(j);
+    softmax(m_use);
+    // Keep the bf16 packing in this phase (the compiler would otherwise sink
+    // it past the barrier, next to its use in the MFMA phase).
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int hc = 0; hc < 2; ++hc)
+      for (int hc = 0; hc < 2; ++hc) asm volatile("" : "+v"(pk[kb][hc]));
+    if (grp == 1) {
+      if (ld_k) wait_vmcnt<2 * T::PER_WAVE>();
+      else if (ld_v) wait_vmcnt<T::PER_WAVE>();
+      else wait_vmcnt0();
+    }
+    if (j + 1 < n_g) {
+      const unsigned char* kb = kbuf(std::integral_constant<int, JM::value + 1>{});
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const unsigned char* p0 = vb_lds + vaddr[db] + (kb * 32 + hc * 16) * T::RB;
-          const u32x2 lo = lds_read_tr(p0);
-          const u32x2 hi = lds_read_tr(p0 + 8 * T::RB);
-          const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pk[kb][hc],
-                                                             oacc[db], 0, 0, 0);
-        }
+      for (int t = 0; t < PF; ++t) kf[t] = kread(kb, t);
+    }
+    {
+      const unsigned char* vb = vbuf(JM{});
+#pragma unroll
+      for (int t = 0; t < PF; ++t) vf[t] = vread(vb, t);
+    }
+    phase_barrier();
   };
 
-  f32x16 sa[2], sb[2];
-  if (ntiles > 0) {
-    issue_tile<D>(rk, kbuf0, voff_k, wave_u, 0u);
-    issue_tile<D>(rv, vbuf0, voff_v, wave_u, 0u);
-    if (ntiles > 1) issue_tile<D>(rk, kbuf1, voff_k, wave_u, tile_bytes);
-    wait_vmcnt0();
-    __syncthreads();
-    qk(kbuf0, sa);
-    __syncthreads();  // everyone is done with K(0) before K(2) overwrites it
-  }
-
-  // One pipeline stage: tile jt with scores `cur`, producing `nxt` for jt + 1
-  // (LAST: tile jt is the final tile, nothing to produce).  K(jt+1) lives in
-  // kb_next, V(jt) in vb_cur; K(jt+2) goes to kb_free and V(jt+1) to vb_free.
-  auto stage = [&](auto last_tag, int jt, f32x16 (&cur)[2], f32x16 (&nxt)[2], const unsigned char* kb_next,
-                   unsigned char* kb_free, const unsigned char* vb_cur, unsigned char* vb_free) {
-    constexpr bool LAST = decltype(last_tag)::value;
-    if (!LAST) {
-      if (jt + 2 < ntiles) issue_tile<D>(rk, kb_free, voff_k, wave_u, (unsigned)(jt + 2) * tile_bytes);
-      issue_tile<D>(rv, vb_free, voff_v, wave_u, (unsigned)(jt + 1) * tile_bytes);
-    }
-    const float m_use = prepare(cur, jt);
-    bf16x8 pk[2][2];
-    if (!LAST) {
-      qk_softmax(kb_next, nxt, cur, m_use, pk);
-    } else {
-      softmax(cur, m_use, pk);
-    }
-    pv(vb_cur, pk);
-    wait_vmcnt0();
-    __syncthreads();
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  // M(j) for j % 3 == JM reads K(j) and V(j-1).
+  auto mboth = [&](auto JM_) {
+    using JM = decltype(JM_);
+    mphase(Yes{}, Yes{}, kbuf(JM{}), vbuf(std::integral_constant<int, JM::value + 2>{}));
+    asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+    phase_barrier();
   };
 
-  using Mid = std::integral_constant<bool, false>;
-  using Last = std::integral_constant<bool, true>;
-  // Two tiles per trip so every buffer address is a compile-time offset.
-  int jt = 0;
-  for (; jt + 2 < ntiles; jt += 2) {
-    stage(Mid{}, jt, sa, sb, kbuf1, kbuf0, vbuf0, vbuf1);
-    stage(Mid{}, jt + 1, sb, sa, kbuf0, kbuf1, vbuf1, vbuf0);
+  if (n_g > 0) {
+#pragma unroll
+    for (int t = 0; t < PF; ++t) kf[t] = kread(kb0, t);
+    if (grp == 1) {
+      // Group 1 starts one phase late; meanwhile it loads K(2) and V(1).
+      if (ntiles > 1) issue_tile<D>(rv, vb1, voff_v, wl, tile_bytes);
+      if (ntiles > 2) issue_tile<D>(rk, kb2, voff_k, wl, 2u * tile_bytes);
+      phase_barrier();
+    }
+    mphase(Yes{}, No{}, kb0, nullptr);   // M(0): S(0) only
+    phase_barrier();
+    xphase(I0{}, 0);
+    int j = 1;
+    for (; j + 2 < n_g; j += 3) {
+      mboth(I1{});
+      xphase(I1{}, j);
+      mboth(I2{});
+      xphase(I2{}, j + 1);
+      mboth(I0{});
+      xphase(I0{}, j + 2);
+    }
+    if (j < n_g) {  // j % 3 == 1
+      mboth(I1{});
+      xphase(I1{}, j);
+      ++j;
+      if (j < n_g) {
+        mboth(I2{});
+        xphase(I2{}, j);
+      }
+    }
+    // M(n_g): O += V(n_g - 1)^T P(n_g - 1) only.
+    const int jl = (n_g - 1) % 3;
+    if (jl == 0) mphase(No{}, Yes{}, nullptr, vb0);
+    else if (jl == 1) mphase(No{}, Yes{}, nullptr, vb1);
+    else mphase(No{}, Yes{}, nullptr, vb2);
+    // Group 0 matches group 1's last barrier, so group 1's final MFMA phase
+    // overlaps group 0's stores.
+    if (grp == 0) phase_barrier();
   }
-  if (jt + 1 < ntiles) {  // two tiles left: jt (buffer parity 0) and the last
-    stage(Mid{}, jt, sa, sb, kbuf1, kbuf0, vbuf0, vbuf1);
-    stage(Last{}, jt + 1, sb, sa, kbuf0, kbuf1, vbuf1, vbuf0);
-  } else if (jt < ntiles) {  // one tile left
-    stage(Last{}, jt, sa, sb, kbuf1, kbuf0, vbuf0, vbuf1);
+  // Every wave passes the same number of barriers: a group that processed
+  // n > 0 tiles passed 2 n + 1 after the first one.  Group 0 stops early
+  // when its rows see fewer tiles and waits out group 1's remaining phases.
+  if (grp == 0) {
+    const int extra = (ntiles > 0 ? 2 * ntiles + 1 : 0) - (n_g > 0 ? 2 * n_g + 1 : 0);
+    for (int b = 0; b < extra; ++b) phase_barrier();
   }
 
   // Combine the two halves' partial sums (they saw disjoint keys).
   const float l_tot = partner_sum(l_run);
+  const float lb_tot = partner_sum(lb_run);
   if (!row_ok) return;
   const bool fin = w.q_rank >= A.fin_lo && w.q_rank < A.fin_hi;
   const int64_t idx = q_row_index(A, w, my_row);
-  const RowMerge rm{0.f, 1.f, m_run, l_tot};   // the state already includes earlier steps
+  // The state already includes earlier steps: finalize with O = o / lb, or
+  // store o l / lb (so that o / l is the normalized output) with l.
+  const RowMerge rm{0.f, fin || !(lb_tot > 0.f) ? 1.f : l_tot / lb_tot, m_run, l_tot, lb_tot};
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < T::NDB; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const float o4[4] = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
@@ -559,6 +679,7 @@ __global__ __launch_bounds__(kF32BM) void step_f32_kernel(StepArgs A) {
 }  // namespace
 
 int step_block_rows_bf16(int) { return kBM; }
+
 int step_block_rows_f32(int) { return kF32BM; }
 
 static int grid_size(const StepArgs& a) {
@@ -591,13 +712,5 @@ hipError_t launch_step_f32(const StepArgs& a, int d, hipStream_t s) {
   return hipGetLastError();
 }
 
-// The bf16 kernel needs more than the default 64 KiB of dynamic LDS.
-hipError_t step_kernel_setup() {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(step_bf16_kernel<128, __bf16>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, Tile<128>::LDS_BYTES);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(step_bf16_kernel<64, __bf16>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, Tile<64>::LDS_BYTES);
-}
 
 }  // namespace ra

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs A) {
   f32x4 oacc[D / 16];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) oacc[db] = f32x4{};
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = kNegInf, l_run = 0.f, lb_run = 0.f;
   const float c = A.scale_log2;
 
   constexpr int CPR = D / 8;                       // 16-byte chunks per row
@@ -138,6 +138,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs A) {
       const float m_new = fmaxf(m_run, m_tile);
       const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
+      lb_run *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 16; ++db)
 #pragma unroll
@@ -146,16 +147,24 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs A) {
     }
     const float m_use = m_run == kNegInf ? 0.f : m_run;
     // B operand: contraction index k = 8*lg + e <-> key 16*(e/4) + 4*lg + e%4.
-    // fp32 weights for the row sum, their bf16 rounding for P V.
+    // fp32 weights for the row sum l (lse), their bf16 rounding for P V and
+    // for the sum lb that normalizes the output (the weights P V applies).
     bf16x8 pb;
-    float lsum = 0.f;
+    float lsum = 0.f, lbsum = 0.f;
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 2][e & 3], c, -m_use));
       lsum += pe;
       pb[e] = (__bf16)pe;
     }
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 pair = {pb[e], pb[e + 1]};
+      lbsum = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lbsum, false);
+    }
     l_run += lsum;
+    lb_run += lbsum;
 
     // V tile -> V^T in this wave's LDS slice.
 #pragma unroll
@@ -192,12 +201,14 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs A) {
   // l: the four lane groups hold disjoint keys of the same head.
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
+  float lb_tot = lb_run + __shfl_xor(lb_run, 16);
+  lb_tot += __shfl_xor(lb_tot, 32);
   if (lc >= A.group) return;
   const int h = hkv * A.group + lc;
   const int S_all = A.S;
   const int sidx = split * kWaves + wave;
   const int64_t pidx = ((int64_t)b * A.H + h) * S_all + sidx;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
   float* op = A.o_part + pidx * D;
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)

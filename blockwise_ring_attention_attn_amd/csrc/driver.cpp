@@ -87,7 +87,6 @@ ra_status get_ctx(DeviceCtx** out) {
       RA_HIP(hipEventCreateWithFlags(&c.copied[i], hipEventDisableTiming), "hipEventCreate");
       RA_HIP(hipEventCreateWithFlags(&c.done[i], hipEventDisableTiming), "hipEventCreate");
     }
-    RA_HIP(step_kernel_setup(), "hipFuncSetAttribute");
     c.ready = true;
   }
   *out = &c;

@@ -88,7 +88,6 @@ struct DecodeArgs {
 };
 
 // Launchers (return hipError_t of the launch).
-hipError_t step_kernel_setup();   // once per device, before the first launch
 hipError_t launch_step_bf16(const StepArgs& a, int d, hipStream_t s);
 hipError_t launch_step_f32(const StepArgs& a, int d, hipStream_t s);
 int step_block_rows_bf16(int d);  // BM of the bf16 kernel
