@@ -78,6 +78,23 @@ def tensor(seed: int, tensor_id: int, B: int, H: int, n: int, d: int, dtype: str
     return out
 
 
+def uniform_tensor(seed: int, tensor_id: int, B: int, H: int, n: int, d: int, lo: float, hi: float,
+                   dtype: str) -> np.ndarray:
+    """A [B, H, n, d] tensor of U(lo, hi) draws, in storage form like `tensor`.
+
+    Used for values of one sign and large magnitude (rows whose output is
+    far from zero)."""
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
+    out = np.empty((B, H, n, d), dtype=np.float32 if dtype == "f32" else np.uint16)
+    for b in range(B):
+        for h in range(H):
+            rng = np.random.default_rng([int(seed), int(tensor_id), int(b), int(h), 1])
+            x = rng.uniform(lo, hi, (n, d)).astype(np.float32)
+            out[b, h] = x if dtype == "f32" else bf16_bits(x)
+    return out
+
+
 def as_f32(x: np.ndarray, dtype: str) -> np.ndarray:
     """Values of a tensor made by `tensor` as float32 (exact for bf16)."""
     return x if dtype == "f32" else bf16_bits_to_f32(x)

@@ -421,3 +421,13 @@ def test_synth_slab_reproducible():
     b = synth.tensor(1, synth.TENSOR_K, 2, 3, 16, 8, "bf16", threads=4)
     np.testing.assert_array_equal(a, b)
     np.testing.assert_array_equal(a[1, 2], synth.slab_bits(1, synth.TENSOR_K, 1, 2, 16, 8))
+
+
+def test_synth_uniform_range_and_reproducible():
+    a = synth.uniform_tensor(4, synth.TENSOR_V, 2, 3, 50, 8, 2.0, 3.9, "bf16")
+    b = synth.uniform_tensor(4, synth.TENSOR_V, 2, 3, 50, 8, 2.0, 3.9, "bf16")
+    np.testing.assert_array_equal(a, b)
+    x = synth.as_f32(a, "bf16")
+    assert x.min() >= 2.0 and x.max() <= 3.9 + 2 ** -6   # bf16 rounding of values below 3.9
+    f = synth.uniform_tensor(4, synth.TENSOR_V, 2, 3, 50, 8, 2.0, 3.9, "f32")
+    np.testing.assert_array_equal(synth.bf16_bits(f), a)

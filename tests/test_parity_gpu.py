@@ -70,6 +70,31 @@ def test_bf16_causal_ragged_zigzag(N, P, d):
     _fwd_and_check(2, 1, 4, 2, N, d, P, True, "zigzag", "bf16")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+def test_bf16_large_outputs_few_keys(d, layout):
+    """Values drawn from U(2, 3.9), so every output lies in [2, 3.9], where
+    one bf16 ulp is 2^-6 and rounding the output alone costs up to 0.0078.
+    The rows with 1-8 keys (the first rows of the sequence; in the striped
+    layout the first row of every host block) leave about 0.002 for the
+    kernel's own error.  Dividing by the sum of the bf16 weights the P V
+    product applies keeps that error proportional to the spread of the
+    values; dividing by the fp32 weight sum would scale it with the values
+    (up to 2^-8 * 3.9 = 0.015)."""
+    import torch
+    B, H, Hkv, N, P = 1, 4, 2, 8 * 130, 8
+    q, k, _ = _case(11, B, H, Hkv, N, d, "bf16")
+    v = synth.uniform_tensor(11, synth.TENSOR_V, B, Hkv, N, d, 2.0, 3.9, "bf16")
+    out, lse = ra.ring_attn_fwd(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), P=P, causal=True,
+                                layout=layout)
+    torch.cuda.synchronize()
+    Ow, Lw = oracle.attention(host_vals(q, "bf16"), host_vals(k, "bf16"), host_vals(v, "bf16"),
+                              scale=1 / math.sqrt(d), causal=True)
+    assert Ow.min() >= 2.0 and Ow.max() <= 3.9
+    eo, el = assert_close(from_dev(out), from_dev(lse), Ow, Lw, "bf16", f"large outputs d={d} {layout}")
+    print(f"large outputs d={d} {layout}: max|dO|={eo:.2e} max|dlse|={el:.2e}")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_bf16_batched_gqa(causal):
     _fwd_and_check(3, 2, 8, 2, 4 * 320, 128, 4, causal, "contiguous", "bf16")
@@ -216,6 +241,21 @@ def test_decode_against_oracle(B, H, Hkv, L, d, P):
     torch.cuda.synchronize()
     Ow, Lw = oracle.decode(host_vals(q, dtype), host_vals(k, dtype), host_vals(v, dtype))
     assert_close(from_dev(out), from_dev(lse), Ow, Lw[:, :, 0], dtype, f"decode B={B} H={H}/{Hkv} L={L}")
+
+
+@pytest.mark.parametrize("L,P", [(24, 8), (200, 4), (1000, 8)])
+def test_decode_large_outputs(L, P):
+    """Decode with values from U(2, 3.9) and short caches (3 to 125 keys per
+    ring block): every output lies in [2, 3.9] (see
+    test_bf16_large_outputs_few_keys)."""
+    import torch
+    B, H, Hkv, d = 2, 8, 2, 128
+    q, k, _ = _case(13, B, H, Hkv, L, d, "bf16", Nq=1)
+    v = synth.uniform_tensor(13, synth.TENSOR_V, B, Hkv, L, d, 2.0, 3.9, "bf16")
+    out, lse = ra.ring_attn_decode(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), P=P)
+    torch.cuda.synchronize()
+    Ow, Lw = oracle.decode(host_vals(q, "bf16"), host_vals(k, "bf16"), host_vals(v, "bf16"))
+    assert_close(from_dev(out), from_dev(lse), Ow, Lw[:, :, 0], "bf16", f"decode large outputs L={L} P={P}")
 
 
 def test_decode_P1_equals_P8():
