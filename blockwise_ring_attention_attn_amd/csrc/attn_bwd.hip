@@ -158,6 +158,19 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int base) {
   return r;
 }
 
+// One LDS buffer per (use, slot): a distinct object for every slot.  The
+// compiler tracks direct-to-LDS loads per LDS object and makes a read wait
+// for every load in flight into the same object, so slots of one array
+// would make each tile's reads wait for the loads just issued for a later
+// tile.
+template <int TAG, int SLOT, int BYTES>
+__device__ __forceinline__ unsigned char* slot_buf() {
+  __shared__ __align__(1024) unsigned char b[BYTES];
+  return b;
+}
+template <int I>
+using IC = std::integral_constant<int, I>;
+
 // Resident fragment of one row of a natural-order bf16 array for MFMA B
 // operands: lane l holds dims 16 ks + 8 (l / 32) .. + 7 of its row.
 template <int D>
@@ -258,14 +271,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   constexpr int PER_WAVE = INSTR / 4;                 // per wave
   constexpr int LOADS = 2 * PER_WAVE + 2;             // vector loads per wave per tile (Q, dO, lse, delta)
   static_assert(PER_WAVE >= 1 && INSTR % 4 == 0, "tile must split over the four waves");
-  __shared__ __align__(1024) unsigned char qbuf[NSLOT][T::BYTES];
-  __shared__ __align__(1024) unsigned char obuf[NSLOT][T::BYTES];
-  // lse / delta: wave w loads rows 8 w .. 8 w + 7 with 4-byte lanes; every
-  // lane of the load owns a float of the wave's 64-float area (lanes 8..63
-  // read out of range and write zeros there)
-  __shared__ __align__(16) float lseb[NSLOT][4][64];
-  __shared__ __align__(16) float delb[NSLOT][4][64];
-  __shared__ __align__(16) int lims[NSLOT][kRows];
+  // Per slot: the Q and dO tiles; lse / delta, where wave w loads rows
+  // 8 w .. 8 w + 7 with 4-byte lanes (every lane of the load owns a float of
+  // the wave's 64-float area; lanes 8..63 read out of range and write zeros
+  // there); the causal limits of the tile's rows.
+  auto qbuf = [](auto I) { return slot_buf<0, decltype(I)::value % NSLOT, T::BYTES>(); };
+  auto obuf = [](auto I) { return slot_buf<1, decltype(I)::value % NSLOT, T::BYTES>(); };
+  auto lseb = [](auto I) { return reinterpret_cast<float(*)[64]>(slot_buf<2, decltype(I)::value % NSLOT, 1024>()); };
+  auto delb = [](auto I) { return reinterpret_cast<float(*)[64]>(slot_buf<3, decltype(I)::value % NSLOT, 1024>()); };
+  auto lims = [](auto I) { return reinterpret_cast<int*>(slot_buf<4, decltype(I)::value % NSLOT, 4 * kRows>()); };
   const LdsOffsets<D> off(lane);
   const int64_t plane_elems = G.n_tok * D;
   const unsigned rec_rows = (unsigned)(G.n_tok * T::RB);   // bytes of one (b, h) plane
@@ -276,7 +290,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   // ROWS_PER_INSTR i + l / CPR, chunk slot l % CPR holding logical chunk
   // (l % CPR) ^ dswz(row).  Rows past the block read as zeros (offset out
   // of the buffer's range).
-  auto issue = [&](int it, int slot) __attribute__((always_inline)) {
+  auto issue = [&](int it, auto slot) __attribute__((always_inline)) {
     const int h = w.hkv * group + it / nqt;
     const int row0 = (qt0 + it % nqt) * kRows;
     const int64_t qplane = (int64_t)w.b * A.H + h;
@@ -293,9 +307,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
       const int q = lane % T::CPR;
       const int i = row0 + r;
       const int voff = i < A.Lq ? lrow<LAYOUT>(w.q_rank, i, A.Lq, A.P) * T::RB + 16 * (q ^ dswz<D>(r)) : (int)rec_rows;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)(qbuf[slot] + ins * 1024),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)(qbuf(slot) + ins * 1024),
                                                16, voff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (__attribute__((address_space(3))) void*)(obuf[slot] + ins * 1024),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (__attribute__((address_space(3))) void*)(obuf(slot) + ins * 1024),
                                                16, voff, 0, 0, 0);
     }
     // lse and delta: wave w loads rows 8 w .. 8 w + 7 (lanes 0..7)
@@ -306,14 +320,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
     {
       const int i = row0 + 8 * wave + lane;
       const int voff = (lane < 8 && i < A.Lq) ? lrow<LAYOUT>(w.q_rank, i, A.Lq, A.P) * 4 : (int)rec_vec;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)(&lseb[slot][wave][0]),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)(&lseb(slot)[wave][0]),
                                                4, voff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (__attribute__((address_space(3))) void*)(&delb[slot][wave][0]),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (__attribute__((address_space(3))) void*)(&delb(slot)[wave][0]),
                                                4, voff, 0, 0, 0);
     }
     if (threadIdx.x < kRows) {
       const int i = row0 + threadIdx.x;
-      lims[slot][threadIdx.x] = i < A.Lq ? llim<LAYOUT>(A, w.q_rank, w.kv_rank, i) : -1;
+      lims(slot)[threadIdx.x] = i < A.Lq ? llim<LAYOUT>(A, w.q_rank, w.kv_rank, i) : -1;
     }
   };
 
@@ -321,15 +335,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   // register r holds query 8 (r / 4) + 4 half + r % 4 of the tile.
   f32x16 sc = f32x16{}, dpc = f32x16{};
   if (total > 0) {
-#pragma unroll
-    for (int it = 0; it < LOOK; ++it)
-      if (it < total) issue(it, it);
+    static_for<LOOK>([&](auto I) __attribute__((always_inline)) {
+      if (decltype(I)::value < total) issue(decltype(I)::value, I);
+    });
     wait_vmcnt0();
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(qbuf[0], off, ks), kf[ks], sc, 0, 0, 0);
-      dpc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(obuf[0], off, ks), vf[ks], dpc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(qbuf(IC<0>{}), off, ks), kf[ks], sc, 0, 0, 0);
+      dpc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(obuf(IC<0>{}), off, ks), vf[ks], dpc, 0, 0, 0);
     }
   }
 
@@ -343,44 +357,56 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
     constexpr int SF = (SL + LOOK) % NSLOT;                // slot of tile t+3 (free: it held t-1)
     constexpr bool MORE = decltype(more_tag)::value;       // t + 1 < total
     const bool ahead = t + LOOK < total;
-    if (ahead) issue(t + LOOK, SF);
+    if (ahead) issue(t + LOOK, IC<SF>{});
     // The causal limit is applied to every element (a row's limit is at
     // least every key of an unmasked tile, so the test is a no-op there);
     // testing per element keeps the phase free of branches.
     f32x16 sn = f32x16{}, dpn = f32x16{}, pf, dsf;
-    bf16x8 fa[2];
-    if constexpr (MORE) fa[0] = read_rowfrag<D>(qbuf[SN], off, 0);
-    float lv[4], dv[4];
-    int lm[4];
+    // Operands of phase A, read PFA steps ahead (step i: Q fragment i / 2 for
+    // even i, dO fragment i / 2 for odd i).
+    constexpr int PFA = 4;
+    auto afrag = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+      return (i & 1) ? read_rowfrag<D>(obuf(IC<SN>{}), off, i >> 1) : read_rowfrag<D>(qbuf(IC<SN>{}), off, i >> 1);
+    };
+    bf16x8 fa[PFA];
+    if constexpr (MORE) {
+#pragma unroll
+      for (int i = 0; i < PFA; ++i) fa[i] = afrag(i);
+    }
+    // Row statistics of the tile (lse2, delta, causal limit) in groups of
+    // four rows, each group read one group ahead of its use.
+    float lv[2][4], dv[2][4];
+    int lm[2][4];
+    auto rowstats = [&](int g, int k) __attribute__((always_inline)) {
+      const int q0 = 8 * g + 4 * half;   // rows q0 .. q0 + 3 (loaded by wave g)
+      const float4 l4 = *reinterpret_cast<const float4*>(&lseb(IC<SL>{})[g][4 * half]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&delb(IC<SL>{})[g][4 * half]);
+      const int4 m4 = *reinterpret_cast<const int4*>(&lims(IC<SL>{})[q0]);
+      lv[k][0] = l4.x; lv[k][1] = l4.y; lv[k][2] = l4.z; lv[k][3] = l4.w;
+      dv[k][0] = d4.x; dv[k][1] = d4.y; dv[k][2] = d4.z; dv[k][3] = d4.w;
+      lm[k][0] = m4.x; lm[k][1] = m4.y; lm[k][2] = m4.z; lm[k][3] = m4.w;
+    };
+    rowstats(0, 0);
     static_for<2 * KS>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
       if constexpr (MORE) {
-        // operand of step i + 1: dO fragment i/2 after a Q fragment, else Q fragment i/2 + 1
-        if constexpr (i + 1 < 2 * KS)
-          fa[(i + 1) & 1] = ((i + 1) & 1) ? read_rowfrag<D>(obuf[SN], off, (i + 1) >> 1)
-                                          : read_rowfrag<D>(qbuf[SN], off, (i + 1) >> 1);
+        const bf16x8 a = fa[i % PFA];
+        if constexpr (i + PFA < 2 * KS) fa[i % PFA] = afrag(i + PFA);
         if constexpr ((i & 1) == 0)
-          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0], kf[i >> 1], sn, 0, 0, 0);
+          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[i >> 1], sn, 0, 0, 0);
         else
-          dpn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1], vf[i >> 1], dpn, 0, 0, 0);
+          dpn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[i >> 1], dpn, 0, 0, 0);
       }
       // VALU: the 16 elements spread over the 2 KS steps
       static_for<16>([&](auto rc) __attribute__((always_inline)) {
         constexpr int r = decltype(rc)::value;
         if constexpr (r * 2 * KS / 16 == i) {
-          if constexpr ((r & 3) == 0) {
-            const int q0 = 8 * (r >> 2) + 4 * half;   // rows q0 .. q0 + 3 (loaded by wave r / 4)
-            const float4 l4 = *reinterpret_cast<const float4*>(&lseb[SL][r >> 2][4 * half]);
-            const float4 d4 = *reinterpret_cast<const float4*>(&delb[SL][r >> 2][4 * half]);
-            const int4 m4 = *reinterpret_cast<const int4*>(&lims[SL][q0]);
-            lv[0] = l4.x; lv[1] = l4.y; lv[2] = l4.z; lv[3] = l4.w;
-            dv[0] = d4.x; dv[1] = d4.y; dv[2] = d4.z; dv[3] = d4.w;
-            lm[0] = m4.x; lm[1] = m4.y; lm[2] = m4.z; lm[3] = m4.w;
-          }
-          float p = fast_exp2(__builtin_fmaf(sc[r], c, -lv[r & 3]));
-          p = my_key > lm[r & 3] ? 0.f : p;
+          constexpr int g = r >> 2, k = g & 1;
+          if constexpr ((r & 3) == 0 && g + 1 < 4) rowstats(g + 1, k ^ 1);
+          float p = fast_exp2(__builtin_fmaf(sc[r], c, -lv[k][r & 3]));
+          p = my_key > lm[k][r & 3] ? 0.f : p;
           pf[r] = p;
-          dsf[r] = p * (dpc[r] - dv[r & 3]);
+          dsf[r] = p * (dpc[r] - dv[k][r & 3]);
         }
       });
       __builtin_amdgcn_sched_barrier(0);
@@ -396,7 +422,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
     constexpr int NB = 4 * NDB;
     auto tfrag = [&](int j) __attribute__((always_inline)) -> bf16x8 {
       const int db = (j >> 1) % NDB, hc = (j >> 1) / NDB;
-      return (j & 1) ? read_trfrag<D>(qbuf[SL], off, db, hc) : read_trfrag<D>(obuf[SL], off, db, hc);
+      return (j & 1) ? read_trfrag<D>(qbuf(IC<SL>{}), off, db, hc) : read_trfrag<D>(obuf(IC<SL>{}), off, db, hc);
     };
     bf16x8 fb[3];
     fb[0] = tfrag(0);
@@ -415,8 +441,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
     dpc = dpn;
     // tile t+2 must have landed before the next tile reads it: only tile
     // t+3's loads (issued above) may still be in flight
+    // (and the causal limits written with ds_write are visible)
     if (ahead) wait_vmcnt<LOADS>(); else wait_vmcnt0();
-    __syncthreads();
+    wait_lgkmcnt0();
+    barrier_no_fence();
   };
 
   using Yes = std::integral_constant<bool, true>;
@@ -487,8 +515,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
   constexpr int PER_WAVE = INSTR / 4;
   constexpr int LOADS = 2 * PER_WAVE;   // vector loads per wave per tile
   static_assert(PER_WAVE >= 1 && INSTR % 4 == 0, "tile must split over the four waves");
-  __shared__ __align__(1024) unsigned char kbuf[NSLOT][T::BYTES];
-  __shared__ __align__(1024) unsigned char vbuf[NSLOT][T::BYTES];
+  auto kbuf = [](auto I) { return slot_buf<5, decltype(I)::value % NSLOT, T::BYTES>(); };
+  auto vbuf = [](auto I) { return slot_buf<6, decltype(I)::value % NSLOT, T::BYTES>(); };
   const LdsOffsets<D> off(lane);
   const int64_t kv_plane = (int64_t)w.b * A.Hkv + w.hkv;
   const unsigned rec_rows = (unsigned)(G.n_tok * T::RB);
@@ -501,7 +529,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
   // Lane l of load instruction i fills LDS slot 64 i + l of the tile: row
   // ROWS_PER_INSTR i + l / CPR, chunk slot l % CPR holding logical chunk
   // (l % CPR) ^ dswz(row); keys past the block read as zeros.
-  auto issue = [&](int t, int slot) __attribute__((always_inline)) {
+  auto issue = [&](int t, auto slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) {
       const int ins = wave * PER_WAVE + u;
@@ -509,18 +537,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
       const int q = lane % T::CPR;
       const int j = t * kRows + r;
       const int voff = j < A.Lkv ? lrow<LAYOUT>(w.kv_rank, j, A.Lkv, A.P) * T::RB + 16 * (q ^ dswz<D>(r)) : (int)rec_rows;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kbuf[slot] + ins * 1024),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kbuf(slot) + ins * 1024),
                                                16, voff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vbuf[slot] + ins * 1024),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vbuf(slot) + ins * 1024),
                                                16, voff, 0, 0, 0);
     }
   };
 
-  if (ntiles > 0) {
-#pragma unroll
-    for (int t = 0; t < LOOK; ++t)
-      if (t < ntiles) issue(t, t);
-  }
+  static_for<LOOK>([&](auto I) __attribute__((always_inline)) {
+    if (decltype(I)::value < ntiles) issue(decltype(I)::value, I);
+  });
   // tile t: S^T = K Q^T and dP^T = V dO^T ([32 keys x 32 queries], one query
   // per lane column; register r holds key 32 t + 8 (r / 4) + 4 half + r % 4),
   // dS^T, then dQ^T += K^T dS^T (contraction over the tile's keys)
@@ -531,10 +557,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
     if (t + 2 < ntiles) wait_vmcnt<2 * LOADS>();
     else if (t + 1 < ntiles) wait_vmcnt<LOADS>();
     else wait_vmcnt0();
-    __syncthreads();
-    if (t + LOOK < ntiles) issue(t + LOOK, SF);   // its slot held tile t-1, done before the barrier
-    const unsigned char* kt = kbuf[SL];
-    const unsigned char* vt = vbuf[SL];
+    barrier_no_fence();
+    if (t + LOOK < ntiles) issue(t + LOOK, IC<SF>{});   // its slot held tile t-1, done before the barrier
+    const unsigned char* kt = kbuf(IC<SL>{});
+    const unsigned char* vt = vbuf(IC<SL>{});
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {

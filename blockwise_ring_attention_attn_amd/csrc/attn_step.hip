@@ -185,16 +185,6 @@ __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rsrc, unsigned
   }
 }
 
-// Workgroup barrier between phases.  It neither waits for this wave's LDS
-// reads nor lets the compiler move memory accesses or instructions across.
-__device__ __forceinline__ void phase_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 template <int D, typename OutT>
 __global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
   using T = Tile<D>;
@@ -508,7 +498,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
 #pragma unroll
       for (int t = 0; t < PF; ++t) vf[t] = vread(vb, t);
     }
-    phase_barrier();
+    barrier_no_fence();
   };
 
   using Yes = std::integral_constant<bool, true>;
@@ -521,7 +511,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
     using JM = decltype(JM_);
     mphase(Yes{}, Yes{}, kbuf(JM{}), vbuf(std::integral_constant<int, JM::value + 2>{}));
     asm volatile("" : "+v"(s[0]), "+v"(s[1]));
-    phase_barrier();
+    barrier_no_fence();
   };
 
   if (n_g > 0) {
@@ -531,10 +521,10 @@ __global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
       // Group 1 starts one phase late; meanwhile it loads K(2) and V(1).
       if (ntiles > 1) issue_tile<D>(rv, vb1, voff_v, wl, tile_bytes);
       if (ntiles > 2) issue_tile<D>(rk, kb2, voff_k, wl, 2u * tile_bytes);
-      phase_barrier();
+      barrier_no_fence();
     }
     mphase(Yes{}, No{}, kb0, nullptr);   // M(0): S(0) only
-    phase_barrier();
+    barrier_no_fence();
     xphase(I0{}, 0);
     int j = 1;
     for (; j + 2 < n_g; j += 3) {
@@ -561,14 +551,14 @@ __global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
     else mphase(No{}, Yes{}, nullptr, vb2);
     // Group 0 matches group 1's last barrier, so group 1's final MFMA phase
     // overlaps group 0's stores.
-    if (grp == 0) phase_barrier();
+    if (grp == 0) barrier_no_fence();
   }
   // Every wave passes the same number of barriers: a group that processed
   // n > 0 tiles passed 2 n + 1 after the first one.  Group 0 stops early
   // when its rows see fewer tiles and waits out group 1's remaining phases.
   if (grp == 0) {
     const int extra = (ntiles > 0 ? 2 * ntiles + 1 : 0) - (n_g > 0 ? 2 * n_g + 1 : 0);
-    for (int b = 0; b < extra; ++b) phase_barrier();
+    for (int b = 0; b < extra; ++b) barrier_no_fence();
   }
 
   // Combine the two halves' partial sums (they saw disjoint keys).

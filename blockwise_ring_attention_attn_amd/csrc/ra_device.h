@@ -161,6 +161,25 @@ __device__ __forceinline__ void wait_vmcnt0() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  // s_waitcnt lgkmcnt(0), leaving vmcnt / expcnt unconstrained
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+}
+
+// Workgroup barrier without a memory fence.  __syncthreads() is a
+// workgroup release/acquire, which waits for every outstanding LDS write of
+// the wave, direct-to-LDS buffer loads included (vmcnt(0)), so loads issued
+// tiles ahead would be drained at every barrier.  Callers wait explicitly
+// (wait_vmcnt<N>) for the loads the other waves must see after the barrier;
+// the compiler fences keep memory accesses and instructions on their side.
+__device__ __forceinline__ void barrier_no_fence() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 
 // Compile-time loop: f(std::integral_constant<int, I>{}) for I = 0..N-1, so
 // every index inside is a constant expression.
