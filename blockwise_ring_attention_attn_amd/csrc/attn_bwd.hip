@@ -261,11 +261,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dvT[db] = dkT[db] = f32x16{};
 
-  // Four LDS slots for the streamed (Q, dO, lse, delta, limit) tiles.  Tile
+  // Five LDS slots for the streamed (Q, dO, lse, delta, limit) tiles.  Tile
   // t+3 is loaded straight into LDS (buffer_load ... lds, no registers)
-  // while tile t is consumed, so each load has two tiles of time to land;
-  // during tile t the MFMAs read tile t (dV, dK) and tile t+1 (next S, dP).
-  constexpr int NSLOT = 4, LOOK = 3;
+  // while tile t is consumed, so each load has two tiles of time to land.
+  constexpr int NSLOT = 5, LOOK = 3;
   constexpr int ROWS_PER_INSTR = 1024 / T::RB;        // tile rows per 1 KiB load instruction
   constexpr int INSTR = T::BYTES / 1024;              // per tensor per tile
   constexpr int PER_WAVE = INSTR / 4;                 // per wave
@@ -347,34 +346,51 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
     }
   }
 
-  // One tile, cut into one-MFMA steps fenced with sched_barrier:
-  //   phase A: S(t+1), dP(t+1) (16 MFMAs, when MORE) while the VALU turns
-  //            S(t), dP(t) into P(t) and dS(t), one element per step;
-  //   phase B: dV^T += dO^T P(t), dK^T += Q^T dS(t) (16 MFMAs).
-  auto body = [&](auto slot_tag, auto more_tag, int t) __attribute__((always_inline)) {
+  // One iteration per query tile t, cut into one-MFMA-pair steps fenced with
+  // sched_barrier.  Step i issues
+  //   S(t+1) (even i) or dP(t+1) (odd i): one MFMA, 2 accumulators;
+  //   dV^T += dO^T P(t-1) (even i) or dK^T += Q^T dS(t-1) (odd i): one MFMA,
+  //   2 NDB accumulators;
+  // and the VALU turns one element of S(t), dP(t) into P(t), dS(t).  The
+  // MFMA pipe therefore always has 2 + 2 NDB independent chains in flight
+  // and the exponentials hide under them.  Tile t's slot keeps (Q, dO)
+  // until the dV/dK products of iteration t+1, so five slots are needed:
+  // t-1 (transposed reads), t (row statistics), t+1 (row reads), t+2
+  // (landing), t+3 (loading).
+  f32x16 pf, dsf;
+  bf16x8 pbp[2], dsbp[2];   // packed P(t-1), dS(t-1)
+  auto body = [&](auto slot_tag, auto hasb_tag, int t) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot_tag)::value;          // t % NSLOT
-    constexpr int SN = (SL + 1) % NSLOT;                   // slot of tile t+1
-    constexpr int SF = (SL + LOOK) % NSLOT;                // slot of tile t+3 (free: it held t-1)
-    constexpr bool MORE = decltype(more_tag)::value;       // t + 1 < total
+    constexpr int SN = (SL + 1) % NSLOT;                   // tile t+1
+    constexpr int SP = (SL + NSLOT - 1) % NSLOT;           // tile t-1
+    constexpr int SF = (SL + LOOK) % NSLOT;                // tile t+3 (the slot held t-2)
+    constexpr bool HASB = decltype(hasb_tag)::value;       // t >= 1
     const bool ahead = t + LOOK < total;
     if (ahead) issue(t + LOOK, IC<SF>{});
-    // The causal limit is applied to every element (a row's limit is at
-    // least every key of an unmasked tile, so the test is a no-op there);
-    // testing per element keeps the phase free of branches.
-    f32x16 sn = f32x16{}, dpn = f32x16{}, pf, dsf;
-    // Operands of phase A, read PFA steps ahead (step i: Q fragment i / 2 for
-    // even i, dO fragment i / 2 for odd i).
-    constexpr int PFA = 4;
+    // (S(t+1), dP(t+1) are computed even for the last tile: the slot holds
+    // stale rows then and the results are not used.)
+    f32x16 sn = f32x16{}, dpn = f32x16{};
+    constexpr int NA = 2 * KS;        // S / dP MFMAs per tile
+    constexpr int NB = 4 * NDB;       // dV / dK MFMAs per tile
+    static_assert(NA == NB, "one S/dP and one dV/dK MFMA per step");
+    constexpr int PFA = 4, PFB = 3;   // steps whose operands are read ahead
     auto afrag = [&](int i) __attribute__((always_inline)) -> bf16x8 {
       return (i & 1) ? read_rowfrag<D>(obuf(IC<SN>{}), off, i >> 1) : read_rowfrag<D>(qbuf(IC<SN>{}), off, i >> 1);
     };
-    bf16x8 fa[PFA];
-    if constexpr (MORE) {
+    // dV on even steps, dK on odd ones; (db, hc) = ((j / 2) % NDB, (j / 2) / NDB)
+    auto bfrag = [&](int j) __attribute__((always_inline)) -> bf16x8 {
+      const int db = (j >> 1) % NDB, hc = (j >> 1) / NDB;
+      return (j & 1) ? read_trfrag<D>(qbuf(IC<SP>{}), off, db, hc) : read_trfrag<D>(obuf(IC<SP>{}), off, db, hc);
+    };
+    bf16x8 fa[PFA], fb[PFB];
 #pragma unroll
-      for (int i = 0; i < PFA; ++i) fa[i] = afrag(i);
+    for (int i = 0; i < PFA; ++i) fa[i] = afrag(i);
+    if constexpr (HASB) {
+#pragma unroll
+      for (int j = 0; j < PFB; ++j) fb[j] = bfrag(j);
     }
-    // Row statistics of the tile (lse2, delta, causal limit) in groups of
-    // four rows, each group read one group ahead of its use.
+    // Row statistics of tile t (lse2, delta, causal limit) in groups of four
+    // rows, each group read one group ahead of its use.
     float lv[2][4], dv[2][4];
     int lm[2][4];
     auto rowstats = [&](int g, int k) __attribute__((always_inline)) {
@@ -387,20 +403,32 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
       lm[k][0] = m4.x; lm[k][1] = m4.y; lm[k][2] = m4.z; lm[k][3] = m4.w;
     };
     rowstats(0, 0);
-    static_for<2 * KS>([&](auto ic) __attribute__((always_inline)) {
+    static_for<NA>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
-      if constexpr (MORE) {
+      {
         const bf16x8 a = fa[i % PFA];
-        if constexpr (i + PFA < 2 * KS) fa[i % PFA] = afrag(i + PFA);
+        if constexpr (i + PFA < NA) fa[i % PFA] = afrag(i + PFA);
         if constexpr ((i & 1) == 0)
           sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[i >> 1], sn, 0, 0, 0);
         else
           dpn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[i >> 1], dpn, 0, 0, 0);
       }
-      // VALU: the 16 elements spread over the 2 KS steps
+      if constexpr (HASB) {
+        constexpr int db = (i >> 1) % NDB, hc = (i >> 1) / NDB;
+        const bf16x8 b = fb[i % PFB];
+        if constexpr (i + PFB < NB) fb[i % PFB] = bfrag(i + PFB);
+        if constexpr ((i & 1) == 0)
+          dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, pbp[hc], dvT[db], 0, 0, 0);
+        else
+          dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, dsbp[hc], dkT[db], 0, 0, 0);
+      }
+      // VALU: the 16 elements of tile t spread over the NA steps.  The causal
+      // limit is applied to every element (a row's limit is at least every
+      // key of an unmasked tile, so the test is a no-op there); testing per
+      // element keeps the step free of branches.
       static_for<16>([&](auto rc) __attribute__((always_inline)) {
         constexpr int r = decltype(rc)::value;
-        if constexpr (r * 2 * KS / 16 == i) {
+        if constexpr (r * NA / 16 == i) {
           constexpr int g = r >> 2, k = g & 1;
           if constexpr ((r & 3) == 0 && g + 1 < 4) rowstats(g + 1, k ^ 1);
           float p = fast_exp2(__builtin_fmaf(sc[r], c, -lv[k][r & 3]));
@@ -411,58 +439,56 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
       });
       __builtin_amdgcn_sched_barrier(0);
     });
-    bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int hc = 0; hc < 2; ++hc) {
-      pb[hc] = pack8(pf, 8 * hc);
-      dsb[hc] = pack8(dsf, 8 * hc);
+      pbp[hc] = pack8(pf, 8 * hc);
+      dsbp[hc] = pack8(dsf, 8 * hc);
     }
-    // phase B: step j uses (db, hc) = ((j / 2) % NDB, (j / 2) / NDB), dV on
-    // even steps, dK on odd ones; fragments read two steps ahead
-    constexpr int NB = 4 * NDB;
-    auto tfrag = [&](int j) __attribute__((always_inline)) -> bf16x8 {
-      const int db = (j >> 1) % NDB, hc = (j >> 1) / NDB;
-      return (j & 1) ? read_trfrag<D>(qbuf(IC<SL>{}), off, db, hc) : read_trfrag<D>(obuf(IC<SL>{}), off, db, hc);
-    };
-    bf16x8 fb[3];
-    fb[0] = tfrag(0);
-    fb[1] = tfrag(1);
-    static_for<NB>([&](auto jc) __attribute__((always_inline)) {
-      constexpr int j = decltype(jc)::value;
-      constexpr int db = (j >> 1) % NDB, hc = (j >> 1) / NDB;
-      if constexpr (j + 2 < NB) fb[(j + 2) % 3] = tfrag(j + 2);
-      if constexpr ((j & 1) == 0)
-        dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j % 3], pb[hc], dvT[db], 0, 0, 0);
-      else
-        dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j % 3], dsb[hc], dkT[db], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    });
     sc = sn;
     dpc = dpn;
-    // tile t+2 must have landed before the next tile reads it: only tile
-    // t+3's loads (issued above) may still be in flight
-    // (and the causal limits written with ds_write are visible)
+    // tile t+2 must have landed before the next iteration reads it: only
+    // tile t+3's loads (issued above) may still be in flight (and the causal
+    // limits written with ds_write are visible)
     if (ahead) wait_vmcnt<LOADS>(); else wait_vmcnt0();
     wait_lgkmcnt0();
     barrier_no_fence();
   };
+  // The dV / dK products of the last tile, alone.
+  auto drain = [&](auto slot_tag) __attribute__((always_inline)) {
+    constexpr int SP = decltype(slot_tag)::value;
+    constexpr int NB = 4 * NDB;
+    static_for<NB>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int db = (j >> 1) % NDB, hc = (j >> 1) / NDB;
+      if constexpr ((j & 1) == 0)
+        dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_trfrag<D>(obuf(IC<SP>{}), off, db, hc), pbp[hc],
+                                                          dvT[db], 0, 0, 0);
+      else
+        dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_trfrag<D>(qbuf(IC<SP>{}), off, db, hc), dsbp[hc],
+                                                          dkT[db], 0, 0, 0);
+    });
+  };
 
   using Yes = std::integral_constant<bool, true>;
   using No = std::integral_constant<bool, false>;
-  auto slot = [](auto n) { return std::integral_constant<int, decltype(n)::value>{}; };
-  int t = 0;
-  for (; t + NSLOT < total; t += NSLOT) {
-    static_for<NSLOT>([&](auto k) __attribute__((always_inline)) { body(slot(k), Yes{}, t + decltype(k)::value); });
-  }
-  // 1..NSLOT tiles left (t % NSLOT == 0): all but the last have a successor
-  const int left = total - t;
-  static_for<NSLOT>([&](auto k) __attribute__((always_inline)) {
-    constexpr int kk = decltype(k)::value;
-    if (kk < left) {
-      if (kk + 1 < left) body(slot(k), Yes{}, t + kk);
-      else body(slot(k), No{}, t + kk);
+  if (total > 0) {
+    body(IC<0>{}, No{}, 0);
+    int t = 1;
+    for (; t + NSLOT - 1 < total; t += NSLOT)   // t % NSLOT == 1
+      static_for<NSLOT>([&](auto k) __attribute__((always_inline)) {
+        body(IC<(decltype(k)::value + 1) % NSLOT>{}, Yes{}, t + decltype(k)::value);
+      });
+    static_for<NSLOT - 1>([&](auto k) __attribute__((always_inline)) {
+      if (t + decltype(k)::value < total) body(IC<(decltype(k)::value + 1) % NSLOT>{}, Yes{}, t + decltype(k)::value);
+    });
+    switch ((total - 1) % NSLOT) {
+      case 0: drain(IC<0>{}); break;
+      case 1: drain(IC<1>{}); break;
+      case 2: drain(IC<2>{}); break;
+      case 3: drain(IC<3>{}); break;
+      default: drain(IC<4>{}); break;
     }
-  });
+  }
   if (!key_ok || total == 0) return;
   float* dk_row = G.dk_acc + key_row * D;
   float* dv_row = G.dv_acc + key_row * D;
