@@ -114,8 +114,11 @@ hipEvent_t prof_event() {
     g_prof.pool.pop_back();
     return e;
   }
+  // Timing-only events: no system-scope fence when they complete (nothing
+  // synchronizes with them except the elapsed-time query after a device
+  // synchronization), so recording them around a kernel costs little.
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
