@@ -13,4 +13,4 @@ from .attention import (  # noqa: F401
     step_partial,
     pair_counts,
 )
-from .backward import attention_bwd  # noqa: F401
+from .backward import attention_bwd, attention_bwd_sampled  # noqa: F401

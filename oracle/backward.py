@@ -94,3 +94,75 @@ def attention_bwd(q, k, v, dout, *, scale=None, causal=False, q_pos=None, k_pos=
     if parts:
         return dq, dk, dv, saved
     return dq, dk, dv
+
+
+def attention_bwd_sampled(q, k, v, dout, *, b, h, rows, keys, scale=None, causal=False, chunk=1024):
+    """Gradients of one (batch b, query head h) at sampled positions, fp64.
+
+    Returns (dq_rows, dk_keys, dv_keys, parts): dq of the sampled query rows,
+    and this head's contribution to dk, dv of the sampled key rows of its kv
+    head g = h * Hkv // H (with grouped heads the full dk, dv of kv head g sum
+    the contributions of its H / Hkv query heads; with H == Hkv this is the
+    whole gradient).  Positions are the row indices (natural token order).
+
+    The formulas are those of `attention_bwd`, evaluated without the full
+    [N, N] matrices: a first pass over chunks of query rows forms each row's
+    lse, O and delta = dO . O (and the sampled rows' P, dS); a second pass
+    forms the sampled keys' columns of P and dS from the stored lse and delta.
+    `parts` holds, for error bounds: P and dS of the sampled rows (all keys),
+    P and dS of the sampled keys' columns (all rows), delta, O of all rows, and
+    od_i = sum_c |dO_ic| (|O_ic| + sum_j P_ij |v_jc|).
+    """
+    B, H, N, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if H % Hkv:
+        raise ValueError("H must be a multiple of Hkv")
+    if Nk != N:
+        raise ValueError("the sampled form takes self-attention shapes (Nk == Nq)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    g = h // (H // Hkv)
+    Q = np.asarray(q[b, h], dtype=np.float64)
+    K = np.asarray(k[b, g], dtype=np.float64)
+    V = np.asarray(v[b, g], dtype=np.float64)
+    dO = np.asarray(dout[b, h], dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    absV = np.abs(V)
+    lse = np.empty(N)
+    delta = np.empty(N)
+    od = np.empty(N)
+    O = np.empty((N, V.shape[1]))
+    P_rows = np.zeros((len(rows), N))
+    dS_rows = np.zeros((len(rows), N))
+    for r0 in range(0, N, chunk):
+        r1 = min(N, r0 + chunk)
+        nk = r1 if causal else N                      # keys any row of the chunk can see
+        S = (Q[r0:r1] @ K[:nk].T) * float(scale)
+        if causal:
+            S = np.where(np.arange(nk)[None, :] <= np.arange(r0, r1)[:, None], S, -np.inf)
+        m = S.max(axis=1)
+        Pc = np.exp(S - m[:, None])
+        lc = Pc.sum(axis=1)
+        Pc /= lc[:, None]
+        lse[r0:r1] = m + np.log(lc)
+        O[r0:r1] = Pc @ V[:nk]
+        delta[r0:r1] = (dO[r0:r1] * O[r0:r1]).sum(axis=1)
+        od[r0:r1] = (np.abs(dO[r0:r1]) * (np.abs(O[r0:r1]) + Pc @ absV[:nk])).sum(axis=1)
+        sel = np.nonzero((rows >= r0) & (rows < r1))[0]
+        if sel.size:
+            Pr = Pc[rows[sel] - r0]
+            dPr = dO[rows[sel]] @ V[:nk].T
+            P_rows[sel, :nk] = Pr
+            dS_rows[sel, :nk] = Pr * (dPr - delta[rows[sel]][:, None])
+    dq_rows = float(scale) * (dS_rows @ K)
+    Sk = (Q @ K[keys].T) * float(scale)                      # [N, len(keys)]
+    if causal:
+        Sk = np.where(keys[None, :] <= np.arange(N)[:, None], Sk, -np.inf)
+    P_keys = np.exp(Sk - lse[:, None])
+    dS_keys = P_keys * (dO @ V[keys].T - delta[:, None])
+    dv_keys = P_keys.T @ dO
+    dk_keys = float(scale) * (dS_keys.T @ Q)
+    parts = {"P_rows": P_rows, "dS_rows": dS_rows, "P_keys": P_keys, "dS_keys": dS_keys,
+             "delta": delta, "O": O, "od": od, "lse": lse}
+    return dq_rows, dk_keys, dv_keys, parts

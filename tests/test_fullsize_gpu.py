@@ -57,6 +57,49 @@ def test_ring_fwd_fullsize(name, seed, B, H, Hkv, N, d, P, layout, nh):
     _log(f"{name}: max|dO|={eo:.2e} max|dlse|={el:.2e}")
 
 
+def test_bwd_fullsize_sampled():
+    """Backward of the prefill workload exactly as bench.py times it (same
+    seeded inputs: B=1 H=32 N=32768 d=128 causal, contiguous, P=8, bf16).
+    The oracle evaluates one head without the [N, N] matrices: dq at the
+    sampled query rows and dk, dv at the same rows taken as keys (H == Hkv,
+    so those are the whole gradients).  Each element is held to the bf16
+    arithmetic bound of test_bwd_gpu (e = 2^-8; |got - ref| <= 2 bound + 1e-6)."""
+    import torch
+    name, seed, B, H, N, d, P = "bwd", 2, 1, 32, 32768, 128, 8
+    _log(f"{name}: generating B={B} H={H} N={N} d={d} P={P} contiguous")
+    q, k, v = synth.qkv(seed, B, H, H, N, d, "bf16")
+    do = synth.tensor(seed, synth.TENSOR_DOUT, B, H, N, d, "bf16")
+    qd, kd, vd, dod = (to_dev(x, "bf16") for x in (q, k, v, do))
+    _log(f"{name}: running ring_attn_fwd and ring_attn_bwd")
+    out, lse = ra.ring_attn_fwd(qd, kd, vd, P=P, causal=True, layout="contiguous")
+    dq, dk, dv = ra.ring_attn_bwd(qd, kd, vd, out, dod, lse, P=P, causal=True, layout="contiguous")
+    torch.cuda.synchronize()
+    h = 17
+    rows = sample_rows(N, P, "contiguous", 64, seed)
+    rows_t = torch.from_numpy(rows).to(dq.device)
+    got = {nm: from_dev(t[0, h].index_select(0, rows_t)) for nm, t in (("dq", dq), ("dk", dk), ("dv", dv))}
+    del qd, kd, vd, dod, out, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    Q, K, V, dO = (host_vals(x[:, h:h + 1], "bf16") for x in (q, k, v, do))
+    _log(f"{name}: oracle on head {h}, {len(rows)} rows and keys")
+    scale = 1 / math.sqrt(d)
+    dq_r, dk_r, dv_r, pt = oracle.attention_bwd_sampled(Q, K, V, dO, b=0, h=0, rows=rows, keys=rows, scale=scale,
+                                                         causal=True)
+    e = 2.0 ** -8
+    aQ, aK, adO = np.abs(Q[0, 0].astype(np.float64)), np.abs(K[0, 0].astype(np.float64)), np.abs(dO[0, 0].astype(np.float64))
+    w_rows = e * np.abs(pt["dS_rows"]) + pt["P_rows"] * (e * pt["od"][rows])[:, None]
+    w_keys = e * np.abs(pt["dS_keys"]) + pt["P_keys"] * (e * pt["od"])[:, None]
+    bounds = {"dq": scale * (w_rows @ aK) + e * np.abs(dq_r),
+              "dk": scale * (w_keys.T @ aQ) + e * np.abs(dk_r),
+              "dv": e * (pt["P_keys"].T @ adO) + e * np.abs(dv_r)}
+    for nm, ref in (("dq", dq_r), ("dk", dk_r), ("dv", dv_r)):
+        err = np.abs(got[nm] - ref)
+        ratio = float((err / (2 * bounds[nm] + 1e-6)).max())
+        rel = float(err.max() / max(np.abs(ref).max(), 1e-30))
+        _log(f"{name}: {nm} max|err|={err.max():.3e} rel={rel:.2e} worst err/bound={ratio:.3f}")
+        assert ratio <= 1.0, f"{name}: {nm} exceeds its bound (err/bound {ratio:.3f})"
+
+
 def test_share_fullsize_1M():
     """Rank 7's share of a 1,048,576-token causal ring (P=8), H=4, d=128."""
     import torch

@@ -119,3 +119,27 @@ def test_layout_invariance_through_positions():
                                    q_pos=order, k_pos=order)
         for a, b in zip(got, ref):
             np.testing.assert_allclose(a, b[:, :, order], atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("chunk", [7, 64])
+def test_sampled_gradients_equal_full(causal, chunk):
+    """The sampled form (one head, chunked, no [N, N] matrix) gives the same
+    rows of dq and the same key rows of dk, dv as the full evaluation, for a
+    head whose kv head has one query head (H == Hkv)."""
+    rng = np.random.default_rng([37, int(causal), chunk])
+    B, H, N, d = 2, 3, 130, 8
+    q, k, v, dO = (_rand(rng, B, H, N, d) for _ in range(4))
+    dq, dk, dv = oracle.attention_bwd(q, k, v, dO, causal=causal, scale=0.4)
+    rows = np.array([0, 1, 63, 64, 129])
+    keys = np.array([0, 5, 127, 129])
+    for (b, h) in ((0, 0), (1, 2)):
+        dqr, dkk, dvk, parts = oracle.attention_bwd_sampled(q, k, v, dO, b=b, h=h, rows=rows, keys=keys,
+                                                             scale=0.4, causal=causal, chunk=chunk)
+        np.testing.assert_allclose(dqr, dq[b, h, rows], atol=1e-12)
+        np.testing.assert_allclose(dkk, dk[b, h, keys], atol=1e-12)
+        np.testing.assert_allclose(dvk, dv[b, h, keys], atol=1e-12)
+        O, lse = oracle.attention(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], scale=0.4,
+                                  causal=causal)
+        np.testing.assert_allclose(parts["O"], O[0, 0], atol=1e-12)
+        np.testing.assert_allclose(parts["lse"], lse[0, 0], atol=1e-12)
