@@ -183,18 +183,32 @@ __device__ __forceinline__ void load_row_frags(bf16x8 (&f)[D / 16], const unsign
   }
 }
 
-// Add a [32 x 32] accumulator block (rows = dims 32 db + 8 (r / 4) + 4 half +
-// r % 4, column = this lane's row) times `mul` into an fp32 row of D floats.
-__device__ __forceinline__ void add_block(float* dst_row, const f32x16& acc, int db, int half, float mul) {
+// Emit a [32 x 32] accumulator block (rows = dims 32 db + 8 (r / 4) + 4 half
+// + r % 4, column = this lane's row) times `mul` into an fp32 row of D
+// floats: added to the row, or written over it on the first launch; on the
+// last launch that touches the row the sum is rounded to bf16 and written to
+// the output row instead.
+__device__ __forceinline__ void emit_block(float* acc_row, __bf16* out_row, const f32x16& acc, int db, int half,
+                                           float mul, bool first, bool fin) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    float4* p = reinterpret_cast<float4*>(dst_row + 32 * db + 8 * g + 4 * half);
-    float4 x = *p;
+    const int c = 32 * db + 8 * g + 4 * half;
+    float4 x = first ? make_float4(0.f, 0.f, 0.f, 0.f) : *reinterpret_cast<const float4*>(acc_row + c);
     x.x += mul * acc[4 * g];
     x.y += mul * acc[4 * g + 1];
     x.z += mul * acc[4 * g + 2];
     x.w += mul * acc[4 * g + 3];
-    *p = x;
+    if (fin) {
+      bf16x2 lo, hi;
+      lo[0] = (__bf16)x.x; lo[1] = (__bf16)x.y;
+      hi[0] = (__bf16)x.z; hi[1] = (__bf16)x.w;
+      u32x2 pk;
+      pk[0] = __builtin_bit_cast(unsigned, lo);
+      pk[1] = __builtin_bit_cast(unsigned, hi);
+      *reinterpret_cast<u32x2*>(out_row + c) = pk;
+    } else {
+      *reinterpret_cast<float4*>(acc_row + c) = x;
+    }
   }
 }
 
@@ -489,13 +503,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
       default: drain(IC<4>{}); break;
     }
   }
-  if (!key_ok || total == 0) return;
+  // (A key tile no query sees still writes its zeros on the first launch
+  // and its final values on the last.)
+  const bool first = G.first != 0;
+  const bool fin = ((G.kv_fin >> w.kv_rank) & 1ull) != 0;
+  if (!key_ok || (total == 0 && !first && !fin)) return;
   float* dk_row = G.dk_acc + key_row * D;
   float* dv_row = G.dv_acc + key_row * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
-    add_block(dk_row, dkT[db], db, half, G.scale);
-    add_block(dv_row, dvT[db], db, half, 1.f);
+    emit_block(dk_row, G.dk_out + key_row * D, dkT[db], db, half, G.scale, first, fin);
+    emit_block(dv_row, G.dv_out + key_row * D, dvT[db], db, half, 1.f, first, fin);
   }
 }
 
@@ -618,10 +636,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
   static_for<NSLOT - 1>([&](auto k) __attribute__((always_inline)) {
     if (t + decltype(k)::value < ntiles) body(std::integral_constant<int, decltype(k)::value>{}, t + decltype(k)::value);
   });
-  if (!row_ok || ntiles == 0) return;
+  const bool first = G.first != 0;
+  const bool fin = ((G.q_fin >> w.q_rank) & 1ull) != 0;
+  if (!row_ok || (ntiles == 0 && !first && !fin)) return;
   float* dq_row = G.dq_acc + qrow * D;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) add_block(dq_row, dqT[db], db, half, G.scale);
+  for (int db = 0; db < NDB; ++db) emit_block(dq_row, G.dq_out + qrow * D, dqT[db], db, half, G.scale, first, fin);
 }
 
 // delta_i = sum_c dO_ic O_ic (one wavefront per row, bf16 inputs) and the
@@ -643,20 +663,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* out, const 
   }
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
-}
-
-__global__ __launch_bounds__(256) void to_bf16_kernel(const float* src, __bf16* dst, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    dst[i] = (__bf16)src[i];
-}
-
-unsigned elementwise_grid(int64_t n) {
-  int64_t g = (n + 255) / 256;
-  return (unsigned)(g < 8192 ? (g < 1 ? 1 : g) : 8192);
-}
-
 }  // namespace
 
 int bwd_dq_rows() { return kDqRows; }
@@ -668,19 +674,6 @@ hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, 
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
                      reinterpret_cast<const __bf16*>(out), reinterpret_cast<const __bf16*>(dout), lse, delta, lse2,
                      rows, d);
-  return hipGetLastError();
-}
-
-hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(elementwise_grid(n)), dim3(256), 0, s, p, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_to_bf16(const float* src, void* dst, int64_t n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(to_bf16_kernel, dim3(elementwise_grid(n)), dim3(256), 0, s, src,
-                     reinterpret_cast<__bf16*>(dst), n);
   return hipGetLastError();
 }
 

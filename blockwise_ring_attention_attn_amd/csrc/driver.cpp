@@ -697,33 +697,46 @@ ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void*
   a.scale = scale;
   a.n_kvtiles = (int)nkt;
 
-  const int64_t nq = (int64_t)B * H * N * d, nkv = (int64_t)B * Hkv * N * d;
-  RA_HIP(launch_fill_zero(a.dq_acc, nq, cs), "fill launch");
-  RA_HIP(launch_fill_zero(a.dk_acc, nkv, cs), "fill launch");
-  RA_HIP(launch_fill_zero(a.dv_acc, nkv, cs), "fill launch");
+  a.dq_out = static_cast<__bf16*>(dq);
+  a.dk_out = static_cast<__bf16*>(dk);
+  a.dv_out = static_cast<__bf16*>(dv);
+
+  // Launch plan: step s pairs query host r with kv block (r + s) mod P; a
+  // launch covers the hosts lo .. hi that have visible work at that step.
+  // Step 0 (every host against its own block, which holds the diagonal)
+  // has work for every host, so its launch writes the accumulators instead
+  // of adding to them, and the last active step of a host (kv block) writes
+  // its dQ (dK, dV) in bf16: no separate clear or conversion pass.
+  static_assert(kMaxP <= 64, "the last-step masks hold one bit per host");
+  std::vector<int> lo_s(P, -1), hi_s(P, -1), last_q(P, -1), last_kv(P, -1);
+  for (int s = 0; s < P; ++s)
+    for (int r = 0; r < P; ++r) {
+      const int kv = (r + s) % P;
+      if (pair_active(lay, a.s.causal, P, r, kv, Bl, Bl)) {
+        if (lo_s[s] < 0) lo_s[s] = r;
+        hi_s[s] = r;
+        last_q[r] = s;
+        last_kv[kv] = s;
+      }
+    }
+  if (lo_s[0] != 0 || hi_s[0] != P - 1) return fail(RA_EUNSUPPORTED, "internal: a host has no diagonal work");
   RA_HIP(launch_bwd_prep(out, dout, lse, const_cast<float*>(a.delta), const_cast<float*>(a.lse2), (int64_t)B * H * N,
                          d, cs),
          "prep launch");
   for (int s = 0; s < P; ++s) {
-    // hosts with visible work against kv block (r + s) mod P
-    int lo = -1, hi = -1;
-    for (int r = 0; r < P; ++r) {
-      const int kv = (r + s) % P;
-      if (pair_active(lay, a.s.causal, P, r, kv, Bl, Bl)) {
-        if (lo < 0) lo = r;
-        hi = r;
-      }
-    }
-    if (lo < 0) continue;
-    a.s.host_lo = lo;
-    a.s.n_hosts = hi - lo + 1;
+    if (lo_s[s] < 0) continue;
+    a.s.host_lo = lo_s[s];
+    a.s.n_hosts = hi_s[s] - lo_s[s] + 1;
     a.s.kv_shift = -s;
+    a.first = s == 0;
+    a.q_fin = a.kv_fin = 0;
+    for (int r = 0; r < P; ++r) {
+      if (last_q[r] == s) a.q_fin |= 1ull << r;
+      if (last_kv[r] == s) a.kv_fin |= 1ull << r;
+    }
     RA_HIP(launch_bwd_dkdv(a, d, cs), "dK/dV kernel launch");
     RA_HIP(launch_bwd_dq(a, d, cs), "dQ kernel launch");
   }
-  RA_HIP(launch_to_bf16(a.dq_acc, dq, nq, cs), "convert launch");
-  RA_HIP(launch_to_bf16(a.dk_acc, dk, nkv, cs), "convert launch");
-  RA_HIP(launch_to_bf16(a.dv_acc, dv, nkv, cs), "convert launch");
   return RA_OK;
 }
 

@@ -60,6 +60,16 @@ struct BwdArgs {
   int64_t n_tok;          // N (rows per plane of every natural-order array)
   float scale;
   int n_kvtiles;          // ceil(Lkv / rows per dK/dV workgroup)
+  // Accumulation: on the first launch (first != 0) the kernels write their
+  // rows of the fp32 accumulators instead of adding to them; on the last
+  // launch that touches a query host's rows (bit q_rank of q_fin) or a kv
+  // block's rows (bit kv_rank of kv_fin) they write the final bf16 value to
+  // dq_out / dk_out / dv_out instead.
+  __bf16* dq_out;
+  __bf16* dk_out;
+  __bf16* dv_out;
+  int first;
+  unsigned long long q_fin, kv_fin;
 };
 
 struct MergeArgs {
@@ -98,14 +108,12 @@ hipError_t launch_decode_partial(const DecodeArgs& a, int d, int bf16, hipStream
 hipError_t launch_decode_merge(const DecodeArgs& a, int d, int bf16, hipStream_t s);
 hipError_t launch_spin(int microseconds, hipStream_t s);  // bounded busy wait (test hook)
 
-// Backward (bf16): delta = rowsum(dO * O); zero fill; dK/dV and dQ step
-// kernels; fp32 accumulator -> bf16 conversion.
+// Backward (bf16): delta = rowsum(dO * O); dK/dV and dQ step kernels (the
+// first step writes the fp32 accumulators, a row's last step its bf16 result).
 int bwd_dq_rows();     // query rows per dQ workgroup
 int bwd_dkdv_rows();   // keys per dK/dV workgroup
 hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, float* delta, float* lse2,
                            int64_t rows, int d, hipStream_t s);
-hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
-hipError_t launch_to_bf16(const float* src, void* dst, int64_t n, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, int d, hipStream_t s);
 
