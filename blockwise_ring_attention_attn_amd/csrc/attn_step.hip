@@ -18,9 +18,11 @@
 // stores the fp32 state or finalizes (O / l, lse = m + ln l; [TKG] §3
 // O_final).  The kernel uses the form P = exp(S - m_new) (the page's beta
 // factor folded into P), base-2 exponentials with log2(e) folded into the
-// scale, and keeps m stale while the new tile max stays within 2^8 of it
-// (skipping the alpha rescale; l and O stay relative to the same m, so the
-// result is unchanged).
+// scale, and keeps m stale while no score of a new tile exceeds it by more
+// than 16 (base 2): the bf16 kernel first exponentiates a tile against the
+// current m and takes the row max (and the alpha rescale) only when the
+// weights come out too large (the fp32 kernel keeps the exact running
+// max).  l and O stay relative to the same m, so the result is unchanged.
 //
 // bf16 path: S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16.
 // With K as the A operand every lane ends up owning one query column of
@@ -400,9 +402,8 @@ __global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // Mask, row max and (lazy) rescale of tile jt's scores; returns the
-  // reference max to subtract.
-  auto prepare = [&](int jt) -> float {
+  // Causal mask of tile jt's scores (only past the all-visible prefix).
+  auto mask_tile = [&](int jt) __attribute__((always_inline)) {
     const int tile0 = jt * kBN;
     if (tile0 + kBN > full_end) {
       // key tile0 + kb*32 + 8*(r/4) + 4*half + r%4 is visible iff its offset
@@ -420,34 +421,33 @@ __global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
                        : "v"(bound), "n"(kb * 32 + 8 * (r >> 2) + (r & 3)), "v"(kNegInf)
                        : "vcc");
     }
+  };
+
+  // Row max of the tile's scores; the reference max moves up to it (if
+  // higher), rescaling l, lb and O.  Returns the reference to subtract.
+  auto refresh_max = [&]() __attribute__((always_inline)) -> float {
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = partner_max(mx);
-    const float m_tile = mx * c;
-    // Lazily refreshed reference max: rescale only when the tile max exceeds
-    // it by more than kTau (base 2).
-    const bool need = m_tile > m_run + kTau;
-    if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run - m_new);
-      l_run *= alpha;
-      lb_run *= alpha;
+    const float m_new = fmaxf(m_run, partner_max(mx) * c);
+    const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run - m_new);
+    l_run *= alpha;
+    lb_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < T::NDB; ++db)
+    for (int db = 0; db < T::NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      m_run = m_new;
-    }
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    m_run = m_new;
     return m_run == kNegInf ? 0.f : m_run;
   };
 
-  // P = exp2(S c - m): l sums the fp32 values, the PV product takes their
-  // bf16 rounding (P cast to the V dtype, as the page's listing does); the
-  // MFMA phase that consumes them also adds them into lb.
-  auto softmax = [&](float m_use) {
+  // P = exp2(S c - m): returns this lane's sum of the fp32 values (for l);
+  // the PV product takes their bf16 rounding (P cast to the V dtype, as the
+  // page's listing does); the MFMA phase that consumes them also adds them
+  // into lb.
+  auto softmax = [&](float m_use) __attribute__((always_inline)) -> float {
     float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -459,7 +459,27 @@ __global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
           if (e & 1) lsum1 += p; else lsum0 += p;
           pk[kb][hc][e] = (__bf16)p;
         }
-    l_run += lsum0 + lsum1;
+    return lsum0 + lsum1;
+  };
+
+  // Softmax of tile jt against the current reference max, without a row
+  // max first: the exponentials are accepted when every lane's sum of its
+  // 32 weights is at most kSumCap (so that every weight is, i.e. no score
+  // exceeds the reference by more than log2 kSumCap; an overflow shows as an
+  // infinite sum).  Otherwise, and on a row's first tile (no reference yet),
+  // the wave takes the row max, refreshes the reference and redoes them.
+  // The reference is only ever moved to a true row max, and l, lb and O
+  // stay relative to it, so the result does not depend on which path ran.
+  auto tile_softmax = [&](int jt) __attribute__((always_inline)) {
+    mask_tile(jt);
+    float ls = 0.f;
+    bool slow = __builtin_amdgcn_ballot_w64(m_run == kNegInf) != 0ull;
+    if (!slow) {
+      ls = softmax(m_run);
+      slow = __builtin_amdgcn_ballot_w64(!(ls <= kSumCap)) != 0ull;
+    }
+    if (slow) ls = softmax(refresh_max());
+    l_run += ls;
     asm volatile("" : "+v"(l_run));  // the sum finishes in this phase
   };
 
@@ -475,8 +495,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
     if (ld_v) issue_tile<D>(rv, vbuf(std::integral_constant<int, JM::value + 2>{}), voff_v, wl,
                             (unsigned)(j + 2) * tile_bytes);
     if (ld_k) issue_tile<D>(rk, kbuf(JM{}), voff_k, wl, (unsigned)(j + 3) * tile_bytes);
-    const float m_use = prepare(j);
-    softmax(m_use);
+    tile_softmax(j);
     // Keep the bf16 packing in this phase (the compiler would otherwise sink
     // it past the barrier, next to its use in the MFMA phase).
 #pragma unroll

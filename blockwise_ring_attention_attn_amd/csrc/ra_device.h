@@ -25,6 +25,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;   // lazy-rescale threshold, base-2 units
+constexpr float kSumCap = 65536.0f;  // largest accepted per-lane weight sum of a tile against a stale reference max
 constexpr float kNegInf = -__builtin_huge_valf();
 
 // Global token position of row i of host `rank`'s block (blk rows):

@@ -118,7 +118,7 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
  *   o [B, H, Lq, d]   sum over keys seen so far of exp(s - m) * v
  * Initialize with m = -inf, l = 0, o = 0.  After the call (m, l, o) describe
  * the keys seen before plus this block.  The kernel may keep m below the
- * true running max (by at most 8 / log2(e) in natural units) to skip
+ * true running max (by at most 16 / log2(e) in natural units) to skip
  * rescaling; l and o are always relative to the stored m, so O = o / l and
  * lse = m + ln l are exact either way (ring_attn_finalize computes them).
  *

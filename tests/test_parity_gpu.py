@@ -95,6 +95,38 @@ def test_bf16_large_outputs_few_keys(d, layout):
     print(f"large outputs d={d} {layout}: max|dO|={eo:.2e} max|dlse|={el:.2e}")
 
 
+@pytest.mark.parametrize("rise", [60.0, -60.0])
+def test_scores_rising_or_falling_along_the_keys(rise):
+    """Scores that grow (or shrink) by about 60 natural units along the keys:
+    q_i = x_i + a u and k_j = y_j + b_j u for a unit vector u and b_j linear
+    in j.  When they grow, a row's weights against its reference max keep
+    outgrowing the accepted range, so the bf16 kernel moves its reference
+    many times in mid-row (and at tiles that are not the first); when they
+    fall, every later tile underflows against the first one's max.  Either
+    way the result must match the oracle.  (bf16 only: the fp32 kernel keeps
+    the exact running max, and with |lse| near 34 the absolute fp32 bound of
+    1e-5 is about three fp32 ulps of lse itself.)"""
+    import torch
+    dtype = "bf16"
+    B, H, Hkv, N, d, P = 1, 2, 1, 4 * 300, 128, 4
+    q, k, v = _case(13, B, H, Hkv, N, d, dtype)
+    rng = np.random.default_rng([13, 99])
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    a = 8.0
+    b = rise * math.sqrt(d) / a * (np.arange(N) / (N - 1) - 0.5)
+    qf = synth.bf16_bits((host_vals(q, dtype) + a * u).astype(np.float32))
+    kf = synth.bf16_bits((host_vals(k, dtype) + b[None, None, :, None] * u).astype(np.float32))
+    q2, k2 = to_dev(qf, dtype), to_dev(kf, dtype)
+    out, lse = ra.ring_attn_fwd(q2, k2, to_dev(v, dtype), P=P, causal=True, layout="contiguous")
+    torch.cuda.synchronize()
+    qh, kh = from_dev(q2), from_dev(k2)
+    S_span = (qh[0, 0] @ kh[0, 0].T / math.sqrt(d))
+    print(f"score range along row {N - 1}: {S_span[-1].min():.1f} .. {S_span[-1].max():.1f}")
+    Ow, Lw = oracle.attention(qh, kh, host_vals(v, dtype), scale=1 / math.sqrt(d), causal=True)
+    assert_close(from_dev(out), from_dev(lse), Ow, Lw, dtype, f"rise={rise}")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_bf16_batched_gqa(causal):
     _fwd_and_check(3, 2, 8, 2, 4 * 320, 128, 4, causal, "contiguous", "bf16")
@@ -157,7 +189,7 @@ def test_share_matches_oracle(layout, dtype):
 def test_step_state_against_oracle(layout, dtype):
     """ring_attn_step on one (q block, kv block) pair, then on a second kv
     block: lse = m + ln l and O = o / l match the oracle's partial over the
-    keys seen; m stays within 8/log2(e) below the true max."""
+    keys seen; m stays within 16/log2(e) below the true max."""
     import torch
     B, H, Hkv, N, d, P = 1, 2, 1, 4 * 200, 64, 4
     q, k, v = _case(9, B, H, Hkv, N, d, dtype)
@@ -182,14 +214,14 @@ def test_step_state_against_oracle(layout, dtype):
             lse = mh + np.log(lh)
             On = np.where(lh[..., None] > 0, oh / lh[..., None], 0.0)
         assert_close(On, lse, Ow, Lw, dtype, f"step kv={seen}")
-        # the stored m is a valid reference: never above the true max, at most 8/log2 e below
+        # the stored m is a valid reference: never above the true max, at most 16/log2 e below
         S = np.einsum("bhid,bhjd->bhij", host_vals(qb, dtype).astype(np.float64),
                       np.repeat(ks, H // Hkv, axis=1).astype(np.float64)) / math.sqrt(d)
         S = np.where(kp[None, None, None, :] <= pos[qr][None, None, :, None], S, -np.inf)
         true_max = S.max(axis=-1)
         fin = np.isfinite(true_max)
         assert np.all(mh[fin] <= true_max[fin] + 1e-4)
-        assert np.all(mh[fin] >= true_max[fin] - 8 / math.log2(math.e) - 1e-4)
+        assert np.all(mh[fin] >= true_max[fin] - 16 / math.log2(math.e) - 1e-4)
         assert np.all(np.isneginf(mh[~fin]))
 
 
