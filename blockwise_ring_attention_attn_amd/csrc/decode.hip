@@ -217,22 +217,24 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs A) {
   if (lg == 0) A.lse_part[pidx] = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
 }
 
-// Merge: one wavefront per (b, h).  Partials of each ring block are merged
-// into the block's (O, lse) and the ring blocks are then merged in order.
+// Merge: one workgroup per (b, h).  Wave w merges the partials of ring
+// blocks w, w + 4, ... into each block's (O, lse); wave 0 then merges the
+// ring blocks in order.  (The arithmetic and its order per (b, h) are those
+// of a single wave doing both in turn; the four waves only run the block
+// merges side by side.)
+constexpr int kMaxRingBlocks = 64;
 template <int D, bool kBf16>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs A) {
-  const int64_t bh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t bh = blockIdx.x;
+  const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  if (bh >= (int64_t)A.B * A.H) return;
   constexpr int PER = D / 64;  // dims per lane
+  __shared__ float blk_o[kMaxRingBlocks][D];
+  __shared__ float blk_lse[kMaxRingBlocks];
   const int per_block = A.chunks_per_block * kWaves;
   const float* lp = A.lse_part + bh * A.S;
   const float* op = A.o_part + bh * A.S * D;
-  float acc[PER];
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  float lse_run = kNegInf;
-  for (int p = 0; p < A.P; ++p) {
-    // block partial
+  for (int p = wave; p < A.P; p += kWaves) {
     float M = kNegInf;
     for (int i = 0; i < per_block; ++i) M = fmaxf(M, lp[p * per_block + i]);
     float blk[PER];
@@ -251,14 +253,24 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs A) {
       const float inv = 1.f / W;
       for (int e = 0; e < PER; ++e) blk[e] *= inv;
     }
-    // ring merge: (acc, lse_run) <- merge((acc, lse_run), (blk, lse_b))
+    for (int e = 0; e < PER; ++e) blk_o[p][lane * PER + e] = blk[e];
+    if (lane == 0) blk_lse[p] = lse_b;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float acc[PER];
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float lse_run = kNegInf;
+  for (int p = 0; p < A.P; ++p) {
+    // ring merge: (acc, lse_run) <- merge((acc, lse_run), (block p's O, lse))
+    const float lse_b = blk_lse[p];
     const float MM = fmaxf(lse_run, lse_b);
     if (MM != kNegInf) {
       float wa = __builtin_amdgcn_exp2f((lse_run - MM) * kLog2e);
       float wb = __builtin_amdgcn_exp2f((lse_b - MM) * kLog2e);
       const float tot = wa + wb;
       const float inv = 1.f / tot;
-      for (int e = 0; e < PER; ++e) acc[e] = (wa * acc[e] + wb * blk[e]) * inv;
+      for (int e = 0; e < PER; ++e) acc[e] = (wa * acc[e] + wb * blk_o[p][lane * PER + e]) * inv;
       lse_run = MM + __builtin_amdgcn_logf(tot) * kLn2;
     }
   }
@@ -282,8 +294,9 @@ hipError_t launch_decode_partial(const DecodeArgs& a, int d, int bf16, hipStream
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, int d, int bf16, hipStream_t s) {
-  const int64_t g = ((int64_t)a.B * a.H + 3) / 4;
+  const int64_t g = (int64_t)a.B * a.H;
   if (g <= 0) return hipSuccess;
+  if (a.P > kMaxRingBlocks) return hipErrorInvalidValue;
   if (d == 128) {
     if (bf16) hipLaunchKernelGGL((decode_merge_kernel<128, true>), dim3((unsigned)g), dim3(256), 0, s, a);
     else hipLaunchKernelGGL((decode_merge_kernel<128, false>), dim3((unsigned)g), dim3(256), 0, s, a);
