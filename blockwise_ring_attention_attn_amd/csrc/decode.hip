@@ -87,9 +87,10 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs A) {
   constexpr int VUNITS = (kTile / 4) * CPR;        // 4-key x 8-dim units per tile
   constexpr int VU = VUNITS / 64;
 
-  for (int64_t t0 = k_begin + (int64_t)wave * kTile; t0 < k_end; t0 += (int64_t)kWaves * kTile) {
+  // The loads of a wave's next tile are issued before the current tile's
+  // arithmetic (two register sets, the loop unrolled by two).
+  auto load_tile = [&](int64_t t0, u32x4 (&kr)[2][D / 32], u32x4 (&vr)[VU][4]) __attribute__((always_inline)) {
     // K as A operand: lane holds key t0 + 16*kg + lc, dims 32*ks + 8*lg.
-    u32x4 kr[2][D / 32];
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg) {
       const int64_t j = t0 + kg * 16 + lc;
@@ -98,7 +99,6 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs A) {
         kr[kg][ks] = j < k_end ? *reinterpret_cast<const u32x4*>(Kp + j * D + ks * 32 + lg * 8)
                                : u32x4{0u, 0u, 0u, 0u};
     }
-    u32x4 vr[VU][4];
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
       const int unit = lane + u * 64;
@@ -110,7 +110,9 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs A) {
                               : u32x4{0u, 0u, 0u, 0u};
       }
     }
+  };
 
+  auto tile = [&](int64_t t0, const u32x4 (&kr)[2][D / 32], const u32x4 (&vr)[VU][4]) __attribute__((always_inline)) {
     f32x4 s[2];
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg) {
@@ -196,6 +198,18 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs A) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  const int64_t stride = (int64_t)kWaves * kTile;
+  u32x4 krA[2][D / 32], vrA[VU][4], krB[2][D / 32], vrB[VU][4];
+  int64_t t0 = k_begin + (int64_t)wave * kTile;
+  if (t0 < k_end) load_tile(t0, krA, vrA);
+  for (; t0 < k_end; t0 += 2 * stride) {
+    if (t0 + stride < k_end) load_tile(t0 + stride, krB, vrB);
+    tile(t0, krA, vrA);
+    if (t0 + stride >= k_end) break;
+    if (t0 + 2 * stride < k_end) load_tile(t0 + 2 * stride, krA, vrA);
+    tile(t0 + stride, krB, vrB);
   }
 
   // l: the four lane groups hold disjoint keys of the same head.
