@@ -212,6 +212,24 @@ __device__ __forceinline__ void emit_block(float* acc_row, __bf16* out_row, cons
   }
 }
 
+// v_mfma_f32_32x32x16_bf16 as volatile inline asm, so that it keeps its
+// place among a step's other instructions (the builtin is a pure function
+// the optimizer moves freely, and in the dK/dV loop it gathered the MFMAs
+// at the end of the tile, after all the exponentials).  The accumulator
+// lives in VGPRs (_v) or AGPRs (_a); _z starts it from zero.  The compiler
+// does not know these are MFMAs, so a VALU read of the result must come
+// after mfma_settle (18 wait states cover the longest MFMA).
+__device__ __forceinline__ void mfma_v_z(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_a(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
 // ---------------------------------------------------------------------------
 // dK / dV: one workgroup per (query host, batch, kv head, 128-key tile).  It
 // sweeps, for every query head of the kv head's group, the 32-row query
@@ -303,7 +321,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   // ROWS_PER_INSTR i + l / CPR, chunk slot l % CPR holding logical chunk
   // (l % CPR) ^ dswz(row).  Rows past the block read as zeros (offset out
   // of the buffer's range).
-  auto issue = [&](int it, auto slot) __attribute__((always_inline)) {
+  // A tile index past the last one issues the same loads with every offset
+  // out of range (they write zeros into the slot and touch no memory), so
+  // that the loop body has no branch: the compiler would otherwise sink the
+  // MFMAs of a step into the block after it, away from the exponentials
+  // they are meant to overlap.
+  auto issue = [&](int it_in, auto slot) __attribute__((always_inline)) {
+    const bool valid = it_in < total;
+    const int it = valid ? it_in : 0;
     const int h = w.hkv * group + it / nqt;
     const int row0 = (qt0 + it % nqt) * kRows;
     const int64_t qplane = (int64_t)w.b * A.H + h;
@@ -319,7 +344,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
       const int r = ins * ROWS_PER_INSTR + lane / T::CPR;
       const int q = lane % T::CPR;
       const int i = row0 + r;
-      const int voff = i < A.Lq ? lrow<LAYOUT>(w.q_rank, i, A.Lq, A.P) * T::RB + 16 * (q ^ dswz<D>(r)) : (int)rec_rows;
+      const int voff = (valid && i < A.Lq) ? lrow<LAYOUT>(w.q_rank, i, A.Lq, A.P) * T::RB + 16 * (q ^ dswz<D>(r))
+                                           : (int)rec_rows;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)(qbuf(slot) + ins * 1024),
                                                16, voff, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (__attribute__((address_space(3))) void*)(obuf(slot) + ins * 1024),
@@ -332,7 +358,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
         const_cast<float*>(G.delta) + qplane * G.n_tok, 0, rec_vec, 0x00020000);
     {
       const int i = row0 + 8 * wave + lane;
-      const int voff = (lane < 8 && i < A.Lq) ? lrow<LAYOUT>(w.q_rank, i, A.Lq, A.P) * 4 : (int)rec_vec;
+      const int voff = (valid && lane < 8 && i < A.Lq) ? lrow<LAYOUT>(w.q_rank, i, A.Lq, A.P) * 4 : (int)rec_vec;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)(&lseb(slot)[wave][0]),
                                                4, voff, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (__attribute__((address_space(3))) void*)(&delb(slot)[wave][0]),
@@ -371,19 +397,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   // until the dV/dK products of iteration t+1, so five slots are needed:
   // t-1 (transposed reads), t (row statistics), t+1 (row reads), t+2
   // (landing), t+3 (loading).
-  f32x16 pf, dsf;
   bf16x8 pbp[2], dsbp[2];   // packed P(t-1), dS(t-1)
   auto body = [&](auto slot_tag, auto hasb_tag, int t) __attribute__((always_inline)) {
+    bf16x8 pbn[2], dsbn[2];  // packed P(t), dS(t), filled pair by pair
+    float p_prev = 0.f, ds_prev = 0.f;
     constexpr int SL = decltype(slot_tag)::value;          // t % NSLOT
     constexpr int SN = (SL + 1) % NSLOT;                   // tile t+1
     constexpr int SP = (SL + NSLOT - 1) % NSLOT;           // tile t-1
     constexpr int SF = (SL + LOOK) % NSLOT;                // tile t+3 (the slot held t-2)
     constexpr bool HASB = decltype(hasb_tag)::value;       // t >= 1
-    const bool ahead = t + LOOK < total;
-    if (ahead) issue(t + LOOK, IC<SF>{});
+    issue(t + LOOK, IC<SF>{});
     // (S(t+1), dP(t+1) are computed even for the last tile: the slot holds
     // stale rows then and the results are not used.)
-    f32x16 sn = f32x16{}, dpn = f32x16{};
+    f32x16 sn, dpn;
     constexpr int NA = 2 * KS;        // S / dP MFMAs per tile
     constexpr int NB = 4 * NDB;       // dV / dK MFMAs per tile
     static_assert(NA == NB, "one S/dP and one dV/dK MFMA per step");
@@ -422,19 +448,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
       {
         const bf16x8 a = fa[i % PFA];
         if constexpr (i + PFA < NA) fa[i % PFA] = afrag(i + PFA);
-        if constexpr ((i & 1) == 0)
-          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[i >> 1], sn, 0, 0, 0);
-        else
-          dpn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[i >> 1], dpn, 0, 0, 0);
+        if constexpr (i == 0) mfma_v_z(sn, a, kf[0]);
+        else if constexpr (i == 1) mfma_v_z(dpn, a, vf[0]);
+        else if constexpr ((i & 1) == 0) mfma_v(sn, a, kf[i >> 1]);
+        else mfma_v(dpn, a, vf[i >> 1]);
       }
       if constexpr (HASB) {
         constexpr int db = (i >> 1) % NDB, hc = (i >> 1) / NDB;
         const bf16x8 b = fb[i % PFB];
         if constexpr (i + PFB < NB) fb[i % PFB] = bfrag(i + PFB);
-        if constexpr ((i & 1) == 0)
-          dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, pbp[hc], dvT[db], 0, 0, 0);
-        else
-          dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, dsbp[hc], dkT[db], 0, 0, 0);
+        if constexpr ((i & 1) == 0) mfma_a(dvT[db], b, pbp[hc]);
+        else mfma_a(dkT[db], b, dsbp[hc]);
       }
       // VALU: the 16 elements of tile t spread over the NA steps.  The causal
       // limit is applied to every element (a row's limit is at least every
@@ -445,25 +469,37 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
         if constexpr (r * NA / 16 == i) {
           constexpr int g = r >> 2, k = g & 1;
           if constexpr ((r & 3) == 0 && g + 1 < 4) rowstats(g + 1, k ^ 1);
-          float p = fast_exp2(__builtin_fmaf(sc[r], c, -lv[k][r & 3]));
+          float x = sc[r];
+          asm volatile("" : "+v"(x));   // (keeps the element's arithmetic in this step)
+          float p = fast_exp2(__builtin_fmaf(x, c, -lv[k][r & 3]));
           p = my_key > lm[k][r & 3] ? 0.f : p;
-          pf[r] = p;
-          dsf[r] = p * (dpc[r] - dv[k][r & 3]);
+          float ds = p * (dpc[r] - dv[k][r & 3]);
+          asm volatile("" : "+v"(p), "+v"(ds));
+          if constexpr (r & 1) {
+            pbn[r >> 3][(r & 7) - 1] = (__bf16)p_prev;
+            pbn[r >> 3][r & 7] = (__bf16)p;
+            dsbn[r >> 3][(r & 7) - 1] = (__bf16)ds_prev;
+            dsbn[r >> 3][r & 7] = (__bf16)ds;
+          } else {
+            p_prev = p;
+            ds_prev = ds;
+          }
         }
       });
       __builtin_amdgcn_sched_barrier(0);
     });
+    mfma_settle();   // S(t+1), dP(t+1) are read by the VALU from here on
 #pragma unroll
     for (int hc = 0; hc < 2; ++hc) {
-      pbp[hc] = pack8(pf, 8 * hc);
-      dsbp[hc] = pack8(dsf, 8 * hc);
+      pbp[hc] = pbn[hc];
+      dsbp[hc] = dsbn[hc];
     }
     sc = sn;
     dpc = dpn;
     // tile t+2 must have landed before the next iteration reads it: only
     // tile t+3's loads (issued above) may still be in flight (and the causal
     // limits written with ds_write are visible)
-    if (ahead) wait_vmcnt<LOADS>(); else wait_vmcnt0();
+    wait_vmcnt<LOADS>();
     wait_lgkmcnt0();
     barrier_no_fence();
   };
@@ -502,6 +538,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
       case 3: drain(IC<3>{}); break;
       default: drain(IC<4>{}); break;
     }
+    wait_vmcnt0();   // the last iterations' loads past the end (zeros into free slots)
   }
   // (A key tile no query sees still writes its zeros on the first launch
   // and its final values on the last.)
