@@ -241,32 +241,36 @@ __global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
     voff_v[u] = (int)(r * rstride * T::RB + 16 * (q ^ vswz<D>(r)));
   }
 
-  __shared__ __align__(1024) unsigned char kb0[T::BYTES];
-  __shared__ __align__(1024) unsigned char kb1[T::BYTES];
-  __shared__ __align__(1024) unsigned char kb2[T::BYTES];
-  __shared__ __align__(1024) unsigned char vb0[T::BYTES];
-  __shared__ __align__(1024) unsigned char vb1[T::BYTES];
-  __shared__ __align__(1024) unsigned char vb2[T::BYTES];
+  // (The V buffers take the low LDS addresses -- the backend lays the
+  // objects out by name -- so that the transposing reads' addresses fit the
+  // 16-bit immediate offset of ds_read_b64_tr_b16 and need no address
+  // arithmetic.)
+  __shared__ __align__(1024) unsigned char av0[T::BYTES];
+  __shared__ __align__(1024) unsigned char av1[T::BYTES];
+  __shared__ __align__(1024) unsigned char av2[T::BYTES];
+  __shared__ __align__(1024) unsigned char bk0[T::BYTES];
+  __shared__ __align__(1024) unsigned char bk1[T::BYTES];
+  __shared__ __align__(1024) unsigned char bk2[T::BYTES];
   // Six separate LDS objects, selected at compile time, so that reads of
   // one buffer are never ordered behind direct-to-LDS loads into another.
   auto kbuf = [&](auto I) -> unsigned char* {
     constexpr int i = decltype(I)::value % 3;
-    if constexpr (i == 0) return kb0;
-    else if constexpr (i == 1) return kb1;
-    else return kb2;
+    if constexpr (i == 0) return bk0;
+    else if constexpr (i == 1) return bk1;
+    else return bk2;
   };
   auto vbuf = [&](auto I) -> unsigned char* {
     constexpr int i = decltype(I)::value % 3;
-    if constexpr (i == 0) return vb0;
-    else if constexpr (i == 1) return vb1;
-    else return vb2;
+    if constexpr (i == 0) return av0;
+    else if constexpr (i == 1) return av1;
+    else return av2;
   };
 
   // Tiles K(0), V(0), K(1) first; their loads overlap the query and state loads.
   if (grp == 1 && ntiles > 0) {
-    issue_tile<D>(rk, kb0, voff_k, wl, 0u);
-    issue_tile<D>(rv, vb0, voff_v, wl, 0u);
-    if (ntiles > 1) issue_tile<D>(rk, kb1, voff_k, wl, tile_bytes);
+    issue_tile<D>(rk, bk0, voff_k, wl, 0u);
+    issue_tile<D>(rv, av0, voff_v, wl, 0u);
+    if (ntiles > 1) issue_tile<D>(rk, bk1, voff_k, wl, tile_bytes);
   }
 
   // Resident query fragment: B operand of S^T = K Q^T (16 dims per MFMA).
@@ -284,9 +288,17 @@ __global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
 
   // LDS read addresses (bytes within a buffer).
   // K: row kb*32 + col, logical chunk 2 ks + half; kswz(kb*32 + col) = kswz(col).
-  int kaddr[D / 16];
+  // The K buffers sit above the V buffers, partly past the 64 KiB that the
+  // 16-bit immediate offset of ds_read_b128 reaches from a zero base, so
+  // each lane keeps its K addresses relative to the first K buffer (kept
+  // opaque, so that the buffer and key-block offsets stay immediates).
+  typedef __attribute__((address_space(3))) const unsigned char lds_u8;
+  unsigned kaddr[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) kaddr[ks] = col * T::RB + 16 * ((2 * ks + half) ^ kswz<D>(col));
+  for (int ks = 0; ks < D / 16; ++ks) {
+    kaddr[ks] = (unsigned)(size_t)(lds_u8*)bk0 + col * T::RB + 16 * ((2 * ks + half) ^ kswz<D>(col));
+    asm volatile("" : "+v"(kaddr[ks]));
+  }
   // V (transposing reads): lane s -> key 4 half + jp (+ 32 kb + 16 hc, + 8),
   // jp = (s%16)/4, and dims 32 db + 16 g + 4 (s%4), g = (s/16)%2, i.e. chunk
   // 4 db + u, u = 2 g + (s%4)/2, byte 8 (s%2) inside it; vswz of the key
@@ -341,8 +353,9 @@ __global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
   // output block db = t % NDB, key half hc = (t / NDB) % 2, key block
   // t / (2 NDB).  Consecutive MFMAs never feed each other.
   auto kread = [&](const unsigned char* kb, int t) -> bf16x8 {
-    return __builtin_bit_cast(bf16x8,
-                              *reinterpret_cast<const u32x4*>(kb + kaddr[t >> 1] + (t & 1) * 32 * T::RB));
+    typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+    const unsigned rel = (unsigned)((lds_u8*)kb - (lds_u8*)bk0) + (t & 1) * 32 * T::RB;
+    return __builtin_bit_cast(bf16x8, *(lds_u32x4*)(size_t)(kaddr[t >> 1] + rel));
   };
   // Contraction index k = 8*half + e of the PV MFMA maps to key
   // 16*hc + 8*(e/4) + 4*half + e%4 of its key block (the S^T register order).
@@ -535,14 +548,14 @@ __global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
 
   if (n_g > 0) {
 #pragma unroll
-    for (int t = 0; t < PF; ++t) kf[t] = kread(kb0, t);
+    for (int t = 0; t < PF; ++t) kf[t] = kread(bk0, t);
     if (grp == 1) {
       // Group 1 starts one phase late; meanwhile it loads K(2) and V(1).
-      if (ntiles > 1) issue_tile<D>(rv, vb1, voff_v, wl, tile_bytes);
-      if (ntiles > 2) issue_tile<D>(rk, kb2, voff_k, wl, 2u * tile_bytes);
+      if (ntiles > 1) issue_tile<D>(rv, av1, voff_v, wl, tile_bytes);
+      if (ntiles > 2) issue_tile<D>(rk, bk2, voff_k, wl, 2u * tile_bytes);
       barrier_no_fence();
     }
-    mphase(Yes{}, No{}, kb0, nullptr);   // M(0): S(0) only
+    mphase(Yes{}, No{}, bk0, nullptr);   // M(0): S(0) only
     barrier_no_fence();
     xphase(I0{}, 0);
     int j = 1;
@@ -565,9 +578,9 @@ __global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
     }
     // M(n_g): O += V(n_g - 1)^T P(n_g - 1) only.
     const int jl = (n_g - 1) % 3;
-    if (jl == 0) mphase(No{}, Yes{}, nullptr, vb0);
-    else if (jl == 1) mphase(No{}, Yes{}, nullptr, vb1);
-    else mphase(No{}, Yes{}, nullptr, vb2);
+    if (jl == 0) mphase(No{}, Yes{}, nullptr, av0);
+    else if (jl == 1) mphase(No{}, Yes{}, nullptr, av1);
+    else mphase(No{}, Yes{}, nullptr, av2);
     // Group 0 matches group 1's last barrier, so group 1's final MFMA phase
     // overlaps group 0's stores.
     if (grp == 0) barrier_no_fence();
