@@ -219,8 +219,10 @@ __device__ __forceinline__ void emit_block(float* acc_row, __bf16* out_row, cons
 // lives in VGPRs (_v) or AGPRs (_a); _z starts it from zero.  The compiler
 // does not know these are MFMAs, so a VALU read of the result must come
 // after mfma_settle (18 wait states cover the longest MFMA).
+// (The zero-start form marks its result early-clobber: an MFMA must not
+// write registers it still reads.)
 __device__ __forceinline__ void mfma_v_z(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
