@@ -17,6 +17,10 @@ resident in HBM.  Prints ONE JSON line:
                recomputation): TFLOP/s at 10 d FLOPs per unmasked pair per
                query head (the five products QK^T, dO V^T, P^T dO, dS K,
                dS^T Q)
+  striped_gqa  the striped GQA ring (bf16 H=8/Hkv=2, N=131072, P=8):
+               TFLOP/s of the whole call
+  share_1m     rank 7's share of a 1,048,576-token causal ring (bf16 H=4):
+               TFLOP/s of the whole call
 """
 from __future__ import annotations
 
@@ -37,6 +41,11 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 METRIC = "causal ring-attn fwd TFLOP/s + % bf16 MFMA peak; split-KV decode HBM GB/s"
 
 PREFILL = dict(B=1, H=32, Hkv=32, N=32768, d=128, P=8, layout="contiguous", causal=True, seed=2)
+# The two other full-size forward workloads, measured beside the headline one
+# (same kernel, other shapes): the striped GQA ring, and the last rank's share
+# of a 1,048,576-token ring (its q block against all eight kv blocks).
+STRIPED = dict(B=1, H=8, Hkv=2, N=131072, d=128, P=8, layout="striped", causal=True, seed=3)
+SHARE = dict(B=1, H=4, Hkv=4, N=1048576, d=128, P=8, rank=7, layout="contiguous", causal=True, seed=4)
 DECODE = dict(B=16, H=32, Hkv=8, L=262144, d=128, P=8, seed=5)
 
 
@@ -74,6 +83,14 @@ def calibration_copy(mib: int) -> None:
 def prefill_flops(c) -> float:
     N = c["N"]
     pairs = N * (N + 1) // 2 if c["causal"] else N * N
+    return 4.0 * c["d"] * pairs * c["B"] * c["H"]
+
+
+def share_flops(c) -> float:
+    """Rank r's query block (positions r Bl + i) against all N keys, causal."""
+    N, P, r = c["N"], c["P"], c["rank"]
+    Bl = N // P
+    pairs = r * Bl * Bl + Bl * (Bl + 1) // 2 if c["causal"] else Bl * N
     return 4.0 * c["d"] * pairs * c["B"] * c["H"]
 
 
@@ -178,6 +195,70 @@ def run_prefill(args) -> dict:
     return res
 
 
+def run_forward_other(args, c, share: bool) -> dict:
+    """Throughput of one of the other full-size forward workloads (HIP events
+    around whole calls on the caller's stream; step-kernel launches timed on
+    the compute stream as for the headline workload)."""
+    import torch
+    import blockwise_ring_attention_attn_amd as ra
+    import synth
+    B, H, Hkv, N, d, P = c["B"], c["H"], c["Hkv"], c["N"], c["d"], c["P"]
+    Nq = N // P if share else N
+    qd = upload(synth.tensor(c["seed"], synth.TENSOR_Q, B, H, Nq, d, "bf16"), "bf16")
+    kd = upload(synth.tensor(c["seed"], synth.TENSOR_K, B, Hkv, N, d, "bf16"), "bf16")
+    vd = upload(synth.tensor(c["seed"], synth.TENSOR_V, B, Hkv, N, d, "bf16"), "bf16")
+    out = torch.empty_like(qd)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda:0")
+    lib = ra.load()
+    nb = (lib.ring_attn_fwd_share_ws_bytes(B, H, Hkv, N, d, P, ra.RA_BF16) if share
+          else ra.ring_attn_fwd_ws_bytes(B, H, Hkv, N, d, P, ra.RA_BF16))
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        if share:
+            ra.ring_attn_fwd_share(qd, kd, vd, P=P, rank=c["rank"], causal=c["causal"], layout=c["layout"],
+                                   out=out, lse=lse, ws=ws, stream=stream)
+        else:
+            ra.ring_attn_fwd(qd, kd, vd, P=P, causal=c["causal"], layout=c["layout"], out=out, lse=lse, ws=ws,
+                             stream=stream)
+
+    flops = share_flops(c) if share else prefill_flops(c)
+    step()
+    torch.cuda.synchronize()
+    # about 2 s of timed calls
+    t0 = time.perf_counter()
+    step()
+    torch.cuda.synchronize()
+    n = int(min(20, max(3, 2.0 / max(time.perf_counter() - t0, 1e-3))))
+    ra.prof_enable(True)
+    ra.prof_reset()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(n):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    prof = ra.prof_read()
+    ra.prof_enable(False)
+    ms = ev0.elapsed_time(ev1) / n
+    tflops = flops / (ms * 1e-3) / 1e12
+    kern = prof["step_flops"] / (prof["step_ms"] * 1e-3) / 1e12 if prof["step_ms"] > 0 else 0.0
+    del qd, kd, vd, out, lse, ws
+    torch.cuda.empty_cache()
+    if share:
+        what = (f"rank {c['rank']} of a P={P} causal ring over N={N}: q {Nq} tokens against all {N} keys, "
+                f"bf16 H={H} d={d}")
+    else:
+        what = f"causal {c['layout']} ring: bf16 B={B} H={H}/Hkv={Hkv} N={N} d={d}, P={P} virtual hosts"
+    return {"value": tflops, "unit": "TFLOP/s", "ms_per_step": ms, "steps": n, "flops_per_step": flops,
+            "pct_bf16_mfma_peak": 100.0 * tflops / MFMA_BF16_PEAK_TFLOPS,
+            "step_kernels": {"achieved": kern, "unit": "TFLOP/s", "frac": kern / MFMA_BF16_PEAK_TFLOPS,
+                             "launches_per_step": prof["step_launches"] / n,
+                             "ms_per_step": prof["step_ms"] / n},
+            "config": {"workload": what, **c}}
+
+
 def run_backward(args) -> dict:
     import torch
     import blockwise_ring_attention_attn_amd as ra
@@ -280,7 +361,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=("prefill", "decode", "backward"), default=None,
+    ap.add_argument("--no-other-forward", action="store_true",
+                    help="skip the striped GQA and 1M-share forward workloads")
+    ap.add_argument("--only", choices=("prefill", "decode", "backward", "striped", "share"), default=None,
                     help="run one workload only (profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first do a plain device copy of this many MiB (counter calibration)")
@@ -300,6 +383,10 @@ def main():
         return
     if args.only == "backward":
         print(json.dumps(run_backward(args)), flush=True)
+        return
+    if args.only in ("striped", "share"):
+        share = args.only == "share"
+        print(json.dumps(run_forward_other(args, SHARE if share else STRIPED, share)), flush=True)
         return
     pre = run_prefill(args)
     c = PREFILL
@@ -330,6 +417,9 @@ def main():
         line["decode"] = run_decode(args)
     if not args.no_backward and args.only is None:
         line["backward"] = run_backward(args)
+    if not args.no_other_forward and args.only is None:
+        line["striped_gqa"] = run_forward_other(args, STRIPED, False)
+        line["share_1m"] = run_forward_other(args, SHARE, True)
     print(json.dumps(line), flush=True)
 
 
