@@ -104,3 +104,60 @@ def test_merge_decode_reject_invalid(lib):
 def test_python_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         ra.load(str(tmp_path / "missing.so"))
+
+
+def _share(lib, **kw):
+    a = dict(q=1, k=1, v=1, out=1, lse=1, B=1, H=2, Hkv=1, N=64, d=64, P=4, rank=3, causal=1, layout=0,
+             scale=0.125, dtype=1, stream=None, ws=256, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.ring_attn_fwd_share(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"],
+                                   a["d"], a["P"], a["rank"], a["causal"], a["layout"], a["scale"], a["dtype"],
+                                   a["stream"], a["ws"], a["ws_bytes"])
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(lse=None), "null"),
+    (dict(rank=4), "rank"),
+    (dict(rank=-1), "rank"),
+    (dict(N=66), "multiple of P"),
+    (dict(d=80), "64 or 128"),
+    (dict(ws_bytes=16), "workspace too small"),
+    (dict(ws=8), "aligned"),
+    (dict(layout=2, N=68), "multiple of 2P"),
+])
+def test_share_rejects_invalid(lib, kw, frag):
+    assert _share(lib, **kw) == ra.RA_EINVAL
+    assert frag in lib.ra_last_error().decode()
+
+
+def _bwd(lib, **kw):
+    a = dict(q=1, k=1, v=1, out=1, dout=1, lse=1, dq=1, dk=1, dv=1, B=1, H=2, Hkv=1, N=64, d=64, P=4, causal=1,
+             layout=0, scale=0.125, dtype=1, stream=None, ws=256, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.ring_attn_bwd(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                             a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["P"], a["causal"], a["layout"], a["scale"],
+                             a["dtype"], a["stream"], a["ws"], a["ws_bytes"])
+
+
+@pytest.mark.parametrize("kw,status,frag", [
+    (dict(dout=None), ra.RA_EINVAL, "null"),
+    (dict(dv=None), ra.RA_EINVAL, "null"),
+    (dict(N=65), ra.RA_EINVAL, "multiple of P"),
+    (dict(H=3, Hkv=2), ra.RA_EINVAL, "multiple of Hkv"),
+    (dict(P=65, N=65 * 4), ra.RA_EINVAL, "P must be"),
+    (dict(dtype=0), ra.RA_EUNSUPPORTED, "bf16 only"),
+    (dict(ws_bytes=16), ra.RA_EINVAL, "workspace too small"),
+    (dict(ws=None), ra.RA_EINVAL, "null workspace"),
+    (dict(ws=100), ra.RA_EINVAL, "aligned"),
+])
+def test_bwd_rejects_invalid(lib, kw, status, frag):
+    assert _bwd(lib, **kw) == status
+    assert frag in lib.ra_last_error().decode()
+
+
+def test_bwd_ws_bytes_cover_fp32_gradients():
+    # fp32 accumulators for dq (B H N d), dk and dv (B Hkv N d), plus lse2 and delta (B H N)
+    B, H, Hkv, N, d, P = 1, 32, 8, 32768, 128, 8
+    need = 4 * (B * H * N * d + 2 * B * Hkv * N * d + 2 * B * H * N)
+    got = ra.load().ring_attn_bwd_ws_bytes(B, H, Hkv, N, d, P, ra.RA_BF16)
+    assert need <= got <= need + (1 << 16)
