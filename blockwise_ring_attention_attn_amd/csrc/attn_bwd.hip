@@ -683,19 +683,29 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
   for (int db = 0; db < NDB; ++db) emit_block(dq_row, G.dq_out + qrow * D, dqT[db], db, half, G.scale, first, fin);
 }
 
-// delta_i = sum_c dO_ic O_ic (one wavefront per row, bf16 inputs) and the
-// base-2 lse the kernels subtract: lse2_i = lse_i log2(e), +inf for a row
-// without visible keys (so that its P is 0).
+// delta_i = sum_c dO_ic O_ic and the base-2 lse the kernels subtract:
+// lse2_i = lse_i log2(e), +inf for a row without visible keys (so that its P
+// is 0).  A row is d/8 lanes, each with one 16-byte chunk of O and of dO
+// (read once: nontemporal loads); the lanes of a row are an aligned group,
+// so the butterfly stays inside it.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* out, const __bf16* dout, const float* lse,
                                                         float* delta, float* lse2, int64_t rows, int d) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
+  const int cpr = d >> 3;                       // 8 or 16 lanes per row
+  const int t = (int)threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * (256 / cpr) + t / cpr;
+  const int c = t % cpr;
+  const bool ok = row < rows;
   float acc = 0.f;
-  for (int cc = lane; cc < d; cc += 64) acc += (float)out[row * d + cc] * (float)dout[row * d + cc];
+  if (ok) {
+    const bf16x8 o = __builtin_bit_cast(
+        bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(out + row * d) + c));
+    const bf16x8 g = __builtin_bit_cast(
+        bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dout + row * d) + c));
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-  if (lane == 0) {
+    for (int e = 0; e < 8; ++e) acc += (float)o[e] * (float)g[e];
+  }
+  for (int m = cpr >> 1; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (ok && c == 0) {
     delta[row] = acc;
     const float l = lse[row];
     lse2[row] = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
@@ -710,7 +720,9 @@ int bwd_dkdv_rows() { return kDkdvKeys; }
 hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, float* delta, float* lse2,
                            int64_t rows, int d, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
+  if (d != 64 && d != 128) return hipErrorInvalidValue;
+  const int64_t per_block = 256 / (d / 8);      // rows per workgroup
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + per_block - 1) / per_block)), dim3(256), 0, s,
                      reinterpret_cast<const __bf16*>(out), reinterpret_cast<const __bf16*>(dout), lse, delta, lse2,
                      rows, d);
   return hipGetLastError();

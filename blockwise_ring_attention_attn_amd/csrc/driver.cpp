@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
+#include <initializer_list>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -225,6 +227,17 @@ StepPlan plan_step(int layout, int causal, int P, int s, int64_t Bl) {
 
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Tensor rows are read and written as 16-byte vectors (a row of d = 64 or 128
+// elements keeps the base's alignment); per-row fp32 statistics as 4-byte words.
+bool misaligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a != 0; }
+ra_status check_tensor_align(std::initializer_list<const void*> vec16, std::initializer_list<const void*> word4) {
+  for (const void* p : vec16)
+    if (misaligned(p, 16)) return fail(RA_EINVAL, "tensor pointers must be 16-byte aligned");
+  for (const void* p : word4)
+    if (misaligned(p, 4)) return fail(RA_EINVAL, "fp32 statistics pointers must be 4-byte aligned");
+  return RA_OK;
+}
 size_t esize(ra_dtype t) { return t == RA_BF16 ? 2 : 4; }
 bool dtype_ok(int t) { return t == RA_F32 || t == RA_BF16; }
 bool layout_ok(int l) { return l == RA_CONTIGUOUS || l == RA_STRIPED || l == RA_ZIGZAG; }
@@ -411,6 +424,7 @@ ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, 
   if (ws_bytes < W.total) return fail(RA_EINVAL, "workspace too small: need %zu bytes, got %zu", W.total, ws_bytes);
   if (W.total && !ws) return fail(RA_EINVAL, "null workspace");
   if (W.total && (reinterpret_cast<uintptr_t>(ws) % kAlign)) return fail(RA_EINVAL, "workspace must be 256-byte aligned");
+  if ((st = check_tensor_align({q, k, v, out}, {lse})) != RA_OK) return st;
   const int64_t Bl = N / P;
   const int BM = block_rows(dtype, d);
   const int64_t nqt = (Bl + BM - 1) / BM;
@@ -524,6 +538,7 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
   if (ws_bytes < W.total) return fail(RA_EINVAL, "workspace too small: need %zu bytes, got %zu", W.total, ws_bytes);
   if (W.total && !ws) return fail(RA_EINVAL, "null workspace");
   if (W.total && (reinterpret_cast<uintptr_t>(ws) % kAlign)) return fail(RA_EINVAL, "workspace must be 256-byte aligned");
+  if ((st = check_tensor_align({q, k, v, out}, {lse})) != RA_OK) return st;
   const int BM = block_rows(dtype, d);
   const int64_t nqt = (Bl + BM - 1) / BM;
   if ((int64_t)B * H * nqt > 0x7fffffffLL) return fail(RA_EINVAL, "problem too large for one launch");
@@ -663,6 +678,7 @@ ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void*
   if (ws_bytes < W.total) return fail(RA_EINVAL, "workspace too small: need %zu bytes, got %zu", W.total, ws_bytes);
   if (!ws) return fail(RA_EINVAL, "null workspace");
   if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(RA_EINVAL, "workspace must be 256-byte aligned");
+  if ((st = check_tensor_align({q, k, v, out, dout, dq, dk, dv}, {lse})) != RA_OK) return st;
   const int64_t Bl = N / P;
   const int64_t nqt = (Bl + bwd_dq_rows() - 1) / bwd_dq_rows();
   const int64_t nkt = (Bl + bwd_dkdv_rows() - 1) / bwd_dkdv_rows();
@@ -762,6 +778,10 @@ ra_status ring_attn_step(const void* q_blk, ra_kv_block kv_blk, float* m, float*
   if ((uint64_t)md->Lkv * md->d * esize(md->dtype) >= (1ull << 31))
     return fail(RA_EINVAL, "one kv head block (Lkv * d elements) must stay below 2 GiB");
   if (!(md->scale > 0.f) || !std::isfinite(md->scale)) return fail(RA_EINVAL, "scale must be finite and > 0");
+  {
+    const ra_status al = check_tensor_align({q_blk, kv_blk.k, kv_blk.v, o}, {m, l});
+    if (al != RA_OK) return al;
+  }
   const int BM = block_rows(md->dtype, md->d);
   const int64_t nqt = (md->Lq + BM - 1) / BM;
   if ((int64_t)md->B * md->H * nqt > 0x7fffffffLL) return fail(RA_EINVAL, "problem too large for one launch");
@@ -859,6 +879,7 @@ ra_status ring_attn_decode(const void* q, const void* k, const void* v, void* ou
   if (ws_bytes < need) return fail(RA_EINVAL, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
   if (!ws) return fail(RA_EINVAL, "null workspace");
   if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(RA_EINVAL, "workspace must be 256-byte aligned");
+  if ((st = check_tensor_align({q, k, v, out}, {lse})) != RA_OK) return st;
   int64_t chunk;
   int cpb;
   decode_split(B, Hkv, L, P, &chunk, &cpb);

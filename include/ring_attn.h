@@ -20,7 +20,10 @@
  *    owned by the caller; the library never allocates device memory inside a
  *    call and never frees caller memory.  Scratch state lives in `ws`, a
  *    caller-allocated device workspace of at least the size reported by the
- *    matching *_ws_bytes() query, aligned to 256 bytes.
+ *    matching *_ws_bytes() query, aligned to 256 bytes.  Tensor pointers
+ *    (q, k, v, out, o, dout, dq, dk, dv) must be 16-byte aligned and the
+ *    fp32 row statistics (lse, m, l) 4-byte aligned: rows are moved as
+ *    16-byte vectors.  Other pointers return RA_EINVAL.
  *  - `stream` is a hipStream_t (passed as void*; NULL = the null stream).
  *    Every call is asynchronous with respect to the host.  Calls that use a
  *    second stream internally fork it from `stream` and join it back before

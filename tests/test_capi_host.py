@@ -161,3 +161,30 @@ def test_bwd_ws_bytes_cover_fp32_gradients():
     need = 4 * (B * H * N * d + 2 * B * Hkv * N * d + 2 * B * H * N)
     got = ra.load().ring_attn_bwd_ws_bytes(B, H, Hkv, N, d, P, ra.RA_BF16)
     assert need <= got <= need + (1 << 16)
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(q=8), "16-byte aligned"),
+    (dict(out=256 + 4), "16-byte aligned"),
+    (dict(lse=258), "4-byte aligned"),
+])
+def test_fwd_rejects_misaligned_tensors(lib, kw, frag):
+    base = dict(q=256, k=512, v=768, out=1024, lse=1280)
+    base.update(kw)
+    assert _fwd(lib, **base) == ra.RA_EINVAL
+    assert frag in lib.ra_last_error().decode()
+
+
+def test_other_entry_points_reject_misaligned_tensors(lib):
+    t = dict(q=256, k=512, v=768, out=1024, lse=1280)
+    assert _share(lib, **dict(t, v=776)) == ra.RA_EINVAL
+    assert b"16-byte" in lib.ra_last_error()
+    assert _bwd(lib, **dict(t, dout=2048, dq=2304, dk=2568, dv=2816)) == ra.RA_EINVAL
+    assert b"16-byte" in lib.ra_last_error()
+    md = ra.ra_mask_desc(1, 2, 1, 64, 16, 16, 0.125, ra.RA_BF16, 1, 0, 4, 1, 0)
+    assert lib.ring_attn_step(256, ra.ra_kv_block(512, 768), 1024, 1280, 1544, ctypes.byref(md), None) == ra.RA_EINVAL
+    assert b"16-byte" in lib.ra_last_error()
+    assert lib.ring_attn_step(256, ra.ra_kv_block(512, 768), 1026, 1280, 1536, ctypes.byref(md), None) == ra.RA_EINVAL
+    assert b"4-byte" in lib.ra_last_error()
+    assert lib.ring_attn_decode(264, 512, 768, 1024, 1280, 1, 4, 1, 64, 64, 4, 0.1, 1, None, 256, 1 << 30) == ra.RA_EINVAL
+    assert b"16-byte" in lib.ra_last_error()
