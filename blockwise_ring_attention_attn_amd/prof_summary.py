@@ -8,6 +8,11 @@
         same counter reads for the plain calibration copy of <calib_mib> MiB;
         writes profiles/traffic.json[<kernel_key>] with bytes per launch and
         the sha256 of the kernel's source file.
+    python -m blockwise_ring_attention_attn_amd.prof_summary overlap <out_dir> <summary.md> "<command>"
+        from the kernel trace of the bench command: over the forward calls of
+        the prefill workload (the step kernels before the first decode
+        kernel), the compute stream's idle share and how much of the staging
+        copies' time runs under a step kernel.
 """
 from __future__ import annotations
 
@@ -53,6 +58,52 @@ def _per_dispatch(d: str):
     return out
 
 
+def _union(iv):
+    out = []
+    for a, b in sorted(iv):
+        if out and a <= out[-1][1]:
+            out[-1][1] = max(out[-1][1], b)
+        else:
+            out.append([a, b])
+    return out
+
+
+def _covered(a, b, merged) -> int:
+    return sum(max(0, min(b, y) - max(a, x)) for x, y in merged)
+
+
+def overlap(out_dir: str, summary: str, command: str) -> None:
+    rows = list(csv.DictReader(open(_one(os.path.join(out_dir, "**", "*_kernel_trace.csv")))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    t_end = min((int(r["Start_Timestamp"]) for r in rows if "decode_partial_kernel" in r["Kernel_Name"]),
+                default=None)
+    if t_end is None:
+        raise SystemExit("no decode kernel in the trace: cannot delimit the prefill calls")
+    steps = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows
+             if "step_bf16_kernel" in r["Kernel_Name"] and int(r["End_Timestamp"]) <= t_end]
+    if not steps:
+        raise SystemExit("no step kernel before the first decode kernel")
+    w0, w1 = steps[0][0], max(b for _, b in steps)
+    busy = _union(steps)
+    busy_ns = sum(b - a for a, b in busy)
+    copies = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows
+              if "copyBuffer" in r["Kernel_Name"] and w0 <= int(r["Start_Timestamp"]) < w1]
+    copy_ns = sum(b - a for a, b in copies)
+    under = sum(_covered(a, b, busy) for a, b in copies)
+    lines = [f"# Ring overlap ({os.path.basename(summary)})", "", "Command:", "", "```", command, "```", "",
+             "Window: from the first step kernel to the last one that ends before the first decode kernel "
+             "(the forward calls of the prefill workload, warm-up included).", "",
+             "| Figure | Value |", "|---|---|",
+             f"| step kernels | {len(steps)} |",
+             f"| window | {(w1 - w0) / 1e6:.3f} ms |",
+             f"| compute stream busy (union of step kernels) | {busy_ns / 1e6:.3f} ms |",
+             f"| compute stream idle | {100.0 * (1 - busy_ns / (w1 - w0)):.2f}% |",
+             f"| staging copy kernels | {len(copies)}, {copy_ns / 1e6:.3f} ms |",
+             f"| copy time under a step kernel | {100.0 * under / max(copy_ns, 1):.1f}% |", ""]
+    open(summary, "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def traffic(fetch_dir, write_dir, calib_mib, kernel_sub, key, source, summary, command) -> None:
     calib_kib = float(calib_mib) * 1024.0
     res = {}
@@ -91,7 +142,9 @@ def traffic(fetch_dir, write_dir, calib_mib, kernel_sub, key, source, summary, c
 
 
 if __name__ == "__main__":
-    if len(sys.argv) >= 5 and sys.argv[1] == "stats":
+    if len(sys.argv) >= 5 and sys.argv[1] == "overlap":
+        overlap(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif len(sys.argv) >= 5 and sys.argv[1] == "stats":
         stats(sys.argv[2], sys.argv[3], sys.argv[4])
     elif len(sys.argv) >= 10 and sys.argv[1] == "traffic":
         traffic(*sys.argv[2:10])

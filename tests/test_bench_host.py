@@ -34,3 +34,26 @@ def test_decode_bytes_counts_kv_once():
     c = bench.DECODE
     kv = 2 * c["B"] * c["Hkv"] * c["L"] * c["d"] * 2
     assert kv <= bench.decode_bytes(c) <= kv * 1.001
+
+
+def test_overlap_summary_on_a_synthetic_trace(tmp_path):
+    """Idle share and copy overlap from a hand-made kernel trace: step kernels
+    [0,10) and [12,20) ns, copies [5,15) and [30,31) (the latter after the
+    window), then a decode kernel at 40."""
+    from blockwise_ring_attention_attn_amd import prof_summary
+    d = tmp_path / "t"
+    d.mkdir()
+    rows = [("step_bf16_kernel<128>", 0, 10), ("__amd_rocclr_copyBuffer", 5, 15),
+            ("step_bf16_kernel<128>", 12, 20), ("__amd_rocclr_copyBuffer", 30, 31),
+            ("decode_partial_kernel<128>", 40, 50)]
+    with open(d / "x_kernel_trace.csv", "w") as f:
+        f.write('"Kernel_Name","Start_Timestamp","End_Timestamp"\n')
+        for n, a, b in rows:
+            f.write(f'"{n}",{a},{b}\n')
+    out = tmp_path / "s.md"
+    prof_summary.overlap(str(d), str(out), "cmd")
+    text = out.read_text()
+    assert "| step kernels | 2 |" in text
+    assert "| compute stream idle | 10.00% |" in text          # 2 of 20 ns
+    assert "| staging copy kernels | 1," in text               # the copy at 30 is outside the window
+    assert "| copy time under a step kernel | 80.0% |" in text  # [5,10) and [12,15) of [5,15)
