@@ -818,9 +818,10 @@ ra_status ring_attn_step(const void* q_blk, ra_kv_block kv_blk, float* m, float*
 ra_status ring_attn_finalize(const float* m, const float* l, const float* o, void* out, float* lse,
                              long long rows, int d, ra_dtype out_dtype, void* stream) {
   g_err.clear();
-  if (!m || !l || !o || !out || !lse) return fail(RA_EINVAL, "null tensor pointer");
   if (rows < 0 || d < 1 || d > 1024) return fail(RA_EINVAL, "bad rows/d");
   if (!dtype_ok(out_dtype)) return fail(RA_EINVAL, "unknown dtype %d", (int)out_dtype);
+  if (rows == 0) return RA_OK;  // nothing to do; empty tensors may carry null pointers
+  if (!m || !l || !o || !out || !lse) return fail(RA_EINVAL, "null tensor pointer");
   FinalizeArgs a{m, l, o, out, lse, rows, d};
   RA_HIP(launch_finalize(a, out_dtype == RA_BF16, static_cast<hipStream_t>(stream)), "finalize launch");
   return RA_OK;
@@ -829,8 +830,9 @@ ra_status ring_attn_finalize(const float* m, const float* l, const float* o, voi
 ra_status lse_merge(float* o_a, float* lse_a, const float* o_b, const float* lse_b, long long rows, int d,
                     void* stream) {
   g_err.clear();
-  if (!o_a || !lse_a || !o_b || !lse_b) return fail(RA_EINVAL, "null tensor pointer");
   if (rows < 0 || d < 1 || d > 1024) return fail(RA_EINVAL, "bad rows/d");
+  if (rows == 0) return RA_OK;  // nothing to do; empty tensors may carry null pointers
+  if (!o_a || !lse_a || !o_b || !lse_b) return fail(RA_EINVAL, "null tensor pointer");
   MergeArgs a{o_a, lse_a, o_b, lse_b, rows, d};
   RA_HIP(launch_lse_merge(a, static_cast<hipStream_t>(stream)), "lse_merge launch");
   return RA_OK;

@@ -148,7 +148,8 @@ ra_status ring_attn_step(const void* q_blk, ra_kv_block kv_blk, float* m, float*
 
 /* ring_attn_finalize -- O_final = o / l ([TKG] §3 equation O_final) cast to
  * out_dtype, and lse = m + ln l, for `rows` independent rows of width d.
- * A row with l == 0 (no visible key) gives out = 0 and lse = -inf.        */
+ * A row with l == 0 (no visible key) gives out = 0 and lse = -inf.
+ * rows == 0 is a no-op (the pointers are not checked then).              */
 ra_status ring_attn_finalize(const float* m, const float* l, const float* o, void* out,
                              float* lse, long long rows, int d, ra_dtype out_dtype,
                              void* stream);
@@ -161,7 +162,8 @@ ra_status ring_attn_finalize(const float* m, const float* l, const float* o, voi
  * This is the [TKG] §3 m_new / alpha / beta / l_new / O_new update applied to
  * two partial states written as (O, lse).  A row whose two lse are -inf
  * gets o = 0, lse = -inf.  o_a, o_b [rows, d] and lse_a, lse_b [rows],
- * float32; d any positive value up to 1024.
+ * float32; d any positive value up to 1024.  rows == 0 is a no-op (the
+ * pointers are not checked then).
  * ---------------------------------------------------------------------- */
 ra_status lse_merge(float* o_a, float* lse_a, const float* o_b, const float* lse_b,
                     long long rows, int d, void* stream);

@@ -188,3 +188,10 @@ def test_other_entry_points_reject_misaligned_tensors(lib):
     assert b"4-byte" in lib.ra_last_error()
     assert lib.ring_attn_decode(264, 512, 768, 1024, 1280, 1, 4, 1, 64, 64, 4, 0.1, 1, None, 256, 1 << 30) == ra.RA_EINVAL
     assert b"16-byte" in lib.ra_last_error()
+
+
+def test_merge_and_finalize_of_zero_rows_are_no_ops(lib):
+    assert lib.lse_merge(None, None, None, None, 0, 8, None) == ra.RA_OK
+    assert lib.ring_attn_finalize(None, None, None, None, None, 0, 128, 1, None) == ra.RA_OK
+    assert lib.lse_merge(None, None, None, None, -1, 8, None) == ra.RA_EINVAL
+    assert lib.ring_attn_finalize(None, None, None, None, None, 0, 128, 9, None) == ra.RA_EINVAL
