@@ -352,6 +352,26 @@ def run_decode(args) -> dict:
     }
 
 
+def run_mfma_calib(args) -> dict:
+    """The library's register-only bf16 MFMA loop: MFMAs issued, duration and
+    rate (the counter calibration run; its rate is the practical MFMA peak)."""
+    import torch
+    import blockwise_ring_attention_attn_amd as ra
+    stream = torch.cuda.current_stream()
+    wgs, iters = 2048, args.calib_iters
+    ra.diag_mfma_loop(wgs, 16, stream)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    n = ra.diag_mfma_loop(wgs, iters, stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    tflops = n * 32768.0 / (ms * 1e-3) / 1e12
+    return {"kernel": "mfma_loop_kernel", "workgroups": wgs, "iters": iters, "mfma_count": n,
+            "flops": n * 32768.0, "ms": ms, "tflops": tflops, "frac_nominal": tflops / MFMA_BF16_PEAK_TFLOPS}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -363,7 +383,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-other-forward", action="store_true",
                     help="skip the striped GQA and 1M-share forward workloads")
-    ap.add_argument("--only", choices=("prefill", "decode", "backward", "striped", "share"), default=None,
+    ap.add_argument("--calib-iters", type=int, default=8192)
+    ap.add_argument("--only", choices=("prefill", "decode", "backward", "striped", "share", "mfma_calib"),
+                    default=None,
                     help="run one workload only (profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first do a plain device copy of this many MiB (counter calibration)")
@@ -378,6 +400,9 @@ def main():
         sys.exit(1)
     if args.calib_copy_mib:
         calibration_copy(args.calib_copy_mib)
+    if args.only == "mfma_calib":
+        print(json.dumps(run_mfma_calib(args)), flush=True)
+        return
     if args.only == "decode":
         print(json.dumps(run_decode(args)), flush=True)
         return

@@ -27,6 +27,7 @@ EXPORTS = (
     "ring_attn_decode_ws_bytes", "ring_attn_decode",
     "ring_attn_bwd_ws_bytes", "ring_attn_bwd",
     "ra_last_error", "ra_version", "ra_debug_set_delays", "ra_prof_enable", "ra_prof_reset", "ra_prof_read",
+    "ra_diag_mfma_loop",
 )
 
 
@@ -95,6 +96,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.ra_prof_reset.restype = i
     lib.ra_prof_read.argtypes = [ctypes.POINTER(ctypes.c_double)]
     lib.ra_prof_read.restype = i
+    lib.ra_diag_mfma_loop.argtypes = [i, i, vp, ctypes.POINTER(ctypes.c_double)]
+    lib.ra_diag_mfma_loop.restype = i
     if path is None:
         _lib = lib
     return lib
@@ -130,26 +133,95 @@ def _stream(stream) -> int:
     return s.cuda_stream
 
 
-def _need(t, name):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+SIZE_MAX = (1 << 64) - 1
+
+
+def _tensor(t, name, shape=None, dtype=None):
+    """Checks a tensor argument's dtype, exact shape and contiguity (raises
+    TypeError / ValueError); _devices() then checks where it lives."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    return t
 
 
-def _workspace(nbytes: int, device, ws=None):
+def _devices(**named):
+    """Every tensor must be a device tensor, all on the same device."""
+    dev = None
+    for name, t in named.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def _need(t, name):
+    _tensor(t, name)
+    _devices(**{name: t})
+
+
+def _workspace(nbytes: int, like, ws=None):
     torch = _torch()
     if nbytes == 0:
         return None
     if ws is not None:
+        _tensor(ws, "ws")
+        _devices(like=like, ws=ws)
         if ws.numel() * ws.element_size() < nbytes:
             raise ValueError(f"workspace too small: need {nbytes} bytes")
         return ws
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+
+
+def _ws_size(n: int) -> int:
+    """A size query's result; SIZE_MAX means the query rejected its arguments."""
+    n = int(n)
+    if n == SIZE_MAX:
+        msg = load().ra_last_error().decode(errors="replace")
+        code = RA_ENOMEM if "address space" in msg else RA_EINVAL
+        raise RingAttnError(code, msg)
+    return n
 
 
 def ring_attn_fwd_ws_bytes(B, H, Hkv, N, d, P, dtype_code) -> int:
-    return int(load().ring_attn_fwd_ws_bytes(B, H, Hkv, N, d, P, dtype_code))
+    return _ws_size(load().ring_attn_fwd_ws_bytes(B, H, Hkv, N, d, P, dtype_code))
+
+
+def _qkv(q, k, v):
+    """Shapes and dtype of q [B, H, Nq, d] and k, v [B, Hkv, N, d]."""
+    _tensor(q, "q")
+    code = _dtype_code(q)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be 4-D: [B, H, N, d] and [B, Hkv, N, d]")
+    B, H, Nq, d = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    _tensor(k, "k", (B, Hkv, N, d), q.dtype)
+    _tensor(v, "v", (B, Hkv, N, d), q.dtype)
+    return B, H, Hkv, Nq, N, d, code
+
+
+def _outputs(q, out, lse, lse_shape):
+    torch = _torch()
+    if out is not None:
+        _tensor(out, "out", tuple(q.shape), q.dtype)
+    if lse is not None:
+        _tensor(lse, "lse", lse_shape, torch.float32)
+    _devices(q=q, out=out, lse=lse)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    return out, lse
 
 
 def ring_attn_fwd(q, k, v, *, P: int, causal: bool, layout: str = "contiguous", scale: float | None = None,
@@ -159,22 +231,15 @@ def ring_attn_fwd(q, k, v, *, P: int, causal: bool, layout: str = "contiguous", 
     q [B, H, N, d], k, v [B, Hkv, N, d] (bf16 or fp32, contiguous, on the GPU).
     Returns (out [B, H, N, d], lse [B, H, N] fp32).
     """
-    torch = _torch()
     lib = load()
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n)
-    B, H, N, d = q.shape
-    Hkv = k.shape[1]
-    code = _dtype_code(q)
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share a dtype")
-    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d):
-        raise ValueError("k, v must be [B, Hkv, N, d]")
+    B, H, Hkv, Nq, N, d, code = _qkv(q, k, v)
+    if Nq != N:
+        raise ValueError("q and k, v must hold the same N tokens")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    nb = lib.ring_attn_fwd_ws_bytes(B, H, Hkv, N, d, P, code)
-    wst = _workspace(nb, q.device, ws)
+    out, lse = _outputs(q, out, lse, (B, H, N))
+    _devices(q=q, k=k, v=v)
+    nb = _ws_size(lib.ring_attn_fwd_ws_bytes(B, H, Hkv, N, d, P, code))
+    wst = _workspace(nb, q, ws)
     _check(lib.ring_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, N, d, P,
                              int(bool(causal)), LAYOUTS[layout], scale, code, _stream(stream),
                              _ptr(wst) if wst is not None else None, nb))
@@ -184,20 +249,15 @@ def ring_attn_fwd(q, k, v, *, P: int, causal: bool, layout: str = "contiguous", 
 def ring_attn_fwd_share(q, k, v, *, P: int, rank: int, causal: bool, layout: str = "contiguous",
                         scale: float | None = None, out=None, lse=None, ws=None, stream=None):
     """One device's share: q [B, H, N/P, d] of host `rank`; k, v [B, Hkv, N, d]."""
-    torch = _torch()
     lib = load()
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n)
-    B, H, Nq, d = q.shape
-    Hkv, N = k.shape[1], k.shape[2]
-    code = _dtype_code(q)
+    B, H, Hkv, Nq, N, d, code = _qkv(q, k, v)
     if Nq * P != N:
         raise ValueError("q must hold N / P rows")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
-    nb = lib.ring_attn_fwd_share_ws_bytes(B, H, Hkv, N, d, P, code)
-    wst = _workspace(nb, q.device, ws)
+    out, lse = _outputs(q, out, lse, (B, H, Nq))
+    _devices(q=q, k=k, v=v)
+    nb = _ws_size(lib.ring_attn_fwd_share_ws_bytes(B, H, Hkv, N, d, P, code))
+    wst = _workspace(nb, q, ws)
     _check(lib.ring_attn_fwd_share(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, N, d, P,
                                    rank, int(bool(causal)), LAYOUTS[layout], scale, code, _stream(stream),
                                    _ptr(wst) if wst is not None else None, nb))
@@ -213,25 +273,24 @@ def ring_attn_bwd(q, k, v, out, dout, lse, *, P: int, causal: bool, layout: str 
     """
     torch = _torch()
     lib = load()
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout"), (lse, "lse")):
-        _need(t, n)
-    B, H, N, d = q.shape
-    Hkv = k.shape[1]
-    code = _dtype_code(q)
-    if any(t.dtype != q.dtype for t in (k, v, out, dout)):
-        raise TypeError("q, k, v, out, dout must share a dtype")
-    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d):
-        raise ValueError("k, v must be [B, Hkv, N, d]")
-    if tuple(out.shape) != (B, H, N, d) or tuple(dout.shape) != (B, H, N, d) or tuple(lse.shape) != (B, H, N):
-        raise ValueError("out, dout must be [B, H, N, d] and lse [B, H, N]")
-    if lse.dtype != torch.float32:
-        raise TypeError("lse must be float32")
+    B, H, Hkv, Nq, N, d, code = _qkv(q, k, v)
+    if Nq != N:
+        raise ValueError("q and k, v must hold the same N tokens")
+    if code != RA_BF16:
+        raise TypeError("ring_attn_bwd supports bfloat16 only")
+    _tensor(out, "out", (B, H, N, d), q.dtype)
+    _tensor(dout, "dout", (B, H, N, d), q.dtype)
+    _tensor(lse, "lse", (B, H, N), torch.float32)
+    for g, like, nm in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        if g is not None:
+            _tensor(g, nm, tuple(like.shape), like.dtype)
+    _devices(q=q, k=k, v=v, out=out, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    nb = lib.ring_attn_bwd_ws_bytes(B, H, Hkv, N, d, P, code)
-    wst = _workspace(nb, q.device, ws)
+    nb = _ws_size(lib.ring_attn_bwd_ws_bytes(B, H, Hkv, N, d, P, code))
+    wst = _workspace(nb, q, ws)
     _check(lib.ring_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
                              _ptr(dv), B, H, Hkv, N, d, P, int(bool(causal)), LAYOUTS[layout], scale, code,
                              _stream(stream), _ptr(wst) if wst is not None else None, nb))
@@ -250,12 +309,13 @@ def init_state(B, H, Lq, d, device):
 def ring_attn_step(q_blk, k_blk, v_blk, m, l, o, *, causal: bool, layout: str = "contiguous", P: int = 1,
                    q_rank: int = 0, kv_rank: int = 0, scale: float | None = None, stream=None):
     """One ring step updating (m, l, o) in place (see ring_attn.h)."""
+    torch = _torch()
     lib = load()
-    for t, n in ((q_blk, "q_blk"), (k_blk, "k_blk"), (v_blk, "v_blk"), (m, "m"), (l, "l"), (o, "o")):
-        _need(t, n)
-    B, H, Lq, d = q_blk.shape
-    Hkv, Lkv = k_blk.shape[1], k_blk.shape[2]
-    code = _dtype_code(q_blk)
+    B, H, Hkv, Lq, Lkv, d, code = _qkv(q_blk, k_blk, v_blk)
+    _tensor(m, "m", (B, H, Lq), torch.float32)
+    _tensor(l, "l", (B, H, Lq), torch.float32)
+    _tensor(o, "o", (B, H, Lq, d), torch.float32)
+    _devices(q_blk=q_blk, k_blk=k_blk, v_blk=v_blk, m=m, l=l, o=o)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     md = ra_mask_desc(B, H, Hkv, d, Lq, Lkv, scale, code, int(bool(causal)), LAYOUTS[layout], P,
                       q_rank, kv_rank)
@@ -268,44 +328,70 @@ def ring_attn_finalize(m, l, o, *, out_dtype=None, out=None, lse=None, stream=No
     """(out, lse) = (o / l, m + ln l) for the rows of the state."""
     torch = _torch()
     lib = load()
+    _tensor(o, "o", None, torch.float32)
+    if o.dim() < 1:
+        raise ValueError("o must have a trailing dim axis")
+    rows_shape = tuple(o.shape[:-1])
+    _tensor(m, "m", rows_shape, torch.float32)
+    _tensor(l, "l", rows_shape, torch.float32)
+    if out is not None:
+        _tensor(out, "out", tuple(o.shape), out_dtype or out.dtype)
+    if lse is not None:
+        _tensor(lse, "lse", rows_shape, torch.float32)
+    _devices(o=o, m=m, l=l, out=out, lse=lse)
     d = o.shape[-1]
-    rows = o.numel() // d
-    out_dtype = out_dtype or torch.bfloat16
-    out = torch.empty(o.shape, dtype=out_dtype, device=o.device) if out is None else out
-    lse = torch.empty(m.shape, dtype=torch.float32, device=o.device) if lse is None else lse
-    _check(lib.ring_attn_finalize(_ptr(m), _ptr(l), _ptr(o), _ptr(out), _ptr(lse), rows, d,
-                                  _dtype_code(out), _stream(stream)))
+    rows = o.numel() // d if d else 0
+    if out is None:
+        out = torch.empty(o.shape, dtype=out_dtype or torch.bfloat16, device=o.device)
+    code = _dtype_code(out)
+    if lse is None:
+        lse = torch.empty(rows_shape, dtype=torch.float32, device=o.device)
+    _check(lib.ring_attn_finalize(_ptr(m), _ptr(l), _ptr(o), _ptr(out), _ptr(lse), rows, d, code,
+                                  _stream(stream)))
     return out, lse
 
 
 def lse_merge(o_a, lse_a, o_b, lse_b, *, stream=None):
     """In-place merge of (o_b, lse_b) into (o_a, lse_a) (fp32)."""
+    torch = _torch()
     lib = load()
-    for t, n in ((o_a, "o_a"), (lse_a, "lse_a"), (o_b, "o_b"), (lse_b, "lse_b")):
-        _need(t, n)
+    _tensor(o_a, "o_a", None, torch.float32)
+    if o_a.dim() < 1:
+        raise ValueError("o_a must have a trailing dim axis")
+    rows_shape = tuple(o_a.shape[:-1])
+    _tensor(o_b, "o_b", tuple(o_a.shape), torch.float32)
+    _tensor(lse_a, "lse_a", rows_shape, torch.float32)
+    _tensor(lse_b, "lse_b", rows_shape, torch.float32)
+    _devices(o_a=o_a, o_b=o_b, lse_a=lse_a, lse_b=lse_b)
     d = o_a.shape[-1]
-    rows = o_a.numel() // d
+    rows = o_a.numel() // d if d else 0
     _check(lib.lse_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), rows, d, _stream(stream)))
     return o_a, lse_a
+
+
+def ring_attn_decode_ws_bytes(B, H, Hkv, L, d, P) -> int:
+    return _ws_size(load().ring_attn_decode_ws_bytes(B, H, Hkv, L, d, P))
+
+
+def _decode_args(q, k, v, out, lse):
+    B, H, Hkv, one, L, d, code = _qkv(q, k, v)
+    if one != 1:
+        raise ValueError("q must be [B, H, 1, d]")
+    if code != RA_BF16:
+        raise TypeError("decode supports bfloat16 only")
+    out, lse = _outputs(q, out, lse, (B, H))
+    _devices(q=q, k=k, v=v)
+    return B, H, Hkv, L, d, code, out, lse
 
 
 def ring_attn_decode(q, k, v, *, P: int, scale: float | None = None, out=None, lse=None, ws=None,
                      stream=None):
     """Split-KV decode: q [B, H, 1, d]; k, v [B, Hkv, L, d] -> (out [B, H, 1, d], lse [B, H])."""
-    torch = _torch()
     lib = load()
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n)
-    B, H, one, d = q.shape
-    Hkv, L = k.shape[1], k.shape[2]
-    if one != 1:
-        raise ValueError("q must be [B, H, 1, d]")
-    code = _dtype_code(q)
+    B, H, Hkv, L, d, code, out, lse = _decode_args(q, k, v, out, lse)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if lse is None else lse
-    nb = lib.ring_attn_decode_ws_bytes(B, H, Hkv, L, d, P)
-    wst = _workspace(nb, q.device, ws)
+    nb = ring_attn_decode_ws_bytes(B, H, Hkv, L, d, P)
+    wst = _workspace(nb, q, ws)
     _check(lib.ring_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, L, d, P, scale,
                                 code, _stream(stream), _ptr(wst) if wst is not None else None, nb))
     return out, lse
@@ -314,6 +400,13 @@ def ring_attn_decode(q, k, v, *, P: int, scale: float | None = None, out=None, l
 def debug_set_delays(compute_us: int = 0, copy_us: int = 0) -> None:
     """Test hook: bounded spins before every step kernel / staging copy."""
     _check(load().ra_debug_set_delays(int(compute_us), int(copy_us)))
+
+
+def diag_mfma_loop(workgroups: int, iters: int, stream=None) -> float:
+    """Counter calibration: a register-only bf16 MFMA loop; returns its MFMA count."""
+    n = ctypes.c_double()
+    _check(load().ra_diag_mfma_loop(int(workgroups), int(iters), _stream(stream), ctypes.byref(n)))
+    return n.value
 
 
 def prof_enable(on: bool = True) -> None:

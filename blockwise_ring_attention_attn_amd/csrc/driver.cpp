@@ -262,31 +262,85 @@ ra_status check_common(int B, int H, int Hkv, long long N, int d, int P, ra_dtyp
   if (N / P > (1LL << 30)) return fail(RA_EINVAL, "block length N/P too large");
   if (!dtype_ok(dtype)) return fail(RA_EINVAL, "unknown dtype %d", (int)dtype);
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(RA_EINVAL, "scale must be finite and > 0");
-  // The bf16 kernels address one (batch, kv head) plane with 32-bit buffer offsets.
-  if ((uint64_t)N * d * esize(dtype) >= (1ull << 31))
-    return fail(RA_EINVAL, "one kv head plane (N * d elements) must stay below 2 GiB");
   return RA_OK;
 }
+
+// The bf16 step kernel reads a key/value block through a buffer descriptor
+// with 32-bit offsets: one block of one (batch, kv head) plane must stay
+// below 2 GiB.  (A striped ring whose whole plane is larger stages its first
+// step's blocks instead of reading them in place; see stage_first_block.)
+constexpr uint64_t kSpanLimit = 1ull << 31;
+ra_status check_block_span(long long rows, int d, ra_dtype dtype) {
+  if (dtype == RA_BF16 && (uint64_t)rows * d * esize(dtype) >= kSpanLimit)
+    return fail(RA_EINVAL, "one key/value block of one head (%lld rows x %d) must stay below 2 GiB", rows, d);
+  return RA_OK;
+}
+
+// Does the first ring step need its key/value blocks staged (compact) rather
+// than read in place from the natural-order k / v?  Zigzag blocks are two
+// separate chunks; a striped block read in place spans the whole plane,
+// which the bf16 kernel's 32-bit buffer offsets reach only below 2 GiB.
+bool stage_first_block(int layout, long long N, int d, int P, ra_dtype dtype) {
+  if (layout == RA_ZIGZAG) return true;
+  return layout == RA_STRIPED && P > 1 && dtype == RA_BF16 && (uint64_t)N * d * esize(dtype) >= kSpanLimit;
+}
+
+// Workspace sizes are computed in 64 bits with overflow checks.  Device
+// virtual addresses are 48 bits wide, so anything at or above 2^48 bytes
+// cannot be allocated: the size queries return SIZE_MAX and the launches
+// RA_ENOMEM.
+constexpr uint64_t kMaxAllocBytes = 1ull << 48;
+struct SizeAcc {
+  uint64_t total = 0;
+  bool bad = false;
+  // appends a region of n1 * n2 * ... bytes (aligned), returns its offset
+  size_t add(std::initializer_list<uint64_t> factors) {
+    uint64_t x = 1;
+    for (uint64_t f : factors)
+      if (__builtin_mul_overflow(x, f, &x)) bad = true;
+    if (x >= kMaxAllocBytes) bad = true;
+    const size_t off = (size_t)total;
+    if (!bad) {
+      x = (x + kAlign - 1) / kAlign * kAlign;
+      if (__builtin_add_overflow(total, x, &total) || total >= kMaxAllocBytes) bad = true;
+    }
+    return off;
+  }
+};
 
 struct FwdWs {
   size_t stage_bytes;  // one staging buffer (K and V)
   size_t kv_bytes;     // K (or V) part of a staging buffer
   size_t off_stage[2], off_m, off_l, off_o, total;
+  bool overflow;       // the sizes do not fit a device allocation
 };
 
 FwdWs fwd_ws_layout(int B, int H, int Hkv, long long Nq, long long Nkv_stage, int d, int P, ra_dtype dtype) {
   FwdWs w{};
   if (P == 1) return w;  // single block: no staging, no state
-  w.kv_bytes = align_up((size_t)B * Hkv * Nkv_stage * d * esize(dtype));
-  w.stage_bytes = 2 * w.kv_bytes;
-  size_t off = 0;
-  w.off_stage[0] = off; off += w.stage_bytes;
-  w.off_stage[1] = off; off += w.stage_bytes;
-  w.off_m = off; off += align_up((size_t)B * H * Nq * 4);
-  w.off_l = off; off += align_up((size_t)B * H * Nq * 4);
-  w.off_o = off; off += align_up((size_t)B * H * Nq * d * 4);
-  w.total = off;
+  SizeAcc a;
+  w.off_stage[0] = a.add({(uint64_t)B, (uint64_t)Hkv, (uint64_t)Nkv_stage, (uint64_t)d, esize(dtype)});
+  const size_t k_end = (size_t)a.total;
+  w.kv_bytes = k_end - w.off_stage[0];
+  a.add({(uint64_t)B, (uint64_t)Hkv, (uint64_t)Nkv_stage, (uint64_t)d, esize(dtype)});
+  w.stage_bytes = (size_t)a.total - w.off_stage[0];
+  w.off_stage[1] = a.add({2, w.kv_bytes});
+  w.off_m = a.add({(uint64_t)B, (uint64_t)H, (uint64_t)Nq, 4});
+  w.off_l = a.add({(uint64_t)B, (uint64_t)H, (uint64_t)Nq, 4});
+  w.off_o = a.add({(uint64_t)B, (uint64_t)H, (uint64_t)Nq, (uint64_t)d, 4});
+  w.total = (size_t)a.total;
+  w.overflow = a.bad;
   return w;
+}
+
+// Workspace check shared by the launches: RA_ENOMEM for sizes no device can
+// hold, RA_EINVAL for a missing, short or misaligned workspace.
+ra_status check_ws(bool overflow, size_t need, const void* ws, size_t ws_bytes) {
+  if (overflow) return fail(RA_ENOMEM, "workspace size exceeds the 48-bit device address space");
+  if (ws_bytes < need) return fail(RA_EINVAL, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
+  if (need && !ws) return fail(RA_EINVAL, "null workspace");
+  if (need && (reinterpret_cast<uintptr_t>(ws) % kAlign)) return fail(RA_EINVAL, "workspace must be 256-byte aligned");
+  return RA_OK;
 }
 
 hipError_t launch_step(const StepArgs& a, int d, ra_dtype dtype, hipStream_t s, double flops) {
@@ -400,14 +454,31 @@ extern "C" {
 const char* ra_last_error(void) { return g_err.c_str(); }
 const char* ra_version(void) { return "ring_attn 0.1 gfx950"; }
 
+// The size queries apply the launch's own checks to the arguments they take
+// and return SIZE_MAX (with a message for ra_last_error) when those fail or
+// the size cannot be allocated; 0 means that no workspace is needed.
 size_t ring_attn_fwd_ws_bytes(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype) {
-  if (B < 1 || H < 1 || Hkv < 1 || P < 1 || N < 1 || N % P) return 0;
-  return fwd_ws_layout(B, H, Hkv, N, N, d, P, dtype).total;
+  g_err.clear();
+  if (check_common(B, H, Hkv, N, d, P, dtype, 1.f) != RA_OK || check_block_span(N / P, d, dtype) != RA_OK)
+    return SIZE_MAX;
+  const FwdWs W = fwd_ws_layout(B, H, Hkv, N, N, d, P, dtype);
+  if (W.overflow) {
+    fail(RA_ENOMEM, "workspace size exceeds the 48-bit device address space");
+    return SIZE_MAX;
+  }
+  return W.total;
 }
 
 size_t ring_attn_fwd_share_ws_bytes(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype) {
-  if (B < 1 || H < 1 || Hkv < 1 || P < 1 || N < 1 || N % P) return 0;
-  return fwd_ws_layout(B, H, Hkv, N / P, N / P, d, P, dtype).total;
+  g_err.clear();
+  if (check_common(B, H, Hkv, N, d, P, dtype, 1.f) != RA_OK || check_block_span(N / P, d, dtype) != RA_OK)
+    return SIZE_MAX;
+  const FwdWs W = fwd_ws_layout(B, H, Hkv, N / P, N / P, d, P, dtype);
+  if (W.overflow) {
+    fail(RA_ENOMEM, "workspace size exceeds the 48-bit device address space");
+    return SIZE_MAX;
+  }
+  return W.total;
 }
 
 ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
@@ -418,12 +489,11 @@ ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, 
   ra_status st = check_common(B, H, Hkv, N, d, P, dtype, scale);
   if (st != RA_OK) return st;
   if ((st = check_layout(layout, N, P)) != RA_OK) return st;
+  if ((st = check_block_span(N / P, d, dtype)) != RA_OK) return st;
   const int lay = effective_layout(layout, P);
-  const bool stage_own = lay == RA_ZIGZAG;  // blocks not readable in place: stage step 0 too
+  const bool stage_own = stage_first_block(lay, N, d, P, dtype);  // step 0 reads staged blocks too
   const FwdWs W = fwd_ws_layout(B, H, Hkv, N, N, d, P, dtype);
-  if (ws_bytes < W.total) return fail(RA_EINVAL, "workspace too small: need %zu bytes, got %zu", W.total, ws_bytes);
-  if (W.total && !ws) return fail(RA_EINVAL, "null workspace");
-  if (W.total && (reinterpret_cast<uintptr_t>(ws) % kAlign)) return fail(RA_EINVAL, "workspace must be 256-byte aligned");
+  if ((st = check_ws(W.overflow, W.total, ws, ws_bytes)) != RA_OK) return st;
   if ((st = check_tensor_align({q, k, v, out}, {lse})) != RA_OK) return st;
   const int64_t Bl = N / P;
   const int BM = block_rows(dtype, d);
@@ -530,14 +600,13 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
   ra_status st = check_common(B, H, Hkv, N, d, P, dtype, scale);
   if (st != RA_OK) return st;
   if ((st = check_layout(layout, N, P)) != RA_OK) return st;
+  if ((st = check_block_span(N / P, d, dtype)) != RA_OK) return st;
   const int lay = effective_layout(layout, P);
-  const bool stage_first = lay == RA_ZIGZAG;  // the first block is not readable in place
+  const bool stage_first = stage_first_block(lay, N, d, P, dtype);  // the first block is not read in place
   if (rank < 0 || rank >= P) return fail(RA_EINVAL, "rank %d out of [0, %d)", rank, P);
   const int64_t Bl = N / P;
   const FwdWs W = fwd_ws_layout(B, H, Hkv, Bl, Bl, d, P, dtype);
-  if (ws_bytes < W.total) return fail(RA_EINVAL, "workspace too small: need %zu bytes, got %zu", W.total, ws_bytes);
-  if (W.total && !ws) return fail(RA_EINVAL, "null workspace");
-  if (W.total && (reinterpret_cast<uintptr_t>(ws) % kAlign)) return fail(RA_EINVAL, "workspace must be 256-byte aligned");
+  if ((st = check_ws(W.overflow, W.total, ws, ws_bytes)) != RA_OK) return st;
   if ((st = check_tensor_align({q, k, v, out}, {lse})) != RA_OK) return st;
   const int BM = block_rows(dtype, d);
   const int64_t nqt = (Bl + BM - 1) / BM;
@@ -644,24 +713,42 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
 // ---------------------------------------------------------------------------
 struct BwdWs {
   size_t off_delta, off_lse2, off_dq, off_dk, off_dv, total;
+  bool overflow;
 };
 
 static BwdWs bwd_ws_layout(int B, int H, int Hkv, long long N, int d) {
   BwdWs w{};
-  size_t off = 0;
-  w.off_delta = off; off += align_up((size_t)B * H * N * 4);
-  w.off_lse2 = off; off += align_up((size_t)B * H * N * 4);
-  w.off_dq = off; off += align_up((size_t)B * H * N * d * 4);
-  w.off_dk = off; off += align_up((size_t)B * Hkv * N * d * 4);
-  w.off_dv = off; off += align_up((size_t)B * Hkv * N * d * 4);
-  w.total = off;
+  SizeAcc a;
+  w.off_delta = a.add({(uint64_t)B, (uint64_t)H, (uint64_t)N, 4});
+  w.off_lse2 = a.add({(uint64_t)B, (uint64_t)H, (uint64_t)N, 4});
+  w.off_dq = a.add({(uint64_t)B, (uint64_t)H, (uint64_t)N, (uint64_t)d, 4});
+  w.off_dk = a.add({(uint64_t)B, (uint64_t)Hkv, (uint64_t)N, (uint64_t)d, 4});
+  w.off_dv = a.add({(uint64_t)B, (uint64_t)Hkv, (uint64_t)N, (uint64_t)d, 4});
+  w.total = (size_t)a.total;
+  w.overflow = a.bad;
   return w;
 }
 
+// The backward kernels read q, dO and the row statistics of a whole
+// (batch, head) plane through buffer descriptors with 32-bit offsets.
+ra_status bwd_args(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype, float scale) {
+  ra_status st = check_common(B, H, Hkv, N, d, P, dtype, scale);
+  if (st != RA_OK) return st;
+  if (dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "ring_attn_bwd supports bf16 only");
+  if ((uint64_t)N * d * esize(dtype) >= kSpanLimit)
+    return fail(RA_EINVAL, "the backward needs one head plane (N * d elements) below 2 GiB");
+  return RA_OK;
+}
+
 size_t ring_attn_bwd_ws_bytes(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype) {
-  (void)dtype;
-  if (B < 1 || H < 1 || Hkv < 1 || P < 1 || N < 1 || N % P) return 0;
-  return bwd_ws_layout(B, H, Hkv, N, d).total;
+  g_err.clear();
+  if (bwd_args(B, H, Hkv, N, d, P, dtype, 1.f) != RA_OK) return SIZE_MAX;
+  const BwdWs W = bwd_ws_layout(B, H, Hkv, N, d);
+  if (W.overflow) {
+    fail(RA_ENOMEM, "workspace size exceeds the 48-bit device address space");
+    return SIZE_MAX;
+  }
+  return W.total;
 }
 
 ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -670,14 +757,11 @@ ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void*
                         size_t ws_bytes) {
   g_err.clear();
   if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv) return fail(RA_EINVAL, "null tensor pointer");
-  ra_status st = check_common(B, H, Hkv, N, d, P, dtype, scale);
+  ra_status st = bwd_args(B, H, Hkv, N, d, P, dtype, scale);
   if (st != RA_OK) return st;
   if ((st = check_layout(layout, N, P)) != RA_OK) return st;
-  if (dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "ring_attn_bwd supports bf16 only");
   const BwdWs W = bwd_ws_layout(B, H, Hkv, N, d);
-  if (ws_bytes < W.total) return fail(RA_EINVAL, "workspace too small: need %zu bytes, got %zu", W.total, ws_bytes);
-  if (!ws) return fail(RA_EINVAL, "null workspace");
-  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(RA_EINVAL, "workspace must be 256-byte aligned");
+  if ((st = check_ws(W.overflow, W.total, ws, ws_bytes)) != RA_OK) return st;
   if ((st = check_tensor_align({q, k, v, out, dout, dq, dk, dv}, {lse})) != RA_OK) return st;
   const int64_t Bl = N / P;
   const int64_t nqt = (Bl + bwd_dq_rows() - 1) / bwd_dq_rows();
@@ -775,8 +859,10 @@ ra_status ring_attn_step(const void* q_blk, ra_kv_block kv_blk, float* m, float*
     return fail(RA_EINVAL, "bad ring description P=%d q_rank=%d kv_rank=%d", md->P, md->q_rank, md->kv_rank);
   if (md->layout == RA_STRIPED && md->causal && md->Lq != md->Lkv)
     return fail(RA_EINVAL, "striped causal blocks must have Lq == Lkv");
-  if ((uint64_t)md->Lkv * md->d * esize(md->dtype) >= (1ull << 31))
-    return fail(RA_EINVAL, "one kv head block (Lkv * d elements) must stay below 2 GiB");
+  {
+    const ra_status sp = check_block_span(md->Lkv, md->d, md->dtype);
+    if (sp != RA_OK) return sp;
+  }
   if (!(md->scale > 0.f) || !std::isfinite(md->scale)) return fail(RA_EINVAL, "scale must be finite and > 0");
   {
     const ra_status al = check_tensor_align({q_blk, kv_blk.k, kv_blk.v, o}, {m, l});
@@ -855,51 +941,58 @@ void decode_split(int B, int Hkv, long long L, int P, int64_t* chunk, int* cpb) 
   *chunk = ch;
   *cpb = (int)((block + ch - 1) / ch);
 }
-}  // namespace
 
-extern "C" {
-
-size_t ring_attn_decode_ws_bytes(int B, int H, int Hkv, long long L, int d, int P) {
-  if (B < 1 || H < 1 || Hkv < 1 || P < 1 || L < 1 || L % P || d < 1) return 0;
-  int64_t chunk;
-  int cpb;
-  decode_split(B, Hkv, L, P, &chunk, &cpb);
-  const int64_t S = (int64_t)P * cpb * kDecodeWaves;
-  return align_up((size_t)B * H * S * d * 4) + align_up((size_t)B * H * S * 4);
-}
-
-ra_status ring_attn_decode(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
-                           int Hkv, long long L, int d, int P, float scale, ra_dtype dtype, void* stream,
-                           void* ws, size_t ws_bytes) {
-  g_err.clear();
-  if (!q || !k || !v || !out || !lse) return fail(RA_EINVAL, "null tensor pointer");
+ra_status decode_args(int B, int H, int Hkv, long long L, int d, int P, ra_dtype dtype, float scale) {
   ra_status st = check_common(B, H, Hkv, L, d, P, dtype, scale);
   if (st != RA_OK) return st;
   if (dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "decode supports bf16 only");
   if (H / Hkv > 16) return fail(RA_EINVAL, "H/Hkv must be <= 16 (got %d)", H / Hkv);
-  const size_t need = ring_attn_decode_ws_bytes(B, H, Hkv, L, d, P);
-  if (ws_bytes < need) return fail(RA_EINVAL, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
-  if (!ws) return fail(RA_EINVAL, "null workspace");
-  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(RA_EINVAL, "workspace must be 256-byte aligned");
-  if ((st = check_tensor_align({q, k, v, out}, {lse})) != RA_OK) return st;
+  return RA_OK;
+}
+
+// Decode workspace: per-wavefront partials o_part [B, H, S, d] and
+// lse_part [B, H, S] (fp32), S = P x chunks per ring block x 4 waves.
+struct DecodeWs {
   int64_t chunk;
-  int cpb;
-  decode_split(B, Hkv, L, P, &chunk, &cpb);
-  if ((int64_t)B * Hkv * P * cpb > 0x7fffffffLL) return fail(RA_EINVAL, "problem too large");
+  int cpb, S;
+  size_t off_o, off_lse, total;
+  bool overflow;
+};
+
+DecodeWs decode_ws_layout(int B, int H, int Hkv, long long L, int d, int P) {
+  DecodeWs w{};
+  decode_split(B, Hkv, L, P, &w.chunk, &w.cpb);
+  const int64_t S = (int64_t)P * w.cpb * kDecodeWaves;
+  w.S = S > 0x7fffffffLL ? 0 : (int)S;
+  SizeAcc a;
+  w.off_o = a.add({(uint64_t)B, (uint64_t)H, (uint64_t)S, (uint64_t)d, 4});
+  w.off_lse = a.add({(uint64_t)B, (uint64_t)H, (uint64_t)S, 4});
+  w.total = (size_t)a.total;
+  w.overflow = a.bad || S > 0x7fffffffLL;
+  return w;
+}
+
+// Shared by ring_attn_decode and ring_attn_decode_noalloc: argument checks
+// past the workspace, then the partial and merge launches on `stream`.
+ra_status decode_launch(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Hkv,
+                        long long L, int d, int P, float scale, const DecodeWs& W, void* wsb_, void* stream) {
+  ra_status st = check_tensor_align({q, k, v, out}, {lse});
+  if (st != RA_OK) return st;
+  if ((int64_t)B * Hkv * P * W.cpb > 0x7fffffffLL) return fail(RA_EINVAL, "problem too large");
   DeviceCtx* ctx = nullptr;
   if ((st = get_ctx(&ctx)) != RA_OK) return st;
   DecodeArgs a{};
   a.q = q; a.k = k; a.v = v;
-  a.S = P * cpb * kDecodeWaves;
-  char* wsb = static_cast<char*>(ws);
-  a.o_part = reinterpret_cast<float*>(wsb);
-  a.lse_part = reinterpret_cast<float*>(wsb + align_up((size_t)B * H * a.S * d * 4));
+  a.S = W.S;
+  char* wsb = static_cast<char*>(wsb_);
+  a.o_part = reinterpret_cast<float*>(wsb + W.off_o);
+  a.lse_part = reinterpret_cast<float*>(wsb + W.off_lse);
   a.out = out; a.lse = lse;
   a.B = B; a.H = H; a.Hkv = Hkv; a.group = H / Hkv;
   a.L = L;
-  a.chunk = chunk;
+  a.chunk = W.chunk;
   a.block = L / P;
-  a.chunks_per_block = cpb;
+  a.chunks_per_block = W.cpb;
   a.P = P;
   a.scale_log2 = scale * 1.4426950408889634f;
   hipStream_t cs = static_cast<hipStream_t>(stream);
@@ -913,12 +1006,49 @@ ra_status ring_attn_decode(const void* q, const void* k, const void* v, void* ou
   return RA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+size_t ring_attn_decode_ws_bytes(int B, int H, int Hkv, long long L, int d, int P) {
+  g_err.clear();
+  if (decode_args(B, H, Hkv, L, d, P, RA_BF16, 1.f) != RA_OK) return SIZE_MAX;
+  const DecodeWs W = decode_ws_layout(B, H, Hkv, L, d, P);
+  if (W.overflow) {
+    fail(RA_ENOMEM, "workspace size exceeds the 48-bit device address space");
+    return SIZE_MAX;
+  }
+  return W.total;
+}
+
+ra_status ring_attn_decode(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                           int Hkv, long long L, int d, int P, float scale, ra_dtype dtype, void* stream,
+                           void* ws, size_t ws_bytes) {
+  g_err.clear();
+  if (!q || !k || !v || !out || !lse) return fail(RA_EINVAL, "null tensor pointer");
+  ra_status st = decode_args(B, H, Hkv, L, d, P, dtype, scale);
+  if (st != RA_OK) return st;
+  const DecodeWs W = decode_ws_layout(B, H, Hkv, L, d, P);
+  if ((st = check_ws(W.overflow, W.total, ws, ws_bytes)) != RA_OK) return st;
+  if (!ws) return fail(RA_EINVAL, "null workspace");
+  return decode_launch(q, k, v, out, lse, B, H, Hkv, L, d, P, scale, W, ws, stream);
+}
+
 ra_status ra_debug_set_delays(int compute_us, int copy_us) {
   if (compute_us < 0 || copy_us < 0 || compute_us > 100000 || copy_us > 100000)
     return fail(RA_EINVAL, "delays must be in [0, 100000] us");
   std::lock_guard<std::mutex> lk(g_mu);
   g_delay_compute_us = compute_us;
   g_delay_copy_us = copy_us;
+  return RA_OK;
+}
+
+ra_status ra_diag_mfma_loop(int workgroups, int iters, void* stream, double* mfma_count) {
+  g_err.clear();
+  if (!mfma_count) return fail(RA_EINVAL, "null output");
+  if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 24))
+    return fail(RA_EINVAL, "workgroups must be in [1, 2^20] and iters in [1, 2^24]");
+  RA_HIP(launch_mfma_loop(workgroups, iters, static_cast<hipStream_t>(stream), mfma_count), "calibration launch");
   return RA_OK;
 }
 

@@ -107,6 +107,9 @@ hipError_t launch_finalize(const FinalizeArgs& a, int out_bf16, hipStream_t s);
 hipError_t launch_decode_partial(const DecodeArgs& a, int d, int bf16, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs& a, int d, int bf16, hipStream_t s);
 hipError_t launch_spin(int microseconds, hipStream_t s);  // bounded busy wait (test hook)
+// Counter calibration: `workgroups` x 4 waves, each issuing iters x 8 bf16
+// 32x32x16 MFMAs from registers; *mfma_count receives the total issued.
+hipError_t launch_mfma_loop(int workgroups, int iters, hipStream_t s, double* mfma_count);
 
 // Backward (bf16): delta = rowsum(dO * O); dK/dV and dQ step kernels (the
 // first step writes the fp32 accumulators, a row's last step its bf16 result).

@@ -30,10 +30,24 @@
  *    returning, so callers see ordinary single-stream semantics.
  *  - Errors: a call returns RA_OK or an error code BEFORE launching anything
  *    when an argument is invalid (RA_EINVAL: null pointer, N % P != 0,
- *    H % Hkv != 0, unsupported d, workspace too small, ...).  A failed HIP
- *    runtime call returns RA_EHIP.  ra_last_error() then gives a message
- *    (thread-local).  Faults inside kernels surface at the caller's next
- *    synchronization, as with any HIP kernel.  No call aborts the process.
+ *    H % Hkv != 0, unsupported d, workspace too small, ...).  RA_ENOMEM:
+ *    the workspace the arguments need would not fit a device allocation
+ *    (its size overflows, or reaches 2^48 bytes, the width of the device's
+ *    virtual addresses).  A failed HIP runtime call returns RA_EHIP.
+ *    ra_last_error() then gives a message (thread-local).  Faults inside
+ *    kernels surface at the caller's next synchronization, as with any HIP
+ *    kernel.  No call aborts the process.
+ *  - Workspace size queries (*_ws_bytes) apply the launch's checks to the
+ *    arguments they take.  They return the size in bytes (0: the call needs
+ *    no workspace), or SIZE_MAX when the arguments are invalid or the size
+ *    cannot be allocated; ra_last_error() then says which.
+ *  - Sizes: block lengths N / P up to 2^30 tokens.  The bf16 step kernel
+ *    reads a key/value block through 32-bit buffer offsets, so one block of
+ *    one (batch, kv head) plane must stay below 2 GiB (N / P * d * 2 bytes);
+ *    whole planes may be larger (a striped ring whose plane is 2 GiB or more
+ *    stages its first step's blocks instead of reading them in place).
+ *    ring_attn_bwd needs one head plane below 2 GiB; decode has no such
+ *    limit (64-bit addressing).
  */
 #ifndef RING_ATTN_H
 #define RING_ATTN_H
@@ -116,14 +130,20 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
  *
  * q_blk [B, H, Lq, d]; kv_blk.k, kv_blk.v [B, Hkv, Lkv, d] (compact blocks,
  * element type mask_desc->dtype).  State, float32, caller-owned:
- *   m [B, H, Lq]      reference row max of the scaled logits (natural units)
+ *   m [B, H, Lq]      the row's REFERENCE max of the scaled logits seen so
+ *                     far (natural units): the running max of [TKG] §3
+ *                     equation m_new, or up to 16 / log2(e) below it
  *   l [B, H, Lq]      sum over keys seen so far of exp(s - m)
  *   o [B, H, Lq, d]   sum over keys seen so far of exp(s - m) * v
  * Initialize with m = -inf, l = 0, o = 0.  After the call (m, l, o) describe
- * the keys seen before plus this block.  The kernel may keep m below the
- * true running max (by at most 16 / log2(e) in natural units) to skip
- * rescaling; l and o are always relative to the stored m, so O = o / l and
- * lse = m + ln l are exact either way (ring_attn_finalize computes them).
+ * the keys seen before plus this block.  The bf16 kernel moves the reference
+ * up to the true running max only when a tile's weights exp(s - m) would
+ * exceed 2^16 (it skips the rescale otherwise); l and o are always relative
+ * to the stored m.  So O = o / l and lse = m + ln l are exact, and so is a
+ * merge of two such states by the [TKG] §3 update (m_new = max(m_a, m_b),
+ * alpha = e^(m_a - m_new), beta = e^(m_b - m_new), l = alpha l_a + beta l_b,
+ * o = alpha o_a + beta o_b): it needs l and o relative to their m, not m
+ * to be the true max.  (The fp32 kernel keeps the true running max.)
  *
  * Positions for the causal mask come from mask_desc: contiguous
  * pos_q(i) = q_rank*Lq + i, pos_k(j) = kv_rank*Lkv + j; striped
@@ -238,6 +258,14 @@ const char* ra_version(void);
  * of about `copy_us` on the copy stream before each staging copy (0 = none,
  * at most 100000).  Results must not change; only the timeline does. */
 ra_status ra_debug_set_delays(int compute_us, int copy_us);
+/* Counter calibration: launches `workgroups` workgroups of four waves on
+ * `stream`, each wave issuing iters x 8 independent bf16 MFMAs
+ * (v_mfma_f32_32x32x16_bf16, 32768 FLOPs each) from registers, and writes
+ * the total MFMA count to *mfma_count.  Reads and writes no memory.  A
+ * profiler's MFMA counters for this launch divided by that count give the
+ * counters' scale; its duration gives the MFMA rate reached in practice.
+ * workgroups in [1, 2^20], iters in [1, 2^24], else RA_EINVAL. */
+ra_status ra_diag_mfma_loop(int workgroups, int iters, void* stream, double* mfma_count);
 ra_status ra_prof_enable(int on);
 ra_status ra_prof_reset(void);
 ra_status ra_prof_read(double* out6);

@@ -34,19 +34,48 @@ def host_vals(x: np.ndarray, dtype: str) -> np.ndarray:
     return synth.as_f32(x, dtype)
 
 
-def max_err(a, b) -> float:
-    a = np.asarray(a, dtype=np.float64)
-    b = np.asarray(b, dtype=np.float64)
-    both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
-    d = np.where(both_inf, 0.0, np.abs(a - b))
-    return float(np.nanmax(d)) if d.size else 0.0
+def max_err(got, want) -> float:
+    """Largest |got - want| over every element.
+
+    NaN anywhere in `got` makes the error infinite, as does an infinity in
+    `got` that `want` does not have (same sign) and vice versa; matching
+    infinities (the -inf lse of a row with no visible key) count as 0.
+    `want` must be fully evaluated: an oracle called on a row or head sample
+    leaves the other entries NaN, and the caller indexes those out first.
+    """
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    if got.shape != want.shape:
+        raise AssertionError(f"shape mismatch: got {got.shape}, want {want.shape}")
+    if np.isnan(want).any():
+        raise ValueError("expected values hold NaN: index out the rows / heads the oracle did not evaluate")
+    if got.size == 0:
+        return 0.0
+    if np.isnan(got).any():
+        return float("inf")
+    same_inf = np.isinf(got) & np.isinf(want) & (np.sign(got) == np.sign(want))
+    with np.errstate(invalid="ignore"):
+        d = np.where(same_inf, 0.0, np.abs(got - want))
+    return float(d.max())
 
 
 def assert_close(got_o, got_lse, want_o, want_lse, dtype: str, what: str = ""):
+    """O and lse against the oracle at the tolerance of `dtype`.
+
+    O must be finite everywhere; lse must be finite exactly where the
+    oracle's is and -inf exactly where the oracle's is (a row with no
+    visible key); NaN anywhere fails.
+    """
     to, tl = TOL[dtype]
+    got_o = np.asarray(got_o, dtype=np.float64)
+    got_lse = np.asarray(got_lse, dtype=np.float64)
+    want_lse = np.asarray(want_lse, dtype=np.float64)
+    assert np.all(np.isfinite(got_o)), f"{what}: non-finite output"
+    assert not np.isnan(got_lse).any(), f"{what}: NaN in lse"
+    assert np.array_equal(np.isfinite(got_lse), np.isfinite(want_lse)), f"{what}: lse finite pattern differs"
+    assert np.array_equal(np.isneginf(got_lse), np.isneginf(want_lse)), f"{what}: lse -inf pattern differs"
     eo = max_err(got_o, want_o)
     el = max_err(got_lse, want_lse)
-    assert np.all(np.isfinite(got_o)), f"{what}: non-finite output"
     assert eo <= to and el <= tl, f"{what}: max|dO|={eo:.3e} (tol {to}) max|dlse|={el:.3e} (tol {tl})"
     return eo, el
 

@@ -38,15 +38,84 @@ def test_version(lib):
     assert b"gfx950" in lib.ra_version()
 
 
+SIZE_MAX = (1 << 64) - 1
+
+
 def test_ws_bytes():
     # C2: two staging buffers of K+V (bf16) plus fp32 m, l, o
     B, H, N, d, P = 1, 32, 32768, 128, 8
     kv = B * H * N * d * 2
     state = B * H * N * 4 * 2 + B * H * N * d * 4
     assert ra.ring_attn_fwd_ws_bytes(B, H, H, N, d, P, ra.RA_BF16) == 4 * kv + state
-    assert ra.ring_attn_fwd_ws_bytes(B, H, H, N, d, 1, ra.RA_BF16) == 0
-    assert ra.load().ring_attn_fwd_ws_bytes(B, H, H, N + 1, d, P, ra.RA_BF16) == 0
+    assert ra.ring_attn_fwd_ws_bytes(B, H, H, N, d, 1, ra.RA_BF16) == 0  # valid, nothing to stage
     assert ra.load().ring_attn_decode_ws_bytes(16, 32, 8, 262144, 128, 8) > 0
+
+
+@pytest.mark.parametrize("args,frag", [
+    ((1, 32, 32, 32768 + 1, 128, 8, 1), "multiple of P"),
+    ((1, 32, 32, 32768, 96, 8, 1), "64 or 128"),
+    ((1, 3, 2, 32768, 128, 8, 1), "multiple of Hkv"),
+    ((1, 32, 32, 32768, 128, 8, 7), "dtype"),
+    ((0, 32, 32, 32768, 128, 8, 1), ">= 1"),
+    ((1, 32, 32, 32768, 128, 0, 1), "P must be"),
+    ((1, 1, 1, 8 << 24, 128, 8, 1), "below 2 GiB"),  # one 2^24-row bf16 block is 4 GiB
+])
+def test_ws_queries_flag_invalid_arguments(lib, args, frag):
+    """Invalid arguments give SIZE_MAX (not 0, which means 'no workspace
+    needed') with the launch's own message."""
+    assert lib.ring_attn_fwd_ws_bytes(*args) == SIZE_MAX
+    assert frag in lib.ra_last_error().decode()
+    assert lib.ring_attn_fwd_share_ws_bytes(*args) == SIZE_MAX
+    with pytest.raises(ra.RingAttnError):
+        ra.ring_attn_fwd_ws_bytes(*args)
+
+
+def test_other_ws_queries_flag_invalid_arguments(lib):
+    assert lib.ring_attn_bwd_ws_bytes(1, 2, 1, 64, 64, 4, ra.RA_F32) == SIZE_MAX
+    assert b"bf16 only" in lib.ra_last_error()
+    assert lib.ring_attn_bwd_ws_bytes(1, 2, 1, 65, 64, 4, ra.RA_BF16) == SIZE_MAX
+    assert lib.ring_attn_bwd_ws_bytes(1, 1, 1, 1 << 24, 128, 8, ra.RA_BF16) == SIZE_MAX  # 4 GiB plane
+    assert b"below 2 GiB" in lib.ra_last_error()
+    assert lib.ring_attn_decode_ws_bytes(1, 32, 1, 64, 64, 4) == SIZE_MAX  # group of 32 > 16
+    assert lib.ring_attn_decode_ws_bytes(1, 4, 1, 66, 64, 4) == SIZE_MAX
+    with pytest.raises(ra.RingAttnError):
+        ra.ring_attn_decode_ws_bytes(1, 4, 1, 66, 64, 4)
+
+
+def test_ws_queries_report_sizes_beyond_the_address_space(lib):
+    """B*H*N*d*4 bytes past 2^48 (the device's virtual address width) or past
+    2^64: SIZE_MAX from the query, RA_ENOMEM from the launch."""
+    B, H, N, d, P = 1 << 20, 1 << 10, 1 << 28, 128, 64
+    assert lib.ring_attn_fwd_ws_bytes(B, H, H, N, d, P, ra.RA_BF16) == SIZE_MAX
+    assert b"address space" in lib.ra_last_error()
+    with pytest.raises(ra.RingAttnError) as e:
+        ra.ring_attn_fwd_ws_bytes(B, H, H, N, d, P, ra.RA_BF16)
+    assert e.value.status == ra.RA_ENOMEM
+    st = lib.ring_attn_fwd(256, 256, 256, 256, 256, B, H, H, N, d, P, 1, 0, 0.1, ra.RA_BF16, None, 256, 1 << 40)
+    assert st == ra.RA_ENOMEM and b"address space" in lib.ra_last_error()
+    st = lib.ring_attn_bwd(256, 256, 256, 256, 256, 256, 256, 256, 256, 1 << 20, 1 << 12, 1 << 12, 1 << 22, 128, 8,
+                           1, 0, 0.1, ra.RA_BF16, None, 256, 1 << 40)
+    assert st == ra.RA_ENOMEM
+    assert lib.ring_attn_decode_ws_bytes(1 << 20, 1 << 16, 1 << 12, 64 * 128, 128, 64) == SIZE_MAX
+    assert b"address space" in lib.ra_last_error()
+
+
+def test_large_planes_are_accepted_where_the_kernels_allow():
+    """A 9,437,184-token kv plane (2.4 GB per head in bf16) passes the
+    argument checks of the forward (contiguous, striped: its first step is
+    staged), the share and decode; they stop at the workspace check here."""
+    lib = ra.load()
+    N, d, P = 9437184, 128, 8
+    for layout in (0, 1, 2):
+        st = lib.ring_attn_fwd(256, 256, 256, 256, 256, 1, 1, 1, N, d, P, 1, layout, 0.1, ra.RA_BF16, None, 256, 16)
+        assert st == ra.RA_EINVAL and b"workspace too small" in lib.ra_last_error(), layout
+        st = lib.ring_attn_fwd_share(256, 256, 256, 256, 256, 1, 1, 1, N, d, P, 7, 1, layout, 0.1, ra.RA_BF16,
+                                     None, 256, 16)
+        assert st == ra.RA_EINVAL and b"workspace too small" in lib.ra_last_error(), layout
+    st = lib.ring_attn_decode(256, 256, 256, 256, 256, 1, 4, 1, N, d, P, 0.1, ra.RA_BF16, None, 256, 16)
+    assert st == ra.RA_EINVAL and b"workspace too small" in lib.ra_last_error()
+    assert 0 < lib.ring_attn_decode_ws_bytes(1, 4, 1, N, d, P) < SIZE_MAX
+    assert 0 < lib.ring_attn_fwd_share_ws_bytes(1, 1, 1, N, d, P, ra.RA_BF16) < SIZE_MAX
 
 
 def _fwd(lib, **kw):
@@ -195,3 +264,80 @@ def test_merge_and_finalize_of_zero_rows_are_no_ops(lib):
     assert lib.ring_attn_finalize(None, None, None, None, None, 0, 128, 1, None) == ra.RA_OK
     assert lib.lse_merge(None, None, None, None, -1, 8, None) == ra.RA_EINVAL
     assert lib.ring_attn_finalize(None, None, None, None, None, 0, 128, 9, None) == ra.RA_EINVAL
+
+
+# ---------------------------------------------------------------------------
+# The Python binding checks every tensor before a pointer reaches the
+# library: dtype, exact shape and contiguity first, then the device.
+# (Host tensors here: each case must fail on the property it breaks.)
+# ---------------------------------------------------------------------------
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def test_binding_rejects_bad_forward_arguments():
+    import torch
+    q, k, v = _t(1, 4, 64, 64), _t(1, 2, 64, 64), _t(1, 2, 64, 64)
+    with pytest.raises(TypeError, match="k must be"):
+        ra.ring_attn_fwd(q, k.float(), v, P=4, causal=True)
+    with pytest.raises(ValueError, match="v must have shape"):
+        ra.ring_attn_fwd(q, k, _t(1, 2, 64, 128), P=4, causal=True)
+    with pytest.raises(ValueError, match="out must have shape"):
+        ra.ring_attn_fwd(q, k, v, P=4, causal=True, out=_t(1, 4, 32, 64))
+    with pytest.raises(TypeError, match="out must be"):
+        ra.ring_attn_fwd(q, k, v, P=4, causal=True, out=_t(1, 4, 64, 64, dtype=torch.float32))
+    with pytest.raises(TypeError, match="lse must be"):
+        ra.ring_attn_fwd(q, k, v, P=4, causal=True, lse=_t(1, 4, 64))
+    with pytest.raises(ValueError, match="lse must have shape"):
+        ra.ring_attn_fwd(q, k, v, P=4, causal=True, lse=_t(1, 4, 65, dtype=torch.float32))
+    with pytest.raises(ValueError, match="contiguous"):
+        ra.ring_attn_fwd(q, k, v, P=4, causal=True, out=_t(1, 4, 64, 64).transpose(2, 3))
+    with pytest.raises(ValueError, match="device tensor"):
+        ra.ring_attn_fwd(q, k, v, P=4, causal=True)
+    with pytest.raises(ValueError, match="q must hold N / P rows"):
+        ra.ring_attn_fwd_share(_t(1, 4, 32, 64), k, v, P=4, rank=3, causal=True)
+
+
+def test_binding_rejects_bad_step_merge_finalize_decode_backward_arguments():
+    import torch
+    f32 = torch.float32
+    q, k, v = _t(1, 2, 16, 64), _t(1, 1, 16, 64), _t(1, 1, 16, 64)
+    m, l, o = _t(1, 2, 16, dtype=f32), _t(1, 2, 16, dtype=f32), _t(1, 2, 16, 64, dtype=f32)
+    with pytest.raises(TypeError, match="o must be"):
+        ra.ring_attn_step(q, k, v, m, l, o.bfloat16(), causal=True)
+    with pytest.raises(ValueError, match="m must have shape"):
+        ra.ring_attn_step(q, k, v, _t(1, 2, 15, dtype=f32), l, o, causal=True)
+    with pytest.raises(ValueError, match="device tensor"):
+        ra.ring_attn_step(q, k, v, m, l, o, causal=True)
+    with pytest.raises(TypeError, match="o_a must be"):
+        ra.lse_merge(o.bfloat16(), m, o, l)
+    with pytest.raises(ValueError, match="lse_b must have shape"):
+        ra.lse_merge(o, m, o.clone(), _t(1, 2, 17, dtype=f32))
+    with pytest.raises(ValueError, match="device tensor"):
+        ra.lse_merge(o, m, o.clone(), l)
+    with pytest.raises(ValueError, match="l must have shape"):
+        ra.ring_attn_finalize(m, _t(2, 16, dtype=f32), o)
+    with pytest.raises(ValueError, match="out must have shape"):
+        ra.ring_attn_finalize(m, l, o, out=_t(1, 2, 16, 32))
+    with pytest.raises(ValueError, match="device tensor"):
+        ra.ring_attn_finalize(m, l, o)
+    qd, kd, vd = _t(2, 8, 1, 128), _t(2, 2, 256, 128), _t(2, 2, 256, 128)
+    with pytest.raises(ValueError, match=r"\[B, H, 1, d\]"):
+        ra.ring_attn_decode(_t(2, 8, 2, 128), kd, vd, P=2)
+    with pytest.raises(TypeError, match="v must be"):
+        ra.ring_attn_decode(qd, kd, vd.float(), P=2)
+    with pytest.raises(ValueError, match="lse must have shape"):
+        ra.ring_attn_decode(qd, kd, vd, P=2, lse=_t(2, 8, 1, dtype=f32))
+    with pytest.raises(ValueError, match="device tensor"):
+        ra.ring_attn_decode(qd, kd, vd, P=2)
+    qb, kb = _t(1, 2, 64, 64), _t(1, 1, 64, 64)
+    lse = _t(1, 2, 64, dtype=f32)
+    with pytest.raises(ValueError, match="dk must have shape"):
+        ra.ring_attn_bwd(qb, kb, kb, qb, qb, lse, P=4, causal=True, dk=_t(1, 2, 64, 64))
+    with pytest.raises(TypeError, match="lse must be"):
+        ra.ring_attn_bwd(qb, kb, kb, qb, qb, lse.bfloat16(), P=4, causal=True)
+    with pytest.raises(TypeError, match="bfloat16 only"):
+        ra.ring_attn_bwd(qb.float(), kb.float(), kb.float(), qb.float(), qb.float(), lse, P=4, causal=True)
+    with pytest.raises(ValueError, match="device tensor"):
+        ra.ring_attn_bwd(qb, kb, kb, qb, qb, lse, P=4, causal=True)

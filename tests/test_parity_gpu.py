@@ -311,3 +311,37 @@ def test_decode_P1_equals_P8():
     torch.cuda.synchronize()
     assert max_err(from_dev(r1[0]), from_dev(r8[0])) <= 1e-2
     assert max_err(from_dev(r1[1]), from_dev(r8[1])) <= 1e-4
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_step_states_merge_by_the_pages_update(dtype):
+    """Two ring_attn_step states over disjoint kv blocks, merged on the host
+    by the [TKG] §3 update (m_new = max(m_a, m_b), alpha = e^(m_a - m_new),
+    beta = e^(m_b - m_new), l = alpha l_a + beta l_b, o = alpha o_a + beta
+    o_b), give the attention over both blocks: the stored m (a reference
+    max, possibly below the true max) carries l and o consistently."""
+    import torch
+    B, H, Hkv, N, d, P = 1, 2, 1, 4 * 192, 128, 4
+    q, k, v = _case(14, B, H, Hkv, N, d, dtype)
+    pos = oracle.host_positions(N, P, "contiguous")
+    qr = 3
+    qb = np.ascontiguousarray(q[:, :, pos[qr]])
+    states = []
+    for kvr in (1, 3):
+        kb = np.ascontiguousarray(k[:, :, pos[kvr]])
+        vb = np.ascontiguousarray(v[:, :, pos[kvr]])
+        m, l, o = ra.init_state(B, H, N // P, d, "cuda:0")
+        ra.ring_attn_step(to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype), m, l, o, causal=True,
+                          layout="contiguous", P=P, q_rank=qr, kv_rank=kvr)
+        torch.cuda.synchronize()
+        states.append(tuple(from_dev(t).astype(np.float64) for t in (m, l, o)))
+    (ma, la, oa), (mb, lb, ob) = states
+    m_new = np.maximum(ma, mb)
+    alpha, beta = np.exp(ma - m_new), np.exp(mb - m_new)
+    l_new = alpha * la + beta * lb
+    o_new = alpha[..., None] * oa + beta[..., None] * ob
+    kp = np.concatenate([pos[1], pos[3]])
+    ks = np.concatenate([host_vals(k, dtype)[:, :, pos[r]] for r in (1, 3)], axis=2)
+    vs = np.concatenate([host_vals(v, dtype)[:, :, pos[r]] for r in (1, 3)], axis=2)
+    Ow, Lw = oracle.attention(host_vals(qb, dtype), ks, vs, causal=True, q_pos=pos[qr], k_pos=kp)
+    assert_close(o_new / l_new[..., None], m_new + np.log(l_new), Ow, Lw, dtype, "pages' merge of two states")
