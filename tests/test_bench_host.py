@@ -53,7 +53,27 @@ def test_overlap_summary_on_a_synthetic_trace(tmp_path):
     out = tmp_path / "s.md"
     prof_summary.overlap(str(d), str(out), "cmd")
     text = out.read_text()
-    assert "| step kernels | 2 |" in text
+    assert "| compute kernels | 2 |" in text
     assert "| compute stream idle | 10.00% |" in text          # 2 of 20 ns
     assert "| staging copy kernels | 1," in text               # the copy at 30 is outside the window
-    assert "| copy time under a step kernel | 80.0% |" in text  # [5,10) and [12,15) of [5,15)
+    assert "| copy time under a compute kernel | 80.0% |" in text  # [5,10) and [12,15) of [5,15)
+
+
+def test_overlap_summary_of_other_compute_kernels(tmp_path):
+    """Without a decode kernel the window spans every listed compute kernel
+    (here the two backward kernels)."""
+    from blockwise_ring_attention_attn_amd import prof_summary
+    d = tmp_path / "t"
+    d.mkdir()
+    rows = [("bwd_dkdv_kernel<128, 0>", 0, 10), ("bwd_dq_kernel<128, 0>", 10, 16), ("__amd_rocclr_copyBuffer", 2, 6),
+            ("bwd_dkdv_kernel<128, 0>", 20, 40)]
+    with open(d / "x_kernel_trace.csv", "w") as f:
+        f.write('"Kernel_Name","Start_Timestamp","End_Timestamp"\n')
+        for n, a, b in rows:
+            f.write(f'"{n}",{a},{b}\n')
+    out = tmp_path / "s.md"
+    prof_summary.overlap(str(d), str(out), "cmd", "bwd_dkdv_kernel,bwd_dq_kernel")
+    text = out.read_text()
+    assert "| compute kernels | 3 |" in text
+    assert "| compute stream idle | 10.00% |" in text          # [16,20) of [0,40)
+    assert "| copy time under a compute kernel | 100.0% |" in text
