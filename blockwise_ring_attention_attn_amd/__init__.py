@@ -24,7 +24,7 @@ EXPORTS = (
     "ring_attn_fwd_ws_bytes", "ring_attn_fwd",
     "ring_attn_fwd_share_ws_bytes", "ring_attn_fwd_share",
     "ring_attn_step", "ring_attn_finalize", "lse_merge",
-    "ring_attn_decode_ws_bytes", "ring_attn_decode",
+    "ring_attn_decode_ws_bytes", "ring_attn_decode", "ring_attn_decode_noalloc",
     "ring_attn_bwd_ws_bytes", "ring_attn_bwd",
     "ra_last_error", "ra_version", "ra_debug_set_delays", "ra_prof_enable", "ra_prof_reset", "ra_prof_read",
     "ra_diag_mfma_loop",
@@ -80,6 +80,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.ring_attn_decode_ws_bytes.restype = st
     lib.ring_attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, ll, i, i, f, i, vp, vp, st]
     lib.ring_attn_decode.restype = i
+    lib.ring_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, ll, i, i, f, i, vp]
+    lib.ring_attn_decode_noalloc.restype = i
     lib.ring_attn_bwd_ws_bytes.argtypes = [i, i, i, ll, i, i, i]
     lib.ring_attn_bwd_ws_bytes.restype = st
     lib.ring_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, ll, i, i, i, i, f, i, vp, vp, st]
@@ -394,6 +396,18 @@ def ring_attn_decode(q, k, v, *, P: int, scale: float | None = None, out=None, l
     wst = _workspace(nb, q, ws)
     _check(lib.ring_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, L, d, P, scale,
                                 code, _stream(stream), _ptr(wst) if wst is not None else None, nb))
+    return out, lse
+
+
+def ring_attn_decode_noalloc(q, k, v, *, P: int, scale: float | None = None, out=None, lse=None, stream=None):
+    """ring_attn_decode with the library's static scratch instead of a
+    workspace (no device allocation inside the call when out and lse are
+    given)."""
+    lib = load()
+    B, H, Hkv, L, d, code, out, lse = _decode_args(q, k, v, out, lse)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib.ring_attn_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, L, d, P, scale,
+                                        code, _stream(stream)))
     return out, lse
 
 

@@ -15,9 +15,20 @@
 // taken straight from the score registers.  Each wavefront writes one
 // normalized partial (O, lse); a second kernel merges the partials of each
 // ring block and then the ring blocks.
+#include <mutex>
+
 #include "ra_internal.h"
 
 namespace ra {
+
+// Static scratch of ring_attn_decode_noalloc (the per-wavefront partials
+// that ring_attn_decode keeps in the caller's workspace), for callers that
+// cannot allocate.  Each GPU the library runs on holds its own copy until
+// the process ends.  In host code `scratch` names a host-side stand-in:
+// kernels get the device address that hipGetSymbolAddress returns for it
+// (decode_scratch below), never the name itself.
+__device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -299,6 +310,29 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs A) {
 }
 
 }  // namespace
+
+hipError_t decode_scratch(void** ptr, size_t* bytes) {
+  // Looked up once per device, with that device current (the first call on
+  // it), and kept: every device holds the array at its own address.
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = kDecodeScratchBytes;
+  return hipSuccess;
+}
 
 hipError_t launch_decode_partial(const DecodeArgs& a, int d, int bf16, hipStream_t s) {
   if (!bf16) return hipErrorInvalidValue;

@@ -1034,6 +1034,24 @@ ra_status ring_attn_decode(const void* q, const void* k, const void* v, void* ou
   return decode_launch(q, k, v, out, lse, B, H, Hkv, L, d, P, scale, W, ws, stream);
 }
 
+ra_status ring_attn_decode_noalloc(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                                   int H, int Hkv, long long L, int d, int P, float scale, ra_dtype dtype,
+                                   void* stream) {
+  g_err.clear();
+  if (!q || !k || !v || !out || !lse) return fail(RA_EINVAL, "null tensor pointer");
+  ra_status st = decode_args(B, H, Hkv, L, d, P, dtype, scale);
+  if (st != RA_OK) return st;
+  const DecodeWs W = decode_ws_layout(B, H, Hkv, L, d, P);
+  if (W.overflow || W.total > kDecodeScratchBytes)
+    return fail(RA_EINVAL, "decode needs %zu bytes of scratch; the static scratch holds %zu (use ring_attn_decode "
+                "with a caller workspace)", W.total, kDecodeScratchBytes);
+  if ((st = check_tensor_align({q, k, v, out}, {lse})) != RA_OK) return st;
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  RA_HIP(decode_scratch(&scratch, &scratch_bytes), "hipGetSymbolAddress(decode scratch)");
+  return decode_launch(q, k, v, out, lse, B, H, Hkv, L, d, P, scale, W, scratch, stream);
+}
+
 ra_status ra_debug_set_delays(int compute_us, int copy_us) {
   if (compute_us < 0 || copy_us < 0 || compute_us > 100000 || copy_us > 100000)
     return fail(RA_EINVAL, "delays must be in [0, 100000] us");

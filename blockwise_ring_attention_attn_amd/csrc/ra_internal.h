@@ -106,6 +106,11 @@ hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, int out_bf16, hipStream_t s);
 hipError_t launch_decode_partial(const DecodeArgs& a, int d, int bf16, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs& a, int d, int bf16, hipStream_t s);
+// Size of the static decode scratch (ring_attn_decode_noalloc).
+constexpr size_t kDecodeScratchBytes = 64ull << 20;
+// Device address and size of the static decode scratch on the current
+// device (looked up with hipGetSymbolAddress on the first call per device).
+hipError_t decode_scratch(void** ptr, size_t* bytes);
 hipError_t launch_spin(int microseconds, hipStream_t s);  // bounded busy wait (test hook)
 // Counter calibration: `workgroups` x 4 waves, each issuing iters x 8 bf16
 // 32x32x16 MFMAs from registers; *mfma_count receives the total issued.

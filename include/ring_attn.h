@@ -206,6 +206,21 @@ ra_status ring_attn_decode(const void* q, const void* k, const void* v, void* ou
                            int B, int H, int Hkv, long long L, int d, int P, float scale,
                            ra_dtype dtype, void* stream, void* ws, size_t ws_bytes);
 
+/* ring_attn_decode_noalloc -- ring_attn_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same kernels and results
+ * (bit for bit), with the partials in a static device array of the library
+ * (64 MiB, held on every GPU the library runs on until the process ends)
+ * instead of a caller workspace.  Allocates nothing.  Arguments as for
+ * ring_attn_decode; RA_EINVAL when the partials would need more than the
+ * 64 MiB (ring_attn_decode_ws_bytes(...) > 64 MiB; e.g. 16 sequences x 32
+ * heads x 262144 keys need 34 MB).  The partials are fully rewritten by
+ * every call, so nothing needs clearing; calls that overlap on one GPU
+ * (different streams, or threads) race on the shared array. */
+ra_status ring_attn_decode_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                                   int B, int H, int Hkv, long long L, int d, int P, float scale,
+                                   ra_dtype dtype, void* stream);
+
 /* ------------------------------------------------------------------------
  * ring_attn_bwd -- gradients of ring_attn_fwd by recomputation over a
  * reverse ring ([TKG] §7, "활성화 체크포인팅과 메모리 재연산": keep the

@@ -341,3 +341,16 @@ def test_binding_rejects_bad_step_merge_finalize_decode_backward_arguments():
         ra.ring_attn_bwd(qb.float(), kb.float(), kb.float(), qb.float(), qb.float(), lse, P=4, causal=True)
     with pytest.raises(ValueError, match="device tensor"):
         ra.ring_attn_bwd(qb, kb, kb, qb, qb, lse, P=4, causal=True)
+
+
+def test_decode_noalloc_rejects_what_the_static_scratch_cannot_hold(lib):
+    """ring_attn_decode_noalloc keeps its partials in a 64 MiB static array:
+    a problem whose partials need more is refused before any device call
+    (64 sequences x 16 heads x 1024 partials x 129 floats)."""
+    need = ra.ring_attn_decode_ws_bytes(64, 16, 16, 64 * 4096, 128, 64)
+    assert need > 64 << 20
+    st = lib.ring_attn_decode_noalloc(256, 256, 256, 256, 256, 64, 16, 16, 64 * 4096, 128, 64, 0.1, ra.RA_BF16, None)
+    assert st == ra.RA_EINVAL and b"static scratch" in lib.ra_last_error()
+    # and the decode workload of 16 sequences x 262144 keys fits (34 MB)
+    assert ra.ring_attn_decode_ws_bytes(16, 32, 8, 262144, 128, 8) <= 64 << 20
+    assert lib.ring_attn_decode_noalloc(None, 1, 1, 1, 1, 16, 32, 8, 262144, 128, 8, 0.1, ra.RA_BF16, None) == ra.RA_EINVAL
