@@ -1,26 +1,26 @@
 #!/usr/bin/env python3
 """Benchmark: blockwise ring attention on one MI355X.
 
-One step = one ring_attn_fwd call over the whole causal prefill workload
-(bf16, B=1, H=32, N=32768, d=128, contiguous layout, P=8 virtual hosts,
-all ring steps with the staging copies on the second stream), inputs already
+One step = one ring_attn_fwd_share call on the largest single-GPU forward
+workload: rank 7's share of a 1,048,576-token causal ring (bf16, H=4,
+d=128, P=8): its 131072 resident queries against all eight kv blocks in
+ring order, each next block staged on the second stream.  Inputs are
 resident in HBM.  Prints ONE JSON line:
   value        causal-adjusted TFLOP/s of the whole call (4 d FLOPs per
-               unmasked query/key pair per query head)
-  roofline     the fused step kernel: algorithmic FLOPs per launch / mean
-               launch time (HIP events on the compute stream) vs the bf16
-               dense MFMA peak
+               unmasked query/key pair per query head), timed with HIP events
+               on the caller's stream and the library's own kernel timing off
+  roofline     the fused step kernel in a separate pass: algorithmic FLOPs per
+               launch / mean launch time (HIP events on the compute stream)
+               vs the bf16 dense MFMA peak; traffic and mfma_busy from the
+               committed counter summaries (null once the kernel changed)
   cpu_baseline the fp64 oracle on a bounded row sample of the same workload
+  prefill_32k  the causal contiguous ring B=1 H=32 N=32768 P=8 (whole call,
+               roofline, cpu_baseline)
+  striped_gqa  the causal striped GQA ring H=8/Hkv=2 N=131072 P=8 (same)
   decode       split-KV decode (16 sequences, H=32/Hkv=8, L=262144, d=128,
                P=8): algorithmic HBM GB/s, with its kernel's roofline
-  backward     ring_attn_bwd on the prefill workload (reverse ring,
-               recomputation): TFLOP/s at 10 d FLOPs per unmasked pair per
-               query head (the five products QK^T, dO V^T, P^T dO, dS K,
-               dS^T Q)
-  striped_gqa  the striped GQA ring (bf16 H=8/Hkv=2, N=131072, P=8):
-               TFLOP/s of the whole call
-  share_1m     rank 7's share of a 1,048,576-token causal ring (bf16 H=4):
-               TFLOP/s of the whole call
+  backward     ring_attn_bwd on the 32k prefill workload: TFLOP/s at 10 d
+               FLOPs per unmasked pair per query head
 """
 from __future__ import annotations
 
@@ -69,6 +69,31 @@ def measured_traffic(kernel: str, source: str):
     return rec.get("bytes_per_launch")
 
 
+def measured_mfma_busy(key: str, source: str):
+    """MFMA-busy fraction of the kernel on a workload from the committed
+    counter summary (profiles/mfma.json), or None if its source changed."""
+    try:
+        rec = json.load(open(os.path.join(PROFILES, "mfma.json")))[key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_sha(source):
+        return None
+    return {"busy": rec.get("mfma_busy"), "busy_rel_calibration_loop": rec.get("mfma_busy_rel_calibration"),
+            "clock_ghz": rec.get("gui_clock_ghz")}
+
+
+def host_cpu():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"os_cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
 def calibration_copy(mib: int) -> None:
     """A plain device-to-device copy of known size, for counter calibration."""
     import torch
@@ -110,103 +135,55 @@ def upload(x, dtype):
     return torch.from_numpy(x).to("cuda:0")
 
 
-def cpu_baseline(c, q, k, v, budget_s: float = 12.0) -> dict:
-    """The fp64 oracle, as it is, on a seeded sample of query rows."""
+def cpu_baseline(c, q, k, v, budget_s: float, share: bool) -> dict:
+    """The fp64 oracle, as it is, on a seeded sample of query rows of the
+    workload (two heads, uniformly random rows, each against all the keys
+    it sees), timed on the host cores; FLOP/s at the same 4 d per pair."""
     import numpy as np
     import oracle
     import synth
     cores = len(os.sched_getaffinity(0))
     rng = np.random.default_rng(c["seed"])
-    heads = [(0, h) for h in (0, c["H"] // 2)]
-    qf = synth.as_f32(q[:, :c["H"]], "bf16")
-    kf = synth.as_f32(k, "bf16")
-    vf = synth.as_f32(v, "bf16")
-    n_rows = 64
-    elapsed, flops, rows_done = 0.0, 0.0, 0
+    group = c["H"] // c["Hkv"]
+    hs = sorted({0, c["H"] // 2})
+    # local heads: query head i of the sample reads kv head i (its own group's)
+    kv_of = [h // group for h in hs]
+    qf = synth.as_f32(q[:, hs], "bf16")
+    kf = synth.as_f32(k[:, kv_of], "bf16")
+    vf = synth.as_f32(v[:, kv_of], "bf16")
+    Nq = q.shape[2]
+    q_pos = (oracle.host_positions(c["N"], c["P"], c["layout"])[c["rank"]] if share else np.arange(Nq))
+    n_rows, elapsed, flops, rows_done = 16, 0.0, 0.0, 0
     while True:
-        rows = np.sort(rng.integers(0, c["N"], n_rows))
+        rows = np.sort(rng.integers(0, Nq, n_rows))
         t0 = time.perf_counter()
-        oracle.attention(qf, kf, vf, causal=True, rows=rows, heads=heads, threads=cores)
+        oracle.attention(qf, kf, vf, causal=c["causal"], q_pos=q_pos, rows=rows,
+                         heads=[(0, i) for i in range(len(hs))], threads=cores)
         dt = time.perf_counter() - t0
         elapsed += dt
-        flops += 4.0 * c["d"] * float((rows + 1).sum()) * len(heads)
-        rows_done += n_rows * len(heads)
+        flops += 4.0 * c["d"] * float((q_pos[rows] + 1).sum()) * len(hs)
+        rows_done += n_rows * len(hs)
         if elapsed >= budget_s:
             break
-        n_rows = int(min(4096, max(n_rows * 2, n_rows * (budget_s - elapsed) / max(dt, 1e-3) * 0.5)))
+        n_rows = int(min(8192, max(n_rows * 2, n_rows * (budget_s - elapsed) / max(dt, 1e-3) * 0.5)))
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{rows_done} query rows (heads 0 and {c['H'] // 2}, uniformly random positions, "
-                      f"causal prefix of each row) of the prefill workload, fp64, {elapsed:.1f} s",
-            "seconds": elapsed}
+            "sample": f"{rows_done} query rows (heads {hs}, uniformly random rows, each against every key it "
+                      f"sees) of this workload, fp64, {elapsed:.1f} s", "seconds": elapsed, **host_cpu()}
 
 
-def run_prefill(args) -> dict:
-    import torch
-    import blockwise_ring_attention_attn_amd as ra
-    import synth
-    c = PREFILL
-    q, k, v = synth.qkv(c["seed"], c["B"], c["H"], c["Hkv"], c["N"], c["d"], "bf16")
-    qd, kd, vd = upload(q, "bf16"), upload(k, "bf16"), upload(v, "bf16")
-    out = torch.empty_like(qd)
-    lse = torch.empty((c["B"], c["H"], c["N"]), dtype=torch.float32, device="cuda:0")
-    nb = ra.ring_attn_fwd_ws_bytes(c["B"], c["H"], c["Hkv"], c["N"], c["d"], c["P"], ra.RA_BF16)
-    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda:0")
-    stream = torch.cuda.current_stream()
-
-    def step():
-        ra.ring_attn_fwd(qd, kd, vd, P=c["P"], causal=c["causal"], layout=c["layout"], out=out, lse=lse,
-                         ws=ws, stream=stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ra.prof_enable(True)
-    ra.prof_reset()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    prof = ra.prof_read()
-    ra.prof_enable(False)
-    ms = ev0.elapsed_time(ev1) / args.steps
-    flops = prefill_flops(c)
-    tflops = flops / (ms * 1e-3) / 1e12
-    launches = prof["step_launches"]
-    kern_ms = prof["step_ms"] / max(1, launches)
-    achieved = prof["step_flops"] / (prof["step_ms"] * 1e-3) / 1e12 if prof["step_ms"] > 0 else 0.0
-    res = {
-        "value": tflops, "ms_per_step": ms, "wall_s": wall, "flops": flops,
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": measured_traffic("step_bf16_kernel<128>", "attn_step.hip"),
-                     "kernel": "step_bf16_kernel<128>", "launches_per_step": launches / args.steps,
-                     "mean_launch_ms": kern_ms,
-                     "flops_per_launch": prof["step_flops"] / max(1, launches)},
-    }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(c, q, k, v, args.cpu_seconds)
-    del qd, kd, vd, out, lse, ws
-    torch.cuda.empty_cache()
-    return res
-
-
-def run_forward_other(args, c, share: bool) -> dict:
-    """Throughput of one of the other full-size forward workloads (HIP events
-    around whole calls on the caller's stream; step-kernel launches timed on
-    the compute stream as for the headline workload)."""
+def run_forward(args, c, share: bool, key: str, cpu_seconds: float) -> dict:
+    """One full-size forward workload: whole calls timed with HIP events on
+    the caller's stream (library kernel timing off), then a separate pass
+    with the library's per-launch events for the step kernel's roofline."""
     import torch
     import blockwise_ring_attention_attn_amd as ra
     import synth
     B, H, Hkv, N, d, P = c["B"], c["H"], c["Hkv"], c["N"], c["d"], c["P"]
     Nq = N // P if share else N
-    qd = upload(synth.tensor(c["seed"], synth.TENSOR_Q, B, H, Nq, d, "bf16"), "bf16")
-    kd = upload(synth.tensor(c["seed"], synth.TENSOR_K, B, Hkv, N, d, "bf16"), "bf16")
-    vd = upload(synth.tensor(c["seed"], synth.TENSOR_V, B, Hkv, N, d, "bf16"), "bf16")
+    q = synth.tensor(c["seed"], synth.TENSOR_Q, B, H, Nq, d, "bf16")
+    k = synth.tensor(c["seed"], synth.TENSOR_K, B, Hkv, N, d, "bf16")
+    v = synth.tensor(c["seed"], synth.TENSOR_V, B, Hkv, N, d, "bf16")
+    qd, kd, vd = upload(q, "bf16"), upload(k, "bf16"), upload(v, "bf16")
     out = torch.empty_like(qd)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda:0")
     lib = ra.load()
@@ -224,39 +201,53 @@ def run_forward_other(args, c, share: bool) -> dict:
                              stream=stream)
 
     flops = share_flops(c) if share else prefill_flops(c)
-    step()
+    for _ in range(max(1, args.warmup)):
+        step()
     torch.cuda.synchronize()
-    # about 2 s of timed calls
-    t0 = time.perf_counter()
-    step()
-    torch.cuda.synchronize()
-    n = int(min(20, max(3, 2.0 / max(time.perf_counter() - t0, 1e-3))))
-    ra.prof_enable(True)
-    ra.prof_reset()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(n):
+    for _ in range(args.steps):
         step()
     ev1.record(stream)
     torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    # roofline pass: the library brackets each step-kernel launch with events
+    n_prof = max(2, min(args.steps, int(2000.0 / max(ms, 1e-3))))
+    ra.prof_enable(True)
+    ra.prof_reset()
+    for _ in range(n_prof):
+        step()
+    torch.cuda.synchronize()
     prof = ra.prof_read()
     ra.prof_enable(False)
-    ms = ev0.elapsed_time(ev1) / n
-    tflops = flops / (ms * 1e-3) / 1e12
-    kern = prof["step_flops"] / (prof["step_ms"] * 1e-3) / 1e12 if prof["step_ms"] > 0 else 0.0
+    launches = prof["step_launches"]
+    achieved = prof["step_flops"] / (prof["step_ms"] * 1e-3) / 1e12 if prof["step_ms"] > 0 else 0.0
     del qd, kd, vd, out, lse, ws
     torch.cuda.empty_cache()
     if share:
-        what = (f"rank {c['rank']} of a P={P} causal ring over N={N}: q {Nq} tokens against all {N} keys, "
-                f"bf16 H={H} d={d}")
+        what = (f"rank {c['rank']}'s share of a P={P} causal {c['layout']} ring over N={N} tokens: its {Nq} "
+                f"queries against all {N} keys in ring order, bf16 B={B} H={H}/Hkv={Hkv} d={d}")
     else:
         what = f"causal {c['layout']} ring: bf16 B={B} H={H}/Hkv={Hkv} N={N} d={d}, P={P} virtual hosts"
-    return {"value": tflops, "unit": "TFLOP/s", "ms_per_step": ms, "steps": n, "flops_per_step": flops,
-            "pct_bf16_mfma_peak": 100.0 * tflops / MFMA_BF16_PEAK_TFLOPS,
-            "step_kernels": {"achieved": kern, "unit": "TFLOP/s", "frac": kern / MFMA_BF16_PEAK_TFLOPS,
-                             "launches_per_step": prof["step_launches"] / n,
-                             "ms_per_step": prof["step_ms"] / n},
-            "config": {"workload": what, **c}}
+    res = {
+        "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "ms_per_step": ms, "steps": args.steps,
+        "wall_s": wall, "flops_per_step": flops,
+        "pct_bf16_mfma_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": measured_traffic(f"step_bf16_kernel<128>:{key}", "attn_step.hip")
+                     if key != "prefill_32k" else measured_traffic("step_bf16_kernel<128>", "attn_step.hip"),
+                     "mfma_busy": measured_mfma_busy(f"step_bf16_kernel<128>:{key}", "attn_step.hip"),
+                     "kernel": "step_bf16_kernel<128>", "launches_per_step": launches / n_prof,
+                     "mean_launch_ms": prof["step_ms"] / max(1, launches),
+                     "flops_per_launch": prof["step_flops"] / max(1, launches), "timed_calls": n_prof},
+        "config": {"workload": what, **c},
+    }
+    if not args.no_cpu_baseline and cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(c, q, k, v, cpu_seconds, share)
+    return res
 
 
 def run_backward(args) -> dict:
@@ -352,6 +343,71 @@ def run_decode(args) -> dict:
     }
 
 
+def run_staging_cost(args) -> dict:
+    """What the staging copies cost the step kernels that run beside them:
+    the same forward calls with the ring exchange on (each step's kv blocks
+    copied into staging buffers on the second stream while the previous step
+    computes) and off (every block read in place, no copies), interleaved;
+    whole-call time and the step kernels' mean launch time (HIP events on the
+    compute stream)."""
+    import torch
+    import blockwise_ring_attention_attn_amd as ra
+    import synth
+    out = {}
+    for key, c, share in (("prefill_32k", PREFILL, False), ("share_1m", SHARE, True)):
+        B, H, Hkv, N, d, P = c["B"], c["H"], c["Hkv"], c["N"], c["d"], c["P"]
+        Nq = N // P if share else N
+        qd = upload(synth.tensor(c["seed"], synth.TENSOR_Q, B, H, Nq, d, "bf16"), "bf16")
+        kd = upload(synth.tensor(c["seed"], synth.TENSOR_K, B, Hkv, N, d, "bf16"), "bf16")
+        vd = upload(synth.tensor(c["seed"], synth.TENSOR_V, B, Hkv, N, d, "bf16"), "bf16")
+        o = torch.empty_like(qd)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda:0")
+        stream = torch.cuda.current_stream()
+
+        def step():
+            if share:
+                ra.ring_attn_fwd_share(qd, kd, vd, P=P, rank=c["rank"], causal=True, layout=c["layout"], out=o,
+                                       lse=lse, stream=stream)
+            else:
+                ra.ring_attn_fwd(qd, kd, vd, P=P, causal=True, layout=c["layout"], out=o, lse=lse, stream=stream)
+
+        step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        step()
+        torch.cuda.synchronize()
+        n = max(2, min(20, int(1.0 / max(time.perf_counter() - t0, 1e-3))))
+        res = {"on": [], "off": []}
+        try:
+            for rnd in range(6):
+                for mode in (("on", "off") if rnd % 2 == 0 else ("off", "on")):
+                    ra.debug_set_staging(mode == "on")
+                    ra.prof_enable(True)
+                    ra.prof_reset()
+                    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    ev0.record(stream)
+                    for _ in range(n):
+                        step()
+                    ev1.record(stream)
+                    torch.cuda.synchronize()
+                    prof = ra.prof_read()
+                    ra.prof_enable(False)
+                    res[mode].append((ev0.elapsed_time(ev1) / n, prof["step_ms"] / max(1, prof["step_launches"])))
+        finally:
+            ra.debug_set_staging(True)
+            ra.prof_enable(False)
+        med = lambda xs: sorted(xs)[len(xs) // 2]
+        on_call, off_call = med([x for x, _ in res["on"]]), med([x for x, _ in res["off"]])
+        on_k, off_k = med([y for _, y in res["on"]]), med([y for _, y in res["off"]])
+        out[key] = {"call_ms_staged": on_call, "call_ms_in_place": off_call,
+                    "step_kernel_ms_staged": on_k, "step_kernel_ms_in_place": off_k,
+                    "step_kernel_slowdown_pct": 100.0 * (on_k / off_k - 1.0),
+                    "call_slowdown_pct": 100.0 * (on_call / off_call - 1.0), "calls_per_sample": n}
+        del qd, kd, vd, o, lse
+        torch.cuda.empty_cache()
+    return out
+
+
 def run_mfma_calib(args) -> dict:
     """The library's register-only bf16 MFMA loop: MFMAs issued, duration and
     rate (the counter calibration run; its rate is the practical MFMA peak)."""
@@ -380,11 +436,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time on the headline workload")
+    ap.add_argument("--cpu-seconds-other", type=float, default=6.0,
+                    help="oracle time on each of the other two forward workloads")
     ap.add_argument("--no-other-forward", action="store_true",
-                    help="skip the striped GQA and 1M-share forward workloads")
+                    help="skip the 32k prefill and striped GQA forward workloads")
     ap.add_argument("--calib-iters", type=int, default=8192)
-    ap.add_argument("--only", choices=("prefill", "decode", "backward", "striped", "share", "mfma_calib"),
+    ap.add_argument("--only", choices=("prefill", "decode", "backward", "striped", "share", "mfma_calib",
+                                       "staging_cost"),
                     default=None,
                     help="run one workload only (profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -403,48 +462,51 @@ def main():
     if args.only == "mfma_calib":
         print(json.dumps(run_mfma_calib(args)), flush=True)
         return
+    if args.only == "staging_cost":
+        print(json.dumps(run_staging_cost(args)), flush=True)
+        return
     if args.only == "decode":
         print(json.dumps(run_decode(args)), flush=True)
         return
     if args.only == "backward":
         print(json.dumps(run_backward(args)), flush=True)
         return
-    if args.only in ("striped", "share"):
-        share = args.only == "share"
-        print(json.dumps(run_forward_other(args, SHARE if share else STRIPED, share)), flush=True)
+    if args.only in ("striped", "share", "prefill"):
+        c, share = {"striped": (STRIPED, False), "share": (SHARE, True), "prefill": (PREFILL, False)}[args.only]
+        key = {"striped": "striped_gqa", "share": "share_1m", "prefill": "prefill_32k"}[args.only]
+        print(json.dumps(run_forward(args, c, share, key, 0.0 if args.no_cpu_baseline else args.cpu_seconds)),
+              flush=True)
         return
-    pre = run_prefill(args)
-    c = PREFILL
+    head = run_forward(args, SHARE, True, "share_1m", args.cpu_seconds)
     line = {
         "metric": METRIC,
-        "value": pre["value"],
+        "value": head["value"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": pre["ms_per_step"],
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "causal prefill ring: bf16 B=1 H=32 N=32768 d=128, contiguous layout, "
-                               "P=8 virtual hosts (all ring steps, KV staging on a second stream)",
-                   "global_batch": c["B"], "seq_len": c["N"], "parallelism": "1 GPU, P=8 virtual ring hosts",
-                   **c},
-        "pct_bf16_mfma_peak": 100.0 * pre["value"] / MFMA_BF16_PEAK_TFLOPS,
-        "algorithmic_flops_per_step": pre["flops"],
-        "roofline": pre["roofline"],
+        "config": {**head["config"], "global_batch": SHARE["B"], "seq_len": SHARE["N"],
+                   "parallelism": "1 GPU: one device's share of a P=8 ring (the other 7 hosts' kv blocks staged "
+                                  "on a second stream)"},
+        "pct_bf16_mfma_peak": head["pct_bf16_mfma_peak"],
+        "algorithmic_flops_per_step": head["flops_per_step"],
+        "roofline": head["roofline"],
     }
-    if "cpu_baseline" in pre:
-        line["cpu_baseline"] = pre["cpu_baseline"]
-    if not args.no_decode and args.only is None:
+    if "cpu_baseline" in head:
+        line["cpu_baseline"] = head["cpu_baseline"]
+    if not args.no_other_forward:
+        line["prefill_32k"] = run_forward(args, PREFILL, False, "prefill_32k", args.cpu_seconds_other)
+        line["striped_gqa"] = run_forward(args, STRIPED, False, "striped_gqa", args.cpu_seconds_other)
+    if not args.no_decode:
         line["decode"] = run_decode(args)
-    if not args.no_backward and args.only is None:
+    if not args.no_backward:
         line["backward"] = run_backward(args)
-    if not args.no_other_forward and args.only is None:
-        line["striped_gqa"] = run_forward_other(args, STRIPED, False)
-        line["share_1m"] = run_forward_other(args, SHARE, True)
     print(json.dumps(line), flush=True)
 
 

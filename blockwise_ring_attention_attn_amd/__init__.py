@@ -27,7 +27,7 @@ EXPORTS = (
     "ring_attn_decode_ws_bytes", "ring_attn_decode", "ring_attn_decode_noalloc",
     "ring_attn_bwd_ws_bytes", "ring_attn_bwd",
     "ra_last_error", "ra_version", "ra_debug_set_delays", "ra_prof_enable", "ra_prof_reset", "ra_prof_read",
-    "ra_diag_mfma_loop",
+    "ra_diag_mfma_loop", "ra_debug_set_staging",
 )
 
 
@@ -98,6 +98,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.ra_prof_reset.restype = i
     lib.ra_prof_read.argtypes = [ctypes.POINTER(ctypes.c_double)]
     lib.ra_prof_read.restype = i
+    lib.ra_debug_set_staging.argtypes = [i]
+    lib.ra_debug_set_staging.restype = i
     lib.ra_diag_mfma_loop.argtypes = [i, i, vp, ctypes.POINTER(ctypes.c_double)]
     lib.ra_diag_mfma_loop.restype = i
     if path is None:
@@ -421,6 +423,11 @@ def diag_mfma_loop(workgroups: int, iters: int, stream=None) -> float:
     n = ctypes.c_double()
     _check(load().ra_diag_mfma_loop(int(workgroups), int(iters), _stream(stream), ctypes.byref(n)))
     return n.value
+
+
+def debug_set_staging(on: bool = True) -> None:
+    """Test / measurement hook: ring steps read their kv blocks in place (off) or staged (on, default)."""
+    _check(load().ra_debug_set_staging(int(bool(on))))
 
 
 def prof_enable(on: bool = True) -> None:

@@ -271,10 +271,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   const bool key_ok = my_key < A.Lkv;
   const int64_t kv_plane = (int64_t)w.b * A.Hkv + w.hkv;
   const int64_t key_row = key_ok ? nat_row<LAYOUT>(A, kv_plane, G.n_tok, w.kv_rank, my_key, A.Lkv) : 0;
+  // the key's K / V row: in place (its natural row) or in the host-major staging
+  const int64_t src_row =
+      G.kv_staged ? ((int64_t)w.q_rank * A.B * A.Hkv + kv_plane) * A.Lkv + (key_ok ? my_key : 0) : key_row;
 
   bf16x8 kf[KS], vf[KS];
-  load_row_frags<D>(kf, reinterpret_cast<const unsigned short*>(A.k), key_row, key_ok, half);
-  load_row_frags<D>(vf, reinterpret_cast<const unsigned short*>(A.v), key_row, key_ok, half);
+  load_row_frags<D>(kf, reinterpret_cast<const unsigned short*>(A.k), src_row, key_ok, half);
+  load_row_frags<D>(vf, reinterpret_cast<const unsigned short*>(A.v), src_row, key_ok, half);
 
   // first query row that sees any key of the workgroup (the limit is
   // non-decreasing in the row)
@@ -602,12 +605,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
   auto vbuf = [](auto I) { return slot_buf<6, decltype(I)::value % NSLOT, T::BYTES>(); };
   const LdsOffsets<D> off(lane);
   const int64_t kv_plane = (int64_t)w.b * A.Hkv + w.hkv;
-  const unsigned rec_rows = (unsigned)(G.n_tok * T::RB);
+  // K / V rows: in place, the plane of the natural-order arrays (block row j
+  // at its token's row); staged, the host's compact block (row j at j)
+  const bool staged = G.kv_staged != 0;
+  const int64_t kv_base = staged ? ((int64_t)w.q_rank * A.B * A.Hkv + kv_plane) * A.Lkv : kv_plane * G.n_tok;
+  const unsigned rec_rows = (unsigned)((staged ? (int64_t)A.Lkv : G.n_tok) * T::RB);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(A.k)) + kv_plane * G.n_tok * D, 0, rec_rows,
+      const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(A.k)) + kv_base * D, 0, rec_rows,
       0x00020000);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(A.v)) + kv_plane * G.n_tok * D, 0, rec_rows,
+      const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(A.v)) + kv_base * D, 0, rec_rows,
       0x00020000);
   // Lane l of load instruction i fills LDS slot 64 i + l of the tile: row
   // ROWS_PER_INSTR i + l / CPR, chunk slot l % CPR holding logical chunk
@@ -619,7 +626,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
       const int r = ins * ROWS_PER_INSTR + lane / T::CPR;
       const int q = lane % T::CPR;
       const int j = t * kRows + r;
-      const int voff = j < A.Lkv ? lrow<LAYOUT>(w.kv_rank, j, A.Lkv, A.P) * T::RB + 16 * (q ^ dswz<D>(r)) : (int)rec_rows;
+      const int src = staged ? j : lrow<LAYOUT>(w.kv_rank, j, A.Lkv, A.P);
+      const int voff = j < A.Lkv ? src * T::RB + 16 * (q ^ dswz<D>(r)) : (int)rec_rows;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kbuf(slot) + ins * 1024),
                                                16, voff, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vbuf(slot) + ins * 1024),

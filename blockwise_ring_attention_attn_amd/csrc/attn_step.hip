@@ -320,12 +320,13 @@ __global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
   // differ, not on their size.  A stored state keeps o scaled to o l / lb,
   // i.e. o / l is that normalized output.
   f32x16 oacc[T::NDB];
-  float m_run = kNegInf, l_run = 0.f, lb_run = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
+  float lbr[4] = {0.f, 0.f, 0.f, 0.f};  // running sums of the bf16 weights, four chains
   if (A.has_prev && row_ok) {
     const int64_t idx = q_row_index(A, w, my_row);
     m_run = A.m[idx] * kLog2e;
     l_run = half == 0 ? A.l[idx] : 0.f;
-    lb_run = l_run;
+    lbr[0] = l_run;
 #pragma unroll
     for (int db = 0; db < T::NDB; ++db)
 #pragma unroll
@@ -376,7 +377,6 @@ __global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
     constexpr bool DO_PV = decltype(do_pv_tag)::value;
     constexpr int NPAIR = 16;                        // packed pairs of P per tile
     constexpr int PAIRS_PER_STEP = NPAIR / NSTEP;    // 1 (d = 128) or 2 (d = 64)
-    float lbs[4] = {0.f, 0.f, 0.f, 0.f};
     const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
     // The wave in its MFMA phase wins instruction issue over the other
     // group's wave on the same SIMD (otherwise the older wave would).
@@ -402,16 +402,12 @@ __global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
         for (int q = 0; q < PAIRS_PER_STEP; ++q) {
           const int pr = t * PAIRS_PER_STEP + q;       // pair index: (kb, hc, element pair)
           const bf16x2 pair = {pk[pr >> 3][(pr >> 2) & 1][2 * (pr & 3)], pk[pr >> 3][(pr >> 2) & 1][2 * (pr & 3) + 1]};
-          lbs[pr & 3] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lbs[pr & 3], false);
-          asm volatile("" : "+v"(lbs[pr & 3]));   // stays at this step (not sunk into the next phase)
+          lbr[pr & 3] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lbr[pr & 3], false);
+          asm volatile("" : "+v"(lbr[pr & 3]));   // stays at this step (not sunk into the next phase)
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     });
-    if constexpr (DO_PV) {
-      lb_run += (lbs[0] + lbs[1]) + (lbs[2] + lbs[3]);
-      asm volatile("" : "+v"(lb_run));
-    }
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -447,7 +443,8 @@ __global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
     const float m_new = fmaxf(m_run, partner_max(mx) * c);
     const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run - m_new);
     l_run *= alpha;
-    lb_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lbr[i] *= alpha;
 #pragma unroll
     for (int db = 0; db < T::NDB; ++db)
 #pragma unroll
@@ -595,7 +592,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_bf16_kernel(StepArgs A) {
 
   // Combine the two halves' partial sums (they saw disjoint keys).
   const float l_tot = partner_sum(l_run);
-  const float lb_tot = partner_sum(lb_run);
+  const float lb_tot = partner_sum((lbr[0] + lbr[1]) + (lbr[2] + lbr[3]));
   if (!row_ok) return;
   const bool fin = w.q_rank >= A.fin_lo && w.q_rank < A.fin_hi;
   const int64_t idx = q_row_index(A, w, my_row);

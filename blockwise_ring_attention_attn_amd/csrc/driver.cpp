@@ -19,6 +19,7 @@
 //   compute(s)   waits for copy(s)
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <initializer_list>
@@ -74,6 +75,7 @@ struct DeviceCtx {
 std::mutex g_mu;
 DeviceCtx g_dev[kMaxDevices];
 int g_delay_compute_us = 0, g_delay_copy_us = 0;  // test hook (ra_debug_set_delays)
+bool g_staging = true;  // ring exchange through staging copies (ra_debug_set_staging)
 
 ra_status get_ctx(DeviceCtx** out) {
   int dev = 0;
@@ -527,15 +529,18 @@ ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, 
     a.o = reinterpret_cast<float*>(wsb + W.off_o);
   }
 
+  // With the exchange switched off (ra_debug_set_staging(0)) every step
+  // reads its blocks in place where the kernel can address them.
+  const bool staged = P > 1 && (g_staging || stage_own);
   auto kbuf = [&](int s) -> const void* {
-    return (s == 0 && !stage_own) ? k : static_cast<const void*>(wsb + W.off_stage[s & 1]);
+    return (s == 0 && !stage_own) || !staged ? k : static_cast<const void*>(wsb + W.off_stage[s & 1]);
   };
   auto vbuf = [&](int s) -> const void* {
-    return (s == 0 && !stage_own) ? v : static_cast<const void*>(wsb + W.off_stage[s & 1] + W.kv_bytes);
+    return (s == 0 && !stage_own) || !staged ? v : static_cast<const void*>(wsb + W.off_stage[s & 1] + W.kv_bytes);
   };
   const int64_t planes = (int64_t)B * Hkv;
 
-  if (P > 1) {
+  if (staged) {
     RA_HIP(hipEventRecord(ctx->fork, cs), "hipEventRecord");
     RA_HIP(hipStreamWaitEvent(ctx->copy, ctx->fork, 0), "hipStreamWaitEvent");
   }
@@ -549,7 +554,7 @@ ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, 
   }
   for (int s = 0; s < P; ++s) {
     // Copy stream: stage the blocks of step s + 1 while step s computes.
-    if (s + 1 < P) {
+    if (staged && s + 1 < P) {
       if (s >= 1) RA_HIP(hipStreamWaitEvent(ctx->copy, ctx->done[(s - 1) & 1], 0), "hipStreamWaitEvent");
       void* kd = wsb + W.off_stage[(s + 1) & 1];
       void* vd = wsb + W.off_stage[(s + 1) & 1] + W.kv_bytes;
@@ -569,12 +574,12 @@ ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, 
       RA_HIP(hipEventRecord(ctx->copied[(s + 1) & 1], ctx->copy), "hipEventRecord");
     }
     // Compute stream: step s.
-    if (s >= 1 || stage_own) RA_HIP(hipStreamWaitEvent(cs, ctx->copied[s & 1], 0), "hipStreamWaitEvent");
+    if (staged && (s >= 1 || stage_own)) RA_HIP(hipStreamWaitEvent(cs, ctx->copied[s & 1], 0), "hipStreamWaitEvent");
     const StepPlan sp = plan_step(lay, a.causal, P, s, Bl);
-    const bool in_place = s == 0 && !stage_own;
+    const bool in_place = (s == 0 && !stage_own) || !staged;
     a.k = kbuf(s);
     a.v = vbuf(s);
-    a.kv_mode = in_place ? ROWS_HOST_Q : ROWS_HOST_MAJOR;
+    a.kv_mode = in_place ? ROWS_HOST_KV : ROWS_HOST_MAJOR;
     a.kv_plane_rows = in_place ? N : Bl;
     a.host_lo = sp.host_lo;
     a.n_hosts = sp.n_hosts;
@@ -586,7 +591,7 @@ ra_status ring_attn_fwd(const void* q, const void* k, const void* v, void* out, 
       RA_HIP(launch_spin(g_delay_compute_us, cs), "delay");
       RA_HIP(launch_step(a, d, dtype, cs, step_flops(a, d)), "step kernel launch");
     }
-    if (s + 2 < P) RA_HIP(hipEventRecord(ctx->done[s & 1], cs), "hipEventRecord");
+    if (staged && s + 2 < P) RA_HIP(hipEventRecord(ctx->done[s & 1], cs), "hipEventRecord");
   }
   return RA_OK;
 }
@@ -647,7 +652,10 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
   }
   const int n = (int)steps.size();
   const int64_t planes = (int64_t)B * Hkv;
-  if (n > 1 || (n > 0 && stage_first)) {
+  // With the exchange switched off (ra_debug_set_staging(0)) every step
+  // reads its block in place where the kernel can address it.
+  const bool staged = g_staging || stage_first;
+  if (staged && (n > 1 || (n > 0 && stage_first))) {
     RA_HIP(hipEventRecord(ctx->fork, cs), "hipEventRecord");
     RA_HIP(hipStreamWaitEvent(ctx->copy, ctx->fork, 0), "hipStreamWaitEvent");
   }
@@ -664,7 +672,7 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
   // or from staging buffer 0 (zigzag).
   for (int i = 0; i < n; ++i) {
     const int s = steps[i];
-    if (i + 1 < n) {
+    if (staged && i + 1 < n) {
       const int s1 = steps[i + 1];
       const int kv1 = ((rank - s1) % P + P) % P;
       if (i >= 1) RA_HIP(hipStreamWaitEvent(ctx->copy, ctx->done[(i - 1) & 1], 0), "hipStreamWaitEvent");
@@ -675,8 +683,8 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
       RA_HIP(gather_block(vd, v, lay, planes, N, Bl, P, kv1, row_bytes, ctx->copy), "staging copy");
       RA_HIP(hipEventRecord(ctx->copied[(i + 1) & 1], ctx->copy), "hipEventRecord");
     }
-    if (i >= 1 || stage_first) RA_HIP(hipStreamWaitEvent(cs, ctx->copied[i & 1], 0), "hipStreamWaitEvent");
-    if (i == 0 && !stage_first) {
+    if (staged && (i >= 1 || stage_first)) RA_HIP(hipStreamWaitEvent(cs, ctx->copied[i & 1], 0), "hipStreamWaitEvent");
+    if ((i == 0 && !stage_first) || !staged) {
       a.k = k;
       a.v = v;
       a.kv_mode = ROWS_HOST_KV;
@@ -693,7 +701,7 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
     a.fin_hi = (i == n - 1) ? rank + 1 : 0;
     RA_HIP(launch_spin(g_delay_compute_us, cs), "delay");
     RA_HIP(launch_step(a, d, dtype, cs, step_flops(a, d)), "step kernel launch");
-    if (i + 2 < n) RA_HIP(hipEventRecord(ctx->done[i & 1], cs), "hipEventRecord");
+    if (staged && i + 2 < n) RA_HIP(hipEventRecord(ctx->done[i & 1], cs), "hipEventRecord");
   }
   if (n == 0) {
     // Nothing visible (cannot happen for a causal ring: a host sees itself).
@@ -712,13 +720,20 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
 // so the kernels of one step never write the same rows.
 // ---------------------------------------------------------------------------
 struct BwdWs {
+  size_t off_stage[2], kv_bytes;  // staging buffers (K then V) and the K part's size
   size_t off_delta, off_lse2, off_dq, off_dk, off_dv, total;
   bool overflow;
 };
 
-static BwdWs bwd_ws_layout(int B, int H, int Hkv, long long N, int d) {
+static BwdWs bwd_ws_layout(int B, int H, int Hkv, long long N, int d, int P) {
   BwdWs w{};
   SizeAcc a;
+  // two staging buffers of K and V for the reverse ring (bf16, host-major)
+  if (P > 1) {
+    w.off_stage[0] = a.add({(uint64_t)B, (uint64_t)Hkv, (uint64_t)N, (uint64_t)d, 2});
+    w.kv_bytes = a.add({(uint64_t)B, (uint64_t)Hkv, (uint64_t)N, (uint64_t)d, 2}) - w.off_stage[0];
+    w.off_stage[1] = a.add({2, w.kv_bytes});
+  }
   w.off_delta = a.add({(uint64_t)B, (uint64_t)H, (uint64_t)N, 4});
   w.off_lse2 = a.add({(uint64_t)B, (uint64_t)H, (uint64_t)N, 4});
   w.off_dq = a.add({(uint64_t)B, (uint64_t)H, (uint64_t)N, (uint64_t)d, 4});
@@ -743,7 +758,7 @@ ra_status bwd_args(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dt
 size_t ring_attn_bwd_ws_bytes(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype) {
   g_err.clear();
   if (bwd_args(B, H, Hkv, N, d, P, dtype, 1.f) != RA_OK) return SIZE_MAX;
-  const BwdWs W = bwd_ws_layout(B, H, Hkv, N, d);
+  const BwdWs W = bwd_ws_layout(B, H, Hkv, N, d, P);
   if (W.overflow) {
     fail(RA_ENOMEM, "workspace size exceeds the 48-bit device address space");
     return SIZE_MAX;
@@ -760,7 +775,7 @@ ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void*
   ra_status st = bwd_args(B, H, Hkv, N, d, P, dtype, scale);
   if (st != RA_OK) return st;
   if ((st = check_layout(layout, N, P)) != RA_OK) return st;
-  const BwdWs W = bwd_ws_layout(B, H, Hkv, N, d);
+  const BwdWs W = bwd_ws_layout(B, H, Hkv, N, d, P);
   if ((st = check_ws(W.overflow, W.total, ws, ws_bytes)) != RA_OK) return st;
   if ((st = check_tensor_align({q, k, v, out, dout, dq, dk, dv}, {lse})) != RA_OK) return st;
   const int64_t Bl = N / P;
@@ -820,11 +835,64 @@ ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void*
       }
     }
   if (lo_s[0] != 0 || hi_s[0] != P - 1) return fail(RA_EUNSUPPORTED, "internal: a host has no diagonal work");
+  // Reverse ring: step s pairs host r with kv block (r + s) mod P.  Step 0
+  // (every host's own block) reads K and V in place; for each later step
+  // the copy stream moves every working host's block into its slot of a
+  // host-major staging buffer (two buffers, alternating) while the
+  // previous step computes: from the slot of the host that held the block
+  // at the previous step when that slot was filled (the block moves one
+  // host down the ring), else from the natural-order arrays.  The dK / dV
+  // accumulators stay at the blocks' rows.
+  std::vector<int> steps;
+  for (int s = 0; s < P; ++s)
+    if (lo_s[s] >= 0) steps.push_back(s);
+  const int n = (int)steps.size();
+  const bool staged = g_staging && P > 1 && n > 1;
+  DeviceCtx* ctx = nullptr;
+  if (staged && (st = get_ctx(&ctx)) != RA_OK) return st;
+  std::unique_lock<std::mutex> enq;
+  if (staged) enq = std::unique_lock<std::mutex>(ctx->enqueue);
+  const size_t row_bytes = (size_t)d * 2;
+  const int64_t planes = (int64_t)B * Hkv;
+  const size_t host_bytes = (size_t)planes * Bl * row_bytes;
   RA_HIP(launch_bwd_prep(out, dout, lse, const_cast<float*>(a.delta), const_cast<float*>(a.lse2), (int64_t)B * H * N,
                          d, cs),
          "prep launch");
-  for (int s = 0; s < P; ++s) {
-    if (lo_s[s] < 0) continue;
+  if (staged) {
+    RA_HIP(hipEventRecord(ctx->fork, cs), "hipEventRecord");
+    RA_HIP(hipStreamWaitEvent(ctx->copy, ctx->fork, 0), "hipStreamWaitEvent");
+  }
+  std::vector<char> filled_prev(P, 0), filled(P, 0);
+  for (int i = 0; i < n; ++i) {
+    const int s = steps[i];
+    if (staged && i + 1 < n) {
+      // copy stream: the blocks of step i + 1 into staging buffer (i + 1) & 1
+      const int s1 = steps[i + 1];
+      if (i >= 1) RA_HIP(hipStreamWaitEvent(ctx->copy, ctx->done[(i - 1) & 1], 0), "hipStreamWaitEvent");
+      RA_HIP(launch_spin(g_delay_copy_us, ctx->copy), "delay");
+      char* kd = wsb + W.off_stage[(i + 1) & 1];
+      char* vd = kd + W.kv_bytes;
+      const char* ks = wsb + W.off_stage[i & 1];
+      const char* vs = ks + W.kv_bytes;
+      std::fill(filled.begin(), filled.end(), 0);
+      for (int r = lo_s[s1]; r <= hi_s[s1]; ++r) {
+        const int blk = (r + s1) % P;
+        const int from = ((blk - s) % P + P) % P;  // host that held the block at step s
+        if (i >= 1 && filled_prev[from]) {
+          RA_HIP(hipMemcpyAsync(kd + r * host_bytes, ks + from * host_bytes, host_bytes, hipMemcpyDeviceToDevice,
+                                ctx->copy), "staging copy");
+          RA_HIP(hipMemcpyAsync(vd + r * host_bytes, vs + from * host_bytes, host_bytes, hipMemcpyDeviceToDevice,
+                                ctx->copy), "staging copy");
+        } else {
+          RA_HIP(gather_block(kd + r * host_bytes, k, lay, planes, N, Bl, P, blk, row_bytes, ctx->copy), "staging copy");
+          RA_HIP(gather_block(vd + r * host_bytes, v, lay, planes, N, Bl, P, blk, row_bytes, ctx->copy), "staging copy");
+        }
+        filled[r] = 1;
+      }
+      filled_prev.swap(filled);
+      RA_HIP(hipEventRecord(ctx->copied[(i + 1) & 1], ctx->copy), "hipEventRecord");
+    }
+    if (staged && i >= 1) RA_HIP(hipStreamWaitEvent(cs, ctx->copied[i & 1], 0), "hipStreamWaitEvent");
     a.s.host_lo = lo_s[s];
     a.s.n_hosts = hi_s[s] - lo_s[s] + 1;
     a.s.kv_shift = -s;
@@ -834,8 +902,14 @@ ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void*
       if (last_q[r] == s) a.q_fin |= 1ull << r;
       if (last_kv[r] == s) a.kv_fin |= 1ull << r;
     }
+    const bool use_stage = staged && i >= 1;
+    a.kv_staged = use_stage ? 1 : 0;
+    a.s.k = use_stage ? static_cast<const void*>(wsb + W.off_stage[i & 1]) : k;
+    a.s.v = use_stage ? static_cast<const void*>(wsb + W.off_stage[i & 1] + W.kv_bytes) : v;
+    RA_HIP(launch_spin(staged ? g_delay_compute_us : 0, cs), "delay");
     RA_HIP(launch_bwd_dkdv(a, d, cs), "dK/dV kernel launch");
     RA_HIP(launch_bwd_dq(a, d, cs), "dQ kernel launch");
+    if (staged && i + 2 < n) RA_HIP(hipEventRecord(ctx->done[i & 1], cs), "hipEventRecord");
   }
   return RA_OK;
 }
@@ -1067,6 +1141,12 @@ ra_status ra_diag_mfma_loop(int workgroups, int iters, void* stream, double* mfm
   if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 24))
     return fail(RA_EINVAL, "workgroups must be in [1, 2^20] and iters in [1, 2^24]");
   RA_HIP(launch_mfma_loop(workgroups, iters, static_cast<hipStream_t>(stream), mfma_count), "calibration launch");
+  return RA_OK;
+}
+
+ra_status ra_debug_set_staging(int on) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_staging = on != 0;
   return RA_OK;
 }
 

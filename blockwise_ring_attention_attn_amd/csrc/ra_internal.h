@@ -70,6 +70,12 @@ struct BwdArgs {
   __bf16* dv_out;
   int first;
   unsigned long long q_fin, kv_fin;
+  // Where the kernels read K and V: 0 in place from the natural-order
+  // arrays (rows of kv block kv_rank); 1 from a host-major staging buffer
+  // (s.k / s.v), where query host q_rank's current block is plane
+  // (q_rank * B + b) * Hkv + hkv of Lkv rows, in block order.  The dK / dV
+  // accumulators always stay at the natural rows of the block.
+  int kv_staged;
 };
 
 struct MergeArgs {

@@ -273,6 +273,17 @@ const char* ra_version(void);
  * of about `copy_us` on the copy stream before each staging copy (0 = none,
  * at most 100000).  Results must not change; only the timeline does. */
 ra_status ra_debug_set_delays(int compute_us, int copy_us);
+
+/* Test and measurement hook for the ring exchange: with on = 0, later
+ * ring_attn_fwd, ring_attn_fwd_share and ring_attn_bwd calls read every ring
+ * step's key/value blocks in place from the natural-order k and v (no staging
+ * copies, no second stream) wherever the kernels can address them in place
+ * (not zigzag forward blocks, nor a striped forward plane of 2 GiB or more,
+ * which are always staged); on = 1 (the default) restores the exchange.  The
+ * kernels and their arithmetic are the same either way, so results are
+ * bitwise identical; only the timeline changes (it isolates what the staging
+ * copies cost the kernels that run beside them). */
+ra_status ra_debug_set_staging(int on);
 /* Counter calibration: launches `workgroups` workgroups of four waves on
  * `stream`, each wave issuing iters x 8 independent bf16 MFMAs
  * (v_mfma_f32_32x32x16_bf16, 32768 FLOPs each) from registers, and writes

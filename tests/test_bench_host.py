@@ -77,3 +77,18 @@ def test_overlap_summary_of_other_compute_kernels(tmp_path):
     assert "| compute kernels | 3 |" in text
     assert "| compute stream idle | 10.00% |" in text          # [16,20) of [0,40)
     assert "| copy time under a compute kernel | 100.0% |" in text
+
+
+def test_cpu_baseline_runs_the_oracle_on_each_workload_shape():
+    """The CPU baseline leg on tiny versions of the three forward workloads
+    (the share with its rank's positions, GQA heads mapped to their kv head)."""
+    import synth
+    for c, share in ((dict(bench.SHARE, N=1024, H=4, Hkv=4), True), (dict(bench.STRIPED, N=512), False),
+                     (dict(bench.PREFILL, N=256, H=4, Hkv=4), False)):
+        Nq = c["N"] // c["P"] if share else c["N"]
+        q = synth.tensor(c["seed"], synth.TENSOR_Q, c["B"], c["H"], Nq, c["d"], "bf16")
+        k = synth.tensor(c["seed"], synth.TENSOR_K, c["B"], c["Hkv"], c["N"], c["d"], "bf16")
+        v = synth.tensor(c["seed"], synth.TENSOR_V, c["B"], c["Hkv"], c["N"], c["d"], "bf16")
+        r = bench.cpu_baseline(c, q, k, v, 0.05, share)
+        assert r["kind"] == "oracle" and r["value"] > 0 and r["cores"] >= 1
+        assert r["os_cpu_count"] >= 1 and r["cpu_model"]

@@ -225,11 +225,15 @@ def test_bwd_rejects_invalid(lib, kw, status, frag):
 
 
 def test_bwd_ws_bytes_cover_fp32_gradients():
-    # fp32 accumulators for dq (B H N d), dk and dv (B Hkv N d), plus lse2 and delta (B H N)
+    # fp32 accumulators for dq (B H N d), dk and dv (B Hkv N d), plus lse2 and delta (B H N);
+    # for P > 1 two bf16 staging buffers of K and V (the reverse ring's exchange)
     B, H, Hkv, N, d, P = 1, 32, 8, 32768, 128, 8
     need = 4 * (B * H * N * d + 2 * B * Hkv * N * d + 2 * B * H * N)
+    stage = 2 * 2 * (B * Hkv * N * d * 2)
     got = ra.load().ring_attn_bwd_ws_bytes(B, H, Hkv, N, d, P, ra.RA_BF16)
-    assert need <= got <= need + (1 << 16)
+    assert need + stage <= got <= need + stage + (1 << 16)
+    got1 = ra.load().ring_attn_bwd_ws_bytes(B, H, Hkv, N, d, 1, ra.RA_BF16)
+    assert need <= got1 <= need + (1 << 16)
 
 
 @pytest.mark.parametrize("kw,frag", [

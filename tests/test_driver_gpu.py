@@ -1,5 +1,6 @@
 """GPU tests of the ring driver's stream ordering, workspace hygiene and
-resumable state (the step state between ring steps is a checkpoint).
+resumable state (the step state between ring steps is a checkpoint), for the
+forward ring, one device's share and the backward's reverse ring.
 
 Stream ordering: the staging copy for step s + 1 must wait for step s - 1's
 kernel (it overwrites what that step read) and step s's kernel must wait for
@@ -101,3 +102,67 @@ def test_step_state_checkpoint_resume():
     out_full = [from_dev(t) for t in ra.ring_attn_finalize(*full)]
     out_res = [from_dev(t) for t in ra.ring_attn_finalize(*restored)]
     assert np.array_equal(out_full[0], out_res[0]) and np.array_equal(out_full[1], out_res[1])
+
+
+def _bwd_inputs(seed, B, H, Hkv, N, d, P, layout):
+    qd, kd, vd = _inputs(seed, B, H, Hkv, N, d)
+    do = to_dev(synth.tensor(seed, synth.TENSOR_DOUT, B, H, N, d, "bf16"), "bf16")
+    out, lse = ra.ring_attn_fwd(qd, kd, vd, P=P, causal=True, layout=layout)
+    return qd, kd, vd, out, do, lse
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
+@pytest.mark.parametrize("delays", [(0, 0), (2000, 0), (0, 2000)])
+def test_bwd_reverse_ring_staging(layout, delays):
+    """The backward's reverse ring with its kv blocks staged on the copy
+    stream (under injected delays on either stream) is bitwise the backward
+    that reads every block in place."""
+    args = _bwd_inputs(25, 1, 4, 2, 8 * 192, 128, 8, layout)
+    kw = dict(P=8, causal=True, layout=layout)
+    try:
+        ra.debug_set_staging(False)
+        ref = [from_dev(t) for t in ra.ring_attn_bwd(*args, **kw)]
+        ra.debug_set_staging(True)
+        ra.debug_set_delays(*delays)
+        got = [from_dev(t) for t in ra.ring_attn_bwd(*args, **kw)]
+    finally:
+        ra.debug_set_staging(True)
+        ra.debug_set_delays(0, 0)
+    for a, b in zip(ref, got):
+        assert np.all(np.isfinite(b)) and np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
+def test_bwd_ignores_stale_workspace(layout):
+    """A backward workspace (staging buffers, accumulators, row statistics)
+    full of NaN bytes gives bitwise the result of a zeroed one."""
+    import torch
+    B, H, Hkv, N, d, P = 1, 4, 2, 8 * 128, 64, 8
+    args = _bwd_inputs(26, B, H, Hkv, N, d, P, layout)
+    nb = ra.load().ring_attn_bwd_ws_bytes(B, H, Hkv, N, d, P, ra.RA_BF16)
+    ws0 = torch.zeros(nb, dtype=torch.uint8, device="cuda:0")
+    wsn = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda:0")
+    a = [from_dev(t) for t in ra.ring_attn_bwd(*args, P=P, causal=True, layout=layout, ws=ws0)]
+    b = [from_dev(t) for t in ra.ring_attn_bwd(*args, P=P, causal=True, layout=layout, ws=wsn)]
+    for x, y in zip(a, b):
+        assert np.all(np.isfinite(y)) and np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+def test_fwd_staged_equals_in_place(layout):
+    """Forward ring and share with the exchange off (every block read in
+    place) are bitwise the staged ones: the staging only moves bytes."""
+    B, H, Hkv, N, d, P = 1, 4, 2, 8 * 256, 128, 8
+    qd, kd, vd = _inputs(27, B, H, Hkv, N, d)
+    try:
+        ra.debug_set_staging(False)
+        ref = [from_dev(t) for t in ra.ring_attn_fwd(qd, kd, vd, P=P, causal=True, layout=layout)]
+        ref_s = [from_dev(t) for t in ra.ring_attn_fwd_share(qd[:, :, :N // P].contiguous(), kd, vd, P=P, rank=3,
+                                                             causal=True, layout=layout)]
+    finally:
+        ra.debug_set_staging(True)
+    got = [from_dev(t) for t in ra.ring_attn_fwd(qd, kd, vd, P=P, causal=True, layout=layout)]
+    got_s = [from_dev(t) for t in ra.ring_attn_fwd_share(qd[:, :, :N // P].contiguous(), kd, vd, P=P, rank=3,
+                                                         causal=True, layout=layout)]
+    for a, b in zip(ref + ref_s, got + got_s):
+        assert np.array_equal(a, b)
