@@ -231,6 +231,11 @@ __device__ __forceinline__ void mfma_a(f32x16& acc, const bf16x8& a, const bf16x
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+// The same wait states, with the accumulators passing through them: no VALU
+// read of these results can be scheduled before the wait.
+__device__ __forceinline__ void mfma_settle(f32x16& x, f32x16& y) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y) :: "memory");
+}
 
 // ---------------------------------------------------------------------------
 // dK / dV: one workgroup per (query host, batch, kv head, 128-key tile).  It
@@ -317,6 +322,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   auto delb = [](auto I) { return reinterpret_cast<float(*)[64]>(slot_buf<3, decltype(I)::value % NSLOT, 1024>()); };
   auto lims = [](auto I) { return reinterpret_cast<int*>(slot_buf<4, decltype(I)::value % NSLOT, 4 * kRows>()); };
   const LdsOffsets<D> off(lane);
+  // Causal mask of a tile's S as an addend: -inf where this lane's key lies
+  // past the row's limit, 0 elsewhere (register r holds query row
+  // 8 (r / 4) + 4 half + r % 4).  Only a tile whose first row does not see
+  // every key of the wave needs it (the limits do not decrease along the
+  // rows); all other tiles skip it.
+  const int wave_last_key = min(key0 + wave * 32 + 31, A.Lkv - 1);
+  auto needs_mask = [&](auto slot) __attribute__((always_inline)) -> bool {
+    return __builtin_amdgcn_readfirstlane(lims(slot)[0]) < wave_last_key;
+  };
+  auto mask_init = [&](auto slot) __attribute__((always_inline)) -> f32x16 {
+    f32x16 m;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int4 l4 = *reinterpret_cast<const int4*>(&lims(slot)[8 * g + 4 * half]);
+      m[4 * g] = my_key > l4.x ? kNegInf : 0.f;
+      m[4 * g + 1] = my_key > l4.y ? kNegInf : 0.f;
+      m[4 * g + 2] = my_key > l4.z ? kNegInf : 0.f;
+      m[4 * g + 3] = my_key > l4.w ? kNegInf : 0.f;
+    }
+    return m;
+  };
   const int64_t plane_elems = G.n_tok * D;
   const unsigned rec_rows = (unsigned)(G.n_tok * T::RB);   // bytes of one (b, h) plane
   const unsigned rec_vec = (unsigned)(G.n_tok * 4);
@@ -384,6 +410,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
     });
     wait_vmcnt0();
     __syncthreads();
+    if (needs_mask(IC<0>{})) sc = mask_init(IC<0>{});
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(qbuf(IC<0>{}), off, ks), kf[ks], sc, 0, 0, 0);
@@ -414,7 +441,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
     issue(t + LOOK, IC<SF>{});
     // (S(t+1), dP(t+1) are computed even for the last tile: the slot holds
     // stale rows then and the results are not used.)
-    f32x16 sn, dpn;
     constexpr int NA = 2 * KS;        // S / dP MFMAs per tile
     constexpr int NB = 4 * NDB;       // dV / dK MFMAs per tile
     static_assert(NA == NB, "one S/dP and one dV/dK MFMA per step");
@@ -434,19 +460,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
 #pragma unroll
       for (int j = 0; j < PFB; ++j) fb[j] = bfrag(j);
     }
-    // Row statistics of tile t (lse2, delta, causal limit) in groups of four
-    // rows, each group read one group ahead of its use.
+    // Row statistics of tile t (lse2, delta) in groups of four rows (rows
+    // 8 g + 4 half .. + 3, loaded by wave g), each group read one group ahead
+    // of its use.
     float lv[2][4], dv[2][4];
-    int lm[2][4];
     auto rowstats = [&](int g, int k) __attribute__((always_inline)) {
-      const int q0 = 8 * g + 4 * half;   // rows q0 .. q0 + 3 (loaded by wave g)
       const float4 l4 = *reinterpret_cast<const float4*>(&lseb(IC<SL>{})[g][4 * half]);
       const float4 d4 = *reinterpret_cast<const float4*>(&delb(IC<SL>{})[g][4 * half]);
-      const int4 m4 = *reinterpret_cast<const int4*>(&lims(IC<SL>{})[q0]);
       lv[k][0] = l4.x; lv[k][1] = l4.y; lv[k][2] = l4.z; lv[k][3] = l4.w;
       dv[k][0] = d4.x; dv[k][1] = d4.y; dv[k][2] = d4.z; dv[k][3] = d4.w;
-      lm[k][0] = m4.x; lm[k][1] = m4.y; lm[k][2] = m4.z; lm[k][3] = m4.w;
     };
+    f32x16 sn, dpn;
     rowstats(0, 0);
     static_for<NA>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
@@ -465,10 +489,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
         if constexpr ((i & 1) == 0) mfma_a(dvT[db], b, pbp[hc]);
         else mfma_a(dkT[db], b, dsbp[hc]);
       }
-      // VALU: the 16 elements of tile t spread over the NA steps.  The causal
-      // limit is applied to every element (a row's limit is at least every
-      // key of an unmasked tile, so the test is a no-op there); testing per
-      // element keeps the step free of branches.
+      // VALU: the 16 elements of tile t spread over the NA steps (the causal
+      // mask is already in S: masked scores are -inf, their P and dS 0).
       static_for<16>([&](auto rc) __attribute__((always_inline)) {
         constexpr int r = decltype(rc)::value;
         if constexpr (r * NA / 16 == i) {
@@ -476,8 +498,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
           if constexpr ((r & 3) == 0 && g + 1 < 4) rowstats(g + 1, k ^ 1);
           float x = sc[r];
           asm volatile("" : "+v"(x));   // (keeps the element's arithmetic in this step)
-          float p = fast_exp2(__builtin_fmaf(x, c, -lv[k][r & 3]));
-          p = my_key > lm[k][r & 3] ? 0.f : p;
+          float p = fast_exp2(__builtin_fmaf(x, c, -lv[k][r & 3]));   // 0 where masked (S = -inf)
           float ds = p * (dpc[r] - dv[k][r & 3]);
           asm volatile("" : "+v"(p), "+v"(ds));
           if constexpr (r & 1) {
@@ -493,7 +514,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
       });
       __builtin_amdgcn_sched_barrier(0);
     });
-    mfma_settle();   // S(t+1), dP(t+1) are read by the VALU from here on
+    mfma_settle(sn, dpn);   // S(t+1), dP(t+1) are read by the VALU from here on
+    // the causal mask of S(t+1), only when its first row does not see every
+    // key of the wave (masked scores become -inf, so their P and dS are 0)
+    if (needs_mask(IC<SN>{})) {
+      const f32x16 m = mask_init(IC<SN>{});
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sn[r] += m[r];
+    }
 #pragma unroll
     for (int hc = 0; hc < 2; ++hc) {
       pbp[hc] = pbn[hc];
@@ -578,6 +606,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
   const int my_row = row_first + wave * 32 + col;
   const bool row_ok = my_row < A.Lq;
   const int lim32 = llim<LAYOUT>(A, w.q_rank, w.kv_rank, row_ok ? my_row : row_last);
+  // limit of the wave's first row: keys up to it are visible to all its rows
+  const int wave_first = row_first + wave * 32;
+  const int wave_first_lim = llim<LAYOUT>(A, w.q_rank, w.kv_rank, wave_first < A.Lq ? wave_first : row_last);
   const int kv_end = llim<LAYOUT>(A, w.q_rank, w.kv_rank, row_last) + 1;
   const int ntiles = (int)((kv_end + kRows - 1) / kRows);
 
@@ -658,13 +689,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(kt, off, ks), qf[ks], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(vt, off, ks), of[ks], dp, 0, 0, 0);
     }
-    // causal limit per element, branch free (a no-op on unmasked tiles)
-    const int bound = lim32 - t * kRows - 4 * half;
+    // causal limit per element, only on the tiles past the wave's fully
+    // visible prefix (the limits do not decrease along the rows)
+    if (t * kRows + kRows - 1 > wave_first_lim) {
+      const int bound = lim32 - t * kRows - 4 * half;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) > bound) s[r] = kNegInf;
+    }
     f32x16 dsf;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float p = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
-      p = 8 * (r >> 2) + (r & 3) > bound ? 0.f : p;
+      const float p = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
       dsf[r] = p * (dp[r] - del);
     }
 #pragma unroll
