@@ -158,6 +158,15 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int base) {
   return r;
 }
 
+// Direct-to-LDS buffer loads (16 or 4 bytes per lane) at a vector offset
+// plus a scalar offset.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff, unsigned soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, void* lds, int voff, unsigned soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
+}
+
 // One LDS buffer per (use, slot): a distinct object for every slot.  The
 // compiler tracks direct-to-LDS loads per LDS object and makes a read wait
 // for every load in flight into the same object, so slots of one array
@@ -303,24 +312,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dvT[db] = dkT[db] = f32x16{};
 
-  // Five LDS slots for the streamed (Q, dO, lse, delta, limit) tiles.  Tile
+  // Five LDS slots for the streamed (Q, dO, row statistics) tiles.  Tile
   // t+3 is loaded straight into LDS (buffer_load ... lds, no registers)
   // while tile t is consumed, so each load has two tiles of time to land.
   constexpr int NSLOT = 5, LOOK = 3;
   constexpr int ROWS_PER_INSTR = 1024 / T::RB;        // tile rows per 1 KiB load instruction
   constexpr int INSTR = T::BYTES / 1024;              // per tensor per tile
   constexpr int PER_WAVE = INSTR / 4;                 // per wave
-  constexpr int LOADS = 2 * PER_WAVE + 2;             // vector loads per wave per tile (Q, dO, lse, delta)
+  constexpr int LOADS = 2 * PER_WAVE;                 // Q and dO loads per wave per tile
   static_assert(PER_WAVE >= 1 && INSTR % 4 == 0, "tile must split over the four waves");
-  // Per slot: the Q and dO tiles; lse / delta, where wave w loads rows
-  // 8 w .. 8 w + 7 with 4-byte lanes (every lane of the load owns a float of
-  // the wave's 64-float area; lanes 8..63 read out of range and write zeros
-  // there); the causal limits of the tile's rows.
+  // Per slot: the Q and dO tiles and the tile's row statistics (lse2,
+  // delta) of its 32 rows, 256 bytes that wave 0 loads with one instruction
+  // (lane l: row l / 2, statistic l % 2).
   auto qbuf = [](auto I) { return slot_buf<0, decltype(I)::value % NSLOT, T::BYTES>(); };
   auto obuf = [](auto I) { return slot_buf<1, decltype(I)::value % NSLOT, T::BYTES>(); };
-  auto lseb = [](auto I) { return reinterpret_cast<float(*)[64]>(slot_buf<2, decltype(I)::value % NSLOT, 1024>()); };
-  auto delb = [](auto I) { return reinterpret_cast<float(*)[64]>(slot_buf<3, decltype(I)::value % NSLOT, 1024>()); };
-  auto lims = [](auto I) { return reinterpret_cast<int*>(slot_buf<4, decltype(I)::value % NSLOT, 4 * kRows>()); };
+  auto rsb = [](auto I) { return reinterpret_cast<float(*)[2]>(slot_buf<2, decltype(I)::value % NSLOT, 8 * kRows>()); };
   const LdsOffsets<D> off(lane);
   // Causal mask of a tile's S as an addend: -inf where this lane's key lies
   // past the row's limit, 0 elsewhere (register r holds query row
@@ -328,78 +334,102 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   // every key of the wave needs it (the limits do not decrease along the
   // rows); all other tiles skip it.
   const int wave_last_key = min(key0 + wave * 32 + 31, A.Lkv - 1);
-  auto needs_mask = [&](auto slot) __attribute__((always_inline)) -> bool {
-    return __builtin_amdgcn_readfirstlane(lims(slot)[0]) < wave_last_key;
+  auto needs_mask = [&](int row0) __attribute__((always_inline)) -> bool {
+    return A.causal && llim<LAYOUT>(A, w.q_rank, w.kv_rank, row0) < wave_last_key;
   };
-  auto mask_init = [&](auto slot) __attribute__((always_inline)) -> f32x16 {
+  auto mask_init = [&](int row0) __attribute__((always_inline)) -> f32x16 {
     f32x16 m;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int4 l4 = *reinterpret_cast<const int4*>(&lims(slot)[8 * g + 4 * half]);
-      m[4 * g] = my_key > l4.x ? kNegInf : 0.f;
-      m[4 * g + 1] = my_key > l4.y ? kNegInf : 0.f;
-      m[4 * g + 2] = my_key > l4.z ? kNegInf : 0.f;
-      m[4 * g + 3] = my_key > l4.w ? kNegInf : 0.f;
+    for (int r = 0; r < 16; ++r) {
+      const int i = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
+      const int lim = i < A.Lq ? llim<LAYOUT>(A, w.q_rank, w.kv_rank, i) : -1;
+      m[r] = my_key > lim ? kNegInf : 0.f;
     }
     return m;
   };
   const int64_t plane_elems = G.n_tok * D;
   const unsigned rec_rows = (unsigned)(G.n_tok * T::RB);   // bytes of one (b, h) plane
-  const unsigned rec_vec = (unsigned)(G.n_tok * 4);
+  const unsigned rec_rs = (unsigned)(G.n_tok * 8);          // bytes of its row statistics
 
-  // tile it: head hkv*group + it / nqt, query tile qt0 + it % nqt.  Lane
-  // l of load instruction i fills LDS slot 64 i + l of the tile: row
-  // ROWS_PER_INSTR i + l / CPR, chunk slot l % CPR holding logical chunk
-  // (l % CPR) ^ dswz(row).  Rows past the block read as zeros (offset out
-  // of the buffer's range).
-  // A tile index past the last one issues the same loads with every offset
-  // out of range (they write zeros into the slot and touch no memory), so
-  // that the loop body has no branch: the compiler would otherwise sink the
-  // MFMAs of a step into the block after it, away from the exponentials
-  // they are meant to overlap.
-  auto issue = [&](int it_in, auto slot) __attribute__((always_inline)) {
-    const bool valid = it_in < total;
-    const int it = valid ? it_in : 0;
-    const int h = w.hkv * group + it / nqt;
-    const int row0 = (qt0 + it % nqt) * kRows;
-    const int64_t qplane = (int64_t)w.b * A.H + h;
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(A.q)) + qplane * plane_elems, 0,
-        rec_rows, 0x00020000);
-    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(G.dout)) + qplane * plane_elems, 0,
-        rec_rows, 0x00020000);
+  // Tile it: head hkv*group + it / nqt, query tile qt0 + it % nqt.  issue()
+  // is called for it = 0, 1, 2, ... in order, so it keeps the head and the
+  // query tile of the next call (no division per tile) and that head's
+  // buffer descriptors.  Lane l of load instruction i fills LDS slot 64 i + l
+  // of the tile: row ROWS_PER_INSTR i + l / CPR, chunk slot l % CPR holding
+  // logical chunk (l % CPR) ^ dswz(row).  In the contiguous and striped
+  // layouts a tile's rows are an arithmetic sequence of natural rows, so
+  // the row base goes into the scalar offset and each lane's vector offset
+  // is a constant; zigzag tiles and the ragged last tile of a head take
+  // per-lane offsets, rows past the block set out of the buffer's range
+  // (they read zeros).  A tile index past the last one issues the same loads
+  // with every offset out of range (they write zeros into the slot and
+  // touch no memory), so that the loop body has no branch around them: the
+  // compiler would otherwise sink the MFMAs of a step into the block after
+  // it, away from the exponentials they are meant to overlap.
+  constexpr bool kAffine = LAYOUT != 2;
+  const int row_stride = LAYOUT == 1 ? A.P : 1;             // natural rows between consecutive block rows
+  int voff_row[PER_WAVE], rr_row[PER_WAVE], qchunk[PER_WAVE];
 #pragma unroll
-    for (int u = 0; u < PER_WAVE; ++u) {
-      const int ins = wave * PER_WAVE + u;
-      const int r = ins * ROWS_PER_INSTR + lane / T::CPR;
-      const int q = lane % T::CPR;
-      const int i = row0 + r;
-      const int voff = (valid && i < A.Lq) ? lrow<LAYOUT>(w.q_rank, i, A.Lq, A.P) * T::RB + 16 * (q ^ dswz<D>(r))
-                                           : (int)rec_rows;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)(qbuf(slot) + ins * 1024),
-                                               16, voff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (__attribute__((address_space(3))) void*)(obuf(slot) + ins * 1024),
-                                               16, voff, 0, 0, 0);
+  for (int u = 0; u < PER_WAVE; ++u) {
+    const int ins = wave * PER_WAVE + u;
+    rr_row[u] = ins * ROWS_PER_INSTR + lane / T::CPR;
+    qchunk[u] = 16 * ((lane % T::CPR) ^ dswz<D>(rr_row[u]));
+    voff_row[u] = rr_row[u] * row_stride * T::RB + qchunk[u];
+  }
+  const int voff_rs = (lane >> 1) * row_stride * 8 + 4 * (lane & 1);
+  int is_h = 0, is_qt = 0;
+  // plane bases of the head being issued (advanced by one plane per head)
+  const int64_t qplane0 = (int64_t)w.b * A.H + w.hkv * group;
+  unsigned short* qbase = const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(A.q)) + qplane0 * plane_elems;
+  unsigned short* obase =
+      const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(G.dout)) + qplane0 * plane_elems;
+  float* rbase = const_cast<float*>(G.rowstat) + qplane0 * G.n_tok * 2;
+  auto issue = [&](int it, auto slot) __attribute__((always_inline)) {
+    const bool valid = it < total;
+    const int row0 = (qt0 + is_qt) * kRows;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(qbase, 0, rec_rows, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(obase, 0, rec_rows, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(rbase, 0, rec_rs, 0x00020000);
+    if (kAffine && valid && row0 + kRows <= A.Lq) {
+      const unsigned nat0 = LAYOUT == 0 ? (unsigned)(w.q_rank * A.Lq + row0) : (unsigned)(row0 * A.P + w.q_rank);
+#pragma unroll
+      for (int u = 0; u < PER_WAVE; ++u) {
+        const int ins = wave * PER_WAVE + u;
+        lds_load16(rq, qbuf(slot) + ins * 1024, voff_row[u], nat0 * T::RB);
+        lds_load16(ro, obuf(slot) + ins * 1024, voff_row[u], nat0 * T::RB);
+      }
+      if (wave == 0) lds_load4(rr, &rsb(slot)[0][0], voff_rs, nat0 * 8);
+    } else {
+#pragma unroll
+      for (int u = 0; u < PER_WAVE; ++u) {
+        const int ins = wave * PER_WAVE + u;
+        const int i = row0 + rr_row[u];
+        const int voff = (valid && i < A.Lq) ? lrow<LAYOUT>(w.q_rank, i, A.Lq, A.P) * T::RB + qchunk[u] : (int)rec_rows;
+        lds_load16(rq, qbuf(slot) + ins * 1024, voff, 0u);
+        lds_load16(ro, obuf(slot) + ins * 1024, voff, 0u);
+      }
+      if (wave == 0) {
+        const int i = row0 + (lane >> 1);
+        const int voff = (valid && i < A.Lq) ? lrow<LAYOUT>(w.q_rank, i, A.Lq, A.P) * 8 + 4 * (lane & 1) : (int)rec_rs;
+        lds_load4(rr, &rsb(slot)[0][0], voff, 0u);
+      }
     }
-    // lse and delta: wave w loads rows 8 w .. 8 w + 7 (lanes 0..7)
-    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(G.lse2) + qplane * G.n_tok, 0, rec_vec, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(G.delta) + qplane * G.n_tok, 0, rec_vec, 0x00020000);
-    {
-      const int i = row0 + 8 * wave + lane;
-      const int voff = (valid && lane < 8 && i < A.Lq) ? lrow<LAYOUT>(w.q_rank, i, A.Lq, A.P) * 4 : (int)rec_vec;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)(&lseb(slot)[wave][0]),
-                                               4, voff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (__attribute__((address_space(3))) void*)(&delb(slot)[wave][0]),
-                                               4, voff, 0, 0, 0);
-    }
-    if (threadIdx.x < kRows) {
-      const int i = row0 + threadIdx.x;
-      lims(slot)[threadIdx.x] = i < A.Lq ? llim<LAYOUT>(A, w.q_rank, w.kv_rank, i) : -1;
+    if (valid && ++is_qt == nqt) {
+      is_qt = 0;
+      ++is_h;
+      qbase += plane_elems;
+      obase += plane_elems;
+      rbase += G.n_tok * 2;
     }
   };
+  // Loads still in flight that a wave may leave behind at the end of a tile:
+  // those of the newest tile (wave 0 also loads its row statistics).
+  auto wait_newest = [&]() __attribute__((always_inline)) {
+    if (wave == 0) wait_vmcnt<LOADS + 1>();
+    else wait_vmcnt<LOADS>();
+  };
+  // query tile of tile t for the mask: cs_qt follows the consumed tiles
+  int cs_qt = 0;
 
   // S and dP of a tile: [32 queries x 32 keys], one key per lane column;
   // register r holds query 8 (r / 4) + 4 half + r % 4 of the tile.
@@ -410,7 +440,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
     });
     wait_vmcnt0();
     __syncthreads();
-    if (needs_mask(IC<0>{})) sc = mask_init(IC<0>{});
+    if (needs_mask(qt0 * kRows)) sc = mask_init(qt0 * kRows);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(qbuf(IC<0>{}), off, ks), kf[ks], sc, 0, 0, 0);
@@ -465,10 +495,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
     // of its use.
     float lv[2][4], dv[2][4];
     auto rowstats = [&](int g, int k) __attribute__((always_inline)) {
-      const float4 l4 = *reinterpret_cast<const float4*>(&lseb(IC<SL>{})[g][4 * half]);
-      const float4 d4 = *reinterpret_cast<const float4*>(&delb(IC<SL>{})[g][4 * half]);
-      lv[k][0] = l4.x; lv[k][1] = l4.y; lv[k][2] = l4.z; lv[k][3] = l4.w;
-      dv[k][0] = d4.x; dv[k][1] = d4.y; dv[k][2] = d4.z; dv[k][3] = d4.w;
+      const int q0 = 8 * g + 4 * half;
+      const float4 a4 = *reinterpret_cast<const float4*>(&rsb(IC<SL>{})[q0][0]);
+      const float4 b4 = *reinterpret_cast<const float4*>(&rsb(IC<SL>{})[q0 + 2][0]);
+      lv[k][0] = a4.x; dv[k][0] = a4.y; lv[k][1] = a4.z; dv[k][1] = a4.w;
+      lv[k][2] = b4.x; dv[k][2] = b4.y; lv[k][3] = b4.z; dv[k][3] = b4.w;
     };
     f32x16 sn, dpn;
     rowstats(0, 0);
@@ -517,8 +548,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
     mfma_settle(sn, dpn);   // S(t+1), dP(t+1) are read by the VALU from here on
     // the causal mask of S(t+1), only when its first row does not see every
     // key of the wave (masked scores become -inf, so their P and dS are 0)
-    if (needs_mask(IC<SN>{})) {
-      const f32x16 m = mask_init(IC<SN>{});
+    const int qt_next = cs_qt + 1 == nqt ? 0 : cs_qt + 1;
+    cs_qt = qt_next;
+    if (needs_mask((qt0 + qt_next) * kRows)) {
+      const f32x16 m = mask_init((qt0 + qt_next) * kRows);
 #pragma unroll
       for (int r = 0; r < 16; ++r) sn[r] += m[r];
     }
@@ -530,9 +563,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
     sc = sn;
     dpc = dpn;
     // tile t+2 must have landed before the next iteration reads it: only
-    // tile t+3's loads (issued above) may still be in flight (and the causal
-    // limits written with ds_write are visible)
-    wait_vmcnt<LOADS>();
+    // tile t+3's loads (issued above) may still be in flight
+    wait_newest();
     wait_lgkmcnt0();
     barrier_no_fence();
   };
@@ -617,8 +649,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
   bf16x8 qf[KS], of[KS];
   load_row_frags<D>(qf, reinterpret_cast<const unsigned short*>(A.q), qrow, row_ok, half);
   load_row_frags<D>(of, reinterpret_cast<const unsigned short*>(G.dout), qrow, row_ok, half);
-  const float lse2 = row_ok ? G.lse2[qrow] : __builtin_huge_valf();   // past the block: P = 0
-  const float del = row_ok ? G.delta[qrow] : 0.f;
+  const float lse2 = row_ok ? G.rowstat[2 * qrow] : __builtin_huge_valf();   // past the block: P = 0
+  const float del = row_ok ? G.rowstat[2 * qrow + 1] : 0.f;
 
   f32x16 dqT[NDB];
 #pragma unroll
@@ -727,13 +759,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
   for (int db = 0; db < NDB; ++db) emit_block(dq_row, G.dq_out + qrow * D, dqT[db], db, half, G.scale, first, fin);
 }
 
-// delta_i = sum_c dO_ic O_ic and the base-2 lse the kernels subtract:
-// lse2_i = lse_i log2(e), +inf for a row without visible keys (so that its P
-// is 0).  A row is d/8 lanes, each with one 16-byte chunk of O and of dO
+// Row statistics (lse2_i, delta_i), interleaved per row: delta_i =
+// sum_c dO_ic O_ic and the base-2 lse the kernels subtract, lse2_i = lse_i
+// log2(e), +inf for a row without visible keys (so that its P is 0).  A row is d/8 lanes, each with one 16-byte chunk of O and of dO
 // (read once: nontemporal loads); the lanes of a row are an aligned group,
 // so the butterfly stays inside it.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* out, const __bf16* dout, const float* lse,
-                                                        float* delta, float* lse2, int64_t rows, int d) {
+                                                        float* rowstat, int64_t rows, int d) {
   const int cpr = d >> 3;                       // 8 or 16 lanes per row
   const int t = (int)threadIdx.x;
   const int64_t row = (int64_t)blockIdx.x * (256 / cpr) + t / cpr;
@@ -750,9 +782,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* out, const 
   }
   for (int m = cpr >> 1; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
   if (ok && c == 0) {
-    delta[row] = acc;
     const float l = lse[row];
-    lse2[row] = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
+    *reinterpret_cast<float2*>(rowstat + 2 * row) = make_float2(l == kNegInf ? __builtin_huge_valf() : l * kLog2e, acc);
   }
 }
 
@@ -761,14 +792,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* out, const 
 int bwd_dq_rows() { return kDqRows; }
 int bwd_dkdv_rows() { return kDkdvKeys; }
 
-hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, float* delta, float* lse2,
-                           int64_t rows, int d, hipStream_t s) {
+hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, float* rowstat, int64_t rows, int d,
+                           hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (d != 64 && d != 128) return hipErrorInvalidValue;
   const int64_t per_block = 256 / (d / 8);      // rows per workgroup
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + per_block - 1) / per_block)), dim3(256), 0, s,
-                     reinterpret_cast<const __bf16*>(out), reinterpret_cast<const __bf16*>(dout), lse, delta, lse2,
-                     rows, d);
+                     reinterpret_cast<const __bf16*>(out), reinterpret_cast<const __bf16*>(dout), lse, rowstat, rows, d);
   return hipGetLastError();
 }
 

@@ -721,7 +721,7 @@ ra_status ring_attn_fwd_share(const void* q, const void* k, const void* v, void*
 // ---------------------------------------------------------------------------
 struct BwdWs {
   size_t off_stage[2], kv_bytes;  // staging buffers (K then V) and the K part's size
-  size_t off_delta, off_lse2, off_dq, off_dk, off_dv, total;
+  size_t off_rowstat, off_dq, off_dk, off_dv, total;
   bool overflow;
 };
 
@@ -734,8 +734,7 @@ static BwdWs bwd_ws_layout(int B, int H, int Hkv, long long N, int d, int P) {
     w.kv_bytes = a.add({(uint64_t)B, (uint64_t)Hkv, (uint64_t)N, (uint64_t)d, 2}) - w.off_stage[0];
     w.off_stage[1] = a.add({2, w.kv_bytes});
   }
-  w.off_delta = a.add({(uint64_t)B, (uint64_t)H, (uint64_t)N, 4});
-  w.off_lse2 = a.add({(uint64_t)B, (uint64_t)H, (uint64_t)N, 4});
+  w.off_rowstat = a.add({(uint64_t)B, (uint64_t)H, (uint64_t)N, 8});
   w.off_dq = a.add({(uint64_t)B, (uint64_t)H, (uint64_t)N, (uint64_t)d, 4});
   w.off_dk = a.add({(uint64_t)B, (uint64_t)Hkv, (uint64_t)N, (uint64_t)d, 4});
   w.off_dv = a.add({(uint64_t)B, (uint64_t)Hkv, (uint64_t)N, (uint64_t)d, 4});
@@ -803,8 +802,7 @@ ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void*
   a.s.n_qtiles = (int)nqt;
   a.s.scale_log2 = scale * 1.4426950408889634f;
   a.dout = dout;
-  a.lse2 = reinterpret_cast<float*>(wsb + W.off_lse2);
-  a.delta = reinterpret_cast<float*>(wsb + W.off_delta);
+  a.rowstat = reinterpret_cast<float*>(wsb + W.off_rowstat);
   a.dq_acc = reinterpret_cast<float*>(wsb + W.off_dq);
   a.dk_acc = reinterpret_cast<float*>(wsb + W.off_dk);
   a.dv_acc = reinterpret_cast<float*>(wsb + W.off_dv);
@@ -855,8 +853,7 @@ ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void*
   const size_t row_bytes = (size_t)d * 2;
   const int64_t planes = (int64_t)B * Hkv;
   const size_t host_bytes = (size_t)planes * Bl * row_bytes;
-  RA_HIP(launch_bwd_prep(out, dout, lse, const_cast<float*>(a.delta), const_cast<float*>(a.lse2), (int64_t)B * H * N,
-                         d, cs),
+  RA_HIP(launch_bwd_prep(out, dout, lse, const_cast<float*>(a.rowstat), (int64_t)B * H * N, d, cs),
          "prep launch");
   if (staged) {
     RA_HIP(hipEventRecord(ctx->fork, cs), "hipEventRecord");

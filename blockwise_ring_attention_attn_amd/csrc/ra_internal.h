@@ -52,8 +52,8 @@ struct StepArgs {
 struct BwdArgs {
   StepArgs s;
   const void* dout;       // [B, H, N, d], same rows as q
-  const float* lse2;      // [B, H, N] lse of the forward times log2(e) (+inf: no visible key)
-  const float* delta;     // [B, H, N] rowsum(dO * O)
+  const float* rowstat;   // [B, H, N][2]: lse of the forward times log2(e) (+inf: no visible key),
+                          // then rowsum(dO * O)
   float* dq_acc;          // [B, H, N, d]
   float* dk_acc;          // [B, Hkv, N, d]
   float* dv_acc;          // [B, Hkv, N, d]
@@ -126,8 +126,8 @@ hipError_t launch_mfma_loop(int workgroups, int iters, hipStream_t s, double* mf
 // first step writes the fp32 accumulators, a row's last step its bf16 result).
 int bwd_dq_rows();     // query rows per dQ workgroup
 int bwd_dkdv_rows();   // keys per dK/dV workgroup
-hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, float* delta, float* lse2,
-                           int64_t rows, int d, hipStream_t s);
+hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, float* rowstat, int64_t rows, int d,
+                           hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, int d, hipStream_t s);
 
