@@ -250,9 +250,26 @@ __device__ __forceinline__ void mfma_settle(f32x16& x, f32x16& y) {
 // dK / dV: one workgroup per (query host, batch, kv head, 128-key tile).  It
 // sweeps, for every query head of the kv head's group, the 32-row query
 // tiles that see any of its keys.
+//
+// Eight waves in producer / consumer pairs: waves p and p + 4 (p = 0..3)
+// share a SIMD and the 32 keys key0 + 32 p ... .  The producer (wave p)
+// keeps the keys' K and V rows in registers and, for query tile t,
+// computes S = Q K^T and dP = dO V^T (MFMA), then P = exp2(S c - lse2) and
+// dS = P (dP - delta) (VALU), and hands P and dS to its consumer through
+// LDS.  The consumer (wave p + 4) holds the fp32 dV^T and dK^T accumulators
+// and adds dO^T P and Q^T dS (MFMA, dO^T and Q^T from transposing LDS reads)
+// one phase later, while the producer computes the next tile.  So on every
+// SIMD one wave's MFMAs run beside the other wave's exponentials, and each
+// wave stays within half the register file (the accumulators and the
+// resident K / V rows would not fit one wave at two waves per SIMD).
+// Phase k: producers on tile k, consumers on tile k - 1; one barrier per
+// phase.  The consumers also issue the tile loads (Q, dO and the row
+// statistics, straight into LDS, LOOK tiles ahead).
 // ---------------------------------------------------------------------------
+constexpr int kDkdvThreads = 512;
+
 template <int D, int LAYOUT>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
+__global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   using T = RowTile<D>;
   constexpr int KS = D / 16, NDB = D / 32;
   const StepArgs& A = G.s;
@@ -276,22 +293,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   const int group = A.H / A.Hkv;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool producer = wave < 4;
+  const int pw = wave & 3;              // the pair: keys key0 + 32 pw ...
+  const int cw = wave - 4;              // consumer index 0..3 (consumers only)
   const int half = lane >> 5, col = lane & 31;
   const float c = A.scale_log2;
 
-  // this lane's key and the wave's key range
+  // this lane's key and the pair's key range
   const int key0 = kt * kDkdvKeys;
-  const int my_key = key0 + wave * 32 + col;
+  const int my_key = key0 + pw * 32 + col;
   const bool key_ok = my_key < A.Lkv;
   const int64_t kv_plane = (int64_t)w.b * A.Hkv + w.hkv;
   const int64_t key_row = key_ok ? nat_row<LAYOUT>(A, kv_plane, G.n_tok, w.kv_rank, my_key, A.Lkv) : 0;
-  // the key's K / V row: in place (its natural row) or in the host-major staging
-  const int64_t src_row =
-      G.kv_staged ? ((int64_t)w.q_rank * A.B * A.Hkv + kv_plane) * A.Lkv + (key_ok ? my_key : 0) : key_row;
-
-  bf16x8 kf[KS], vf[KS];
-  load_row_frags<D>(kf, reinterpret_cast<const unsigned short*>(A.k), src_row, key_ok, half);
-  load_row_frags<D>(vf, reinterpret_cast<const unsigned short*>(A.v), src_row, key_ok, half);
 
   // first query row that sees any key of the workgroup (the limit is
   // non-decreasing in the row)
@@ -308,77 +321,49 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   const int nqt = (A.Lq + kRows - 1) / kRows - qt0;   // query tiles per head
   const int total = nqt > 0 ? nqt * group : 0;
 
-  f32x16 dvT[NDB], dkT[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) dvT[db] = dkT[db] = f32x16{};
-
-  // Five LDS slots for the streamed (Q, dO, row statistics) tiles.  Tile
-  // t+3 is loaded straight into LDS (buffer_load ... lds, no registers)
-  // while tile t is consumed, so each load has two tiles of time to land.
-  constexpr int NSLOT = 5, LOOK = 3;
+  // LDS: NSLOT slots for the streamed (Q, dO, row statistics) tiles (tile k
+  // is read by the producers in phase k and by the consumers in phase k + 1,
+  // and the loads of tile k + LOOK are issued in phase k), and two exchange
+  // buffers of packed P and dS per pair (written in phase k, read in k + 1).
+  constexpr int LOOK = 2, NSLOT = LOOK + 2;
   constexpr int ROWS_PER_INSTR = 1024 / T::RB;        // tile rows per 1 KiB load instruction
   constexpr int INSTR = T::BYTES / 1024;              // per tensor per tile
-  constexpr int PER_WAVE = INSTR / 4;                 // per wave
-  constexpr int LOADS = 2 * PER_WAVE;                 // Q and dO loads per wave per tile
-  static_assert(PER_WAVE >= 1 && INSTR % 4 == 0, "tile must split over the four waves");
-  // Per slot: the Q and dO tiles and the tile's row statistics (lse2,
-  // delta) of its 32 rows, 256 bytes that wave 0 loads with one instruction
-  // (lane l: row l / 2, statistic l % 2).
+  constexpr int PER_WAVE = INSTR / 4;                 // per consumer wave
+  static_assert(PER_WAVE >= 1 && INSTR % 4 == 0, "tile must split over the four consumer waves");
   auto qbuf = [](auto I) { return slot_buf<0, decltype(I)::value % NSLOT, T::BYTES>(); };
   auto obuf = [](auto I) { return slot_buf<1, decltype(I)::value % NSLOT, T::BYTES>(); };
   auto rsb = [](auto I) { return reinterpret_cast<float(*)[2]>(slot_buf<2, decltype(I)::value % NSLOT, 8 * kRows>()); };
+  // exchange buffer: per pair, packed P then packed dS, 32 bytes each per lane
+  auto xbuf = [](auto I) { return slot_buf<3, decltype(I)::value % 2, 4 * 2 * 64 * 32>(); };
   const LdsOffsets<D> off(lane);
-  // Causal mask of a tile's S as an addend: -inf where this lane's key lies
-  // past the row's limit, 0 elsewhere (register r holds query row
-  // 8 (r / 4) + 4 half + r % 4).  Only a tile whose first row does not see
-  // every key of the wave needs it (the limits do not decrease along the
-  // rows); all other tiles skip it.
-  const int wave_last_key = min(key0 + wave * 32 + 31, A.Lkv - 1);
-  auto needs_mask = [&](int row0) __attribute__((always_inline)) -> bool {
-    return A.causal && llim<LAYOUT>(A, w.q_rank, w.kv_rank, row0) < wave_last_key;
-  };
-  auto mask_init = [&](int row0) __attribute__((always_inline)) -> f32x16 {
-    f32x16 m;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
-      const int lim = i < A.Lq ? llim<LAYOUT>(A, w.q_rank, w.kv_rank, i) : -1;
-      m[r] = my_key > lim ? kNegInf : 0.f;
-    }
-    return m;
-  };
-  const int64_t plane_elems = G.n_tok * D;
-  const unsigned rec_rows = (unsigned)(G.n_tok * T::RB);   // bytes of one (b, h) plane
-  const unsigned rec_rs = (unsigned)(G.n_tok * 8);          // bytes of its row statistics
 
-  // Tile it: head hkv*group + it / nqt, query tile qt0 + it % nqt.  issue()
-  // is called for it = 0, 1, 2, ... in order, so it keeps the head and the
-  // query tile of the next call (no division per tile) and that head's
-  // buffer descriptors.  Lane l of load instruction i fills LDS slot 64 i + l
-  // of the tile: row ROWS_PER_INSTR i + l / CPR, chunk slot l % CPR holding
-  // logical chunk (l % CPR) ^ dswz(row).  In the contiguous and striped
-  // layouts a tile's rows are an arithmetic sequence of natural rows, so
-  // the row base goes into the scalar offset and each lane's vector offset
-  // is a constant; zigzag tiles and the ragged last tile of a head take
-  // per-lane offsets, rows past the block set out of the buffer's range
-  // (they read zeros).  A tile index past the last one issues the same loads
-  // with every offset out of range (they write zeros into the slot and
-  // touch no memory), so that the loop body has no branch around them: the
-  // compiler would otherwise sink the MFMAs of a step into the block after
-  // it, away from the exponentials they are meant to overlap.
+  // ---- consumer side: the tile loads -------------------------------------
+  // Tile it: head hkv*group + it / nqt, query tile qt0 + it % nqt, issued in
+  // order, so the next call's head and query tile are kept (no division per
+  // tile).  Lane l of load instruction i fills LDS slot 64 i + l of the tile:
+  // row ROWS_PER_INSTR i + l / CPR, chunk slot l % CPR holding logical chunk
+  // (l % CPR) ^ dswz(row).  Contiguous and striped tiles are arithmetic
+  // sequences of natural rows: the row base goes into the scalar offset and
+  // each lane's vector offset is a constant.  Zigzag tiles and a head's ragged
+  // last tile take per-lane offsets, rows past the block out of the buffer's
+  // range (they read zeros); a tile index past the last one loads zeros.
+  // Consumer 0 also loads the tile's row statistics (lse2, delta): 256 bytes,
+  // lane l: row l / 2, statistic l % 2.
+  const int64_t plane_elems = G.n_tok * D;
+  const unsigned rec_rows = (unsigned)(G.n_tok * T::RB);
+  const unsigned rec_rs = (unsigned)(G.n_tok * 8);
   constexpr bool kAffine = LAYOUT != 2;
-  const int row_stride = LAYOUT == 1 ? A.P : 1;             // natural rows between consecutive block rows
+  const int row_stride = LAYOUT == 1 ? A.P : 1;
   int voff_row[PER_WAVE], rr_row[PER_WAVE], qchunk[PER_WAVE];
 #pragma unroll
   for (int u = 0; u < PER_WAVE; ++u) {
-    const int ins = wave * PER_WAVE + u;
+    const int ins = cw * PER_WAVE + u;
     rr_row[u] = ins * ROWS_PER_INSTR + lane / T::CPR;
     qchunk[u] = 16 * ((lane % T::CPR) ^ dswz<D>(rr_row[u]));
     voff_row[u] = rr_row[u] * row_stride * T::RB + qchunk[u];
   }
   const int voff_rs = (lane >> 1) * row_stride * 8 + 4 * (lane & 1);
-  int is_h = 0, is_qt = 0;
-  // plane bases of the head being issued (advanced by one plane per head)
+  int is_qt = 0;
   const int64_t qplane0 = (int64_t)w.b * A.H + w.hkv * group;
   unsigned short* qbase = const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(A.q)) + qplane0 * plane_elems;
   unsigned short* obase =
@@ -394,21 +379,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
       const unsigned nat0 = LAYOUT == 0 ? (unsigned)(w.q_rank * A.Lq + row0) : (unsigned)(row0 * A.P + w.q_rank);
 #pragma unroll
       for (int u = 0; u < PER_WAVE; ++u) {
-        const int ins = wave * PER_WAVE + u;
+        const int ins = cw * PER_WAVE + u;
         lds_load16(rq, qbuf(slot) + ins * 1024, voff_row[u], nat0 * T::RB);
         lds_load16(ro, obuf(slot) + ins * 1024, voff_row[u], nat0 * T::RB);
       }
-      if (wave == 0) lds_load4(rr, &rsb(slot)[0][0], voff_rs, nat0 * 8);
+      if (cw == 0) lds_load4(rr, &rsb(slot)[0][0], voff_rs, nat0 * 8);
     } else {
 #pragma unroll
       for (int u = 0; u < PER_WAVE; ++u) {
-        const int ins = wave * PER_WAVE + u;
+        const int ins = cw * PER_WAVE + u;
         const int i = row0 + rr_row[u];
         const int voff = (valid && i < A.Lq) ? lrow<LAYOUT>(w.q_rank, i, A.Lq, A.P) * T::RB + qchunk[u] : (int)rec_rows;
         lds_load16(rq, qbuf(slot) + ins * 1024, voff, 0u);
         lds_load16(ro, obuf(slot) + ins * 1024, voff, 0u);
       }
-      if (wave == 0) {
+      if (cw == 0) {
         const int i = row0 + (lane >> 1);
         const int voff = (valid && i < A.Lq) ? lrow<LAYOUT>(w.q_rank, i, A.Lq, A.P) * 8 + 4 * (lane & 1) : (int)rec_rs;
         lds_load4(rr, &rsb(slot)[0][0], voff, 0u);
@@ -416,195 +401,137 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
     }
     if (valid && ++is_qt == nqt) {
       is_qt = 0;
-      ++is_h;
       qbase += plane_elems;
       obase += plane_elems;
       rbase += G.n_tok * 2;
     }
   };
-  // Loads still in flight that a wave may leave behind at the end of a tile:
-  // those of the newest tile (wave 0 also loads its row statistics).
-  auto wait_newest = [&]() __attribute__((always_inline)) {
-    if (wave == 0) wait_vmcnt<LOADS + 1>();
-    else wait_vmcnt<LOADS>();
+  // Loads a consumer may leave in flight at the end of a phase: those of the
+  // LOOK - 1 newest tiles (consumer 0 also loads each tile's row statistics).
+  constexpr int LOADS = 2 * PER_WAVE;
+  auto wait_landed = [&]() __attribute__((always_inline)) {
+    if (cw == 0) wait_vmcnt<(LOOK - 1) * (LOADS + 1)>();
+    else wait_vmcnt<(LOOK - 1) * LOADS>();
   };
-  // query tile of tile t for the mask: cs_qt follows the consumed tiles
-  int cs_qt = 0;
 
-  // S and dP of a tile: [32 queries x 32 keys], one key per lane column;
-  // register r holds query 8 (r / 4) + 4 half + r % 4 of the tile.
-  f32x16 sc = f32x16{}, dpc = f32x16{};
-  if (total > 0) {
-    static_for<LOOK>([&](auto I) __attribute__((always_inline)) {
-      if (decltype(I)::value < total) issue(decltype(I)::value, I);
+  // Each role runs its own copy of the phase loop (same phases, same
+  // barriers), so that the producers' resident K / V rows and the
+  // consumers' accumulators are never live in the same code and the
+  // register allocator gives each role the whole per-wave budget.
+  // Phase k (0 <= k <= total): producers produce tile k (k < total) into
+  // exchange buffer k % 2; consumers consume tile k - 1 (k >= 1) and issue the
+  // loads of tile k + LOOK.  The slot of tile k is k % NSLOT.
+  const int n_phases = total > 0 ? total + 1 : 0;
+  auto run_phases = [&](auto&& phase) __attribute__((always_inline)) {
+    int k = 0;
+    for (; k + NSLOT <= n_phases; k += NSLOT)
+      static_for<NSLOT>([&](auto i) __attribute__((always_inline)) { phase(i, k + decltype(i)::value); });
+    static_for<NSLOT - 1>([&](auto i) __attribute__((always_inline)) {
+      if (k + decltype(i)::value < n_phases) phase(i, k + decltype(i)::value);
     });
-    wait_vmcnt0();
-    __syncthreads();
-    if (needs_mask(qt0 * kRows)) sc = mask_init(qt0 * kRows);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(qbuf(IC<0>{}), off, ks), kf[ks], sc, 0, 0, 0);
-      dpc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(obuf(IC<0>{}), off, ks), vf[ks], dpc, 0, 0, 0);
-    }
-  }
+  };
 
-  // One iteration per query tile t, cut into one-MFMA-pair steps fenced with
-  // sched_barrier.  Step i issues
-  //   S(t+1) (even i) or dP(t+1) (odd i): one MFMA, 2 accumulators;
-  //   dV^T += dO^T P(t-1) (even i) or dK^T += Q^T dS(t-1) (odd i): one MFMA,
-  //   2 NDB accumulators;
-  // and the VALU turns one element of S(t), dP(t) into P(t), dS(t).  The
-  // MFMA pipe therefore always has 2 + 2 NDB independent chains in flight
-  // and the exponentials hide under them.  Tile t's slot keeps (Q, dO)
-  // until the dV/dK products of iteration t+1, so five slots are needed:
-  // t-1 (transposed reads), t (row statistics), t+1 (row reads), t+2
-  // (landing), t+3 (loading).
-  bf16x8 pbp[2], dsbp[2];   // packed P(t-1), dS(t-1)
-  auto body = [&](auto slot_tag, auto hasb_tag, int t) __attribute__((always_inline)) {
-    bf16x8 pbn[2], dsbn[2];  // packed P(t), dS(t), filled pair by pair
-    float p_prev = 0.f, ds_prev = 0.f;
-    constexpr int SL = decltype(slot_tag)::value;          // t % NSLOT
-    constexpr int SN = (SL + 1) % NSLOT;                   // tile t+1
-    constexpr int SP = (SL + NSLOT - 1) % NSLOT;           // tile t-1
-    constexpr int SF = (SL + LOOK) % NSLOT;                // tile t+3 (the slot held t-2)
-    constexpr bool HASB = decltype(hasb_tag)::value;       // t >= 1
-    issue(t + LOOK, IC<SF>{});
-    // (S(t+1), dP(t+1) are computed even for the last tile: the slot holds
-    // stale rows then and the results are not used.)
-    constexpr int NA = 2 * KS;        // S / dP MFMAs per tile
-    constexpr int NB = 4 * NDB;       // dV / dK MFMAs per tile
-    static_assert(NA == NB, "one S/dP and one dV/dK MFMA per step");
-    constexpr int PFA = 4, PFB = 3;   // steps whose operands are read ahead
-    auto afrag = [&](int i) __attribute__((always_inline)) -> bf16x8 {
-      return (i & 1) ? read_rowfrag<D>(obuf(IC<SN>{}), off, i >> 1) : read_rowfrag<D>(qbuf(IC<SN>{}), off, i >> 1);
-    };
-    // dV on even steps, dK on odd ones; (db, hc) = ((j / 2) % NDB, (j / 2) / NDB)
-    auto bfrag = [&](int j) __attribute__((always_inline)) -> bf16x8 {
-      const int db = (j >> 1) % NDB, hc = (j >> 1) / NDB;
-      return (j & 1) ? read_trfrag<D>(qbuf(IC<SP>{}), off, db, hc) : read_trfrag<D>(obuf(IC<SP>{}), off, db, hc);
-    };
-    bf16x8 fa[PFA], fb[PFB];
-#pragma unroll
-    for (int i = 0; i < PFA; ++i) fa[i] = afrag(i);
-    if constexpr (HASB) {
-#pragma unroll
-      for (int j = 0; j < PFB; ++j) fb[j] = bfrag(j);
+  if (producer) {
+    // ---- producer: S, dP, P, dS ------------------------------------------
+    bf16x8 kf[KS], vf[KS];
+    {
+      const int64_t src_row =
+          G.kv_staged ? ((int64_t)w.q_rank * A.B * A.Hkv + kv_plane) * A.Lkv + (key_ok ? my_key : 0) : key_row;
+      load_row_frags<D>(kf, reinterpret_cast<const unsigned short*>(A.k), src_row, key_ok, half);
+      load_row_frags<D>(vf, reinterpret_cast<const unsigned short*>(A.v), src_row, key_ok, half);
     }
-    // Row statistics of tile t (lse2, delta) in groups of four rows (rows
-    // 8 g + 4 half .. + 3, loaded by wave g), each group read one group ahead
-    // of its use.
-    float lv[2][4], dv[2][4];
-    auto rowstats = [&](int g, int k) __attribute__((always_inline)) {
-      const int q0 = 8 * g + 4 * half;
-      const float4 a4 = *reinterpret_cast<const float4*>(&rsb(IC<SL>{})[q0][0]);
-      const float4 b4 = *reinterpret_cast<const float4*>(&rsb(IC<SL>{})[q0 + 2][0]);
-      lv[k][0] = a4.x; dv[k][0] = a4.y; lv[k][1] = a4.z; dv[k][1] = a4.w;
-      lv[k][2] = b4.x; dv[k][2] = b4.y; lv[k][3] = b4.z; dv[k][3] = b4.w;
-    };
-    f32x16 sn, dpn;
-    rowstats(0, 0);
-    static_for<NA>([&](auto ic) __attribute__((always_inline)) {
-      constexpr int i = decltype(ic)::value;
-      {
-        const bf16x8 a = fa[i % PFA];
-        if constexpr (i + PFA < NA) fa[i % PFA] = afrag(i + PFA);
-        if constexpr (i == 0) mfma_v_z(sn, a, kf[0]);
-        else if constexpr (i == 1) mfma_v_z(dpn, a, vf[0]);
-        else if constexpr ((i & 1) == 0) mfma_v(sn, a, kf[i >> 1]);
-        else mfma_v(dpn, a, vf[i >> 1]);
+    // Causal mask: -inf where this lane's key lies past the row's limit
+    // (register r holds query row 8 (r / 4) + 4 half + r % 4); only for tiles
+    // whose first row does not see every key of the pair.
+    const int pair_last_key = min(key0 + pw * 32 + 31, A.Lkv - 1);
+    int cs_qt = 0;  // query tile (within its head) of the tile being produced
+    auto produce = [&](auto slot, auto xs) __attribute__((always_inline)) {
+      const int row0 = (qt0 + cs_qt) * kRows;
+      cs_qt = cs_qt + 1 == nqt ? 0 : cs_qt + 1;
+      f32x16 sc = f32x16{}, dpc = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(qbuf(slot), off, ks), kf[ks], sc, 0, 0, 0);
+        dpc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(obuf(slot), off, ks), vf[ks], dpc, 0, 0, 0);
       }
-      if constexpr (HASB) {
-        constexpr int db = (i >> 1) % NDB, hc = (i >> 1) / NDB;
-        const bf16x8 b = fb[i % PFB];
-        if constexpr (i + PFB < NB) fb[i % PFB] = bfrag(i + PFB);
-        if constexpr ((i & 1) == 0) mfma_a(dvT[db], b, pbp[hc]);
-        else mfma_a(dkT[db], b, dsbp[hc]);
-      }
-      // VALU: the 16 elements of tile t spread over the NA steps (the causal
-      // mask is already in S: masked scores are -inf, their P and dS 0).
-      static_for<16>([&](auto rc) __attribute__((always_inline)) {
-        constexpr int r = decltype(rc)::value;
-        if constexpr (r * NA / 16 == i) {
-          constexpr int g = r >> 2, k = g & 1;
-          if constexpr ((r & 3) == 0 && g + 1 < 4) rowstats(g + 1, k ^ 1);
-          float x = sc[r];
-          asm volatile("" : "+v"(x));   // (keeps the element's arithmetic in this step)
-          float p = fast_exp2(__builtin_fmaf(x, c, -lv[k][r & 3]));   // 0 where masked (S = -inf)
-          float ds = p * (dpc[r] - dv[k][r & 3]);
-          asm volatile("" : "+v"(p), "+v"(ds));
-          if constexpr (r & 1) {
-            pbn[r >> 3][(r & 7) - 1] = (__bf16)p_prev;
-            pbn[r >> 3][r & 7] = (__bf16)p;
-            dsbn[r >> 3][(r & 7) - 1] = (__bf16)ds_prev;
-            dsbn[r >> 3][r & 7] = (__bf16)ds;
-          } else {
-            p_prev = p;
-            ds_prev = ds;
-          }
+      if (A.causal && llim<LAYOUT>(A, w.q_rank, w.kv_rank, row0) < pair_last_key) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int lim = i < A.Lq ? llim<LAYOUT>(A, w.q_rank, w.kv_rank, i) : -1;
+          if (my_key > lim) sc[r] = kNegInf;
         }
-      });
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    mfma_settle(sn, dpn);   // S(t+1), dP(t+1) are read by the VALU from here on
-    // the causal mask of S(t+1), only when its first row does not see every
-    // key of the wave (masked scores become -inf, so their P and dS are 0)
-    const int qt_next = cs_qt + 1 == nqt ? 0 : cs_qt + 1;
-    cs_qt = qt_next;
-    if (needs_mask((qt0 + qt_next) * kRows)) {
-      const f32x16 m = mask_init((qt0 + qt_next) * kRows);
+      }
+      bf16x8 pb[2], dsb[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sn[r] += m[r];
-    }
+      for (int g = 0; g < 4; ++g) {
+        // row statistics of rows 8 g + 4 half + e
+        const int q0 = 8 * g + 4 * half;
+        const float4 a4 = *reinterpret_cast<const float4*>(&rsb(slot)[q0][0]);
+        const float4 b4 = *reinterpret_cast<const float4*>(&rsb(slot)[q0 + 2][0]);
+        const float lv[4] = {a4.x, a4.z, b4.x, b4.z};
+        const float dv[4] = {a4.y, a4.w, b4.y, b4.w};
 #pragma unroll
-    for (int hc = 0; hc < 2; ++hc) {
-      pbp[hc] = pbn[hc];
-      dsbp[hc] = dsbn[hc];
-    }
-    sc = sn;
-    dpc = dpn;
-    // tile t+2 must have landed before the next iteration reads it: only
-    // tile t+3's loads (issued above) may still be in flight
-    wait_newest();
-    wait_lgkmcnt0();
-    barrier_no_fence();
-  };
-  // The dV / dK products of the last tile, alone.
-  auto drain = [&](auto slot_tag) __attribute__((always_inline)) {
-    constexpr int SP = decltype(slot_tag)::value;
-    constexpr int NB = 4 * NDB;
-    static_for<NB>([&](auto jc) __attribute__((always_inline)) {
-      constexpr int j = decltype(jc)::value;
-      constexpr int db = (j >> 1) % NDB, hc = (j >> 1) / NDB;
-      if constexpr ((j & 1) == 0)
-        dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_trfrag<D>(obuf(IC<SP>{}), off, db, hc), pbp[hc],
-                                                          dvT[db], 0, 0, 0);
-      else
-        dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_trfrag<D>(qbuf(IC<SP>{}), off, db, hc), dsbp[hc],
-                                                          dkT[db], 0, 0, 0);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const float pr = fast_exp2(__builtin_fmaf(sc[r], c, -lv[e]));   // 0 where masked (S = -inf)
+          const float ds = pr * (dpc[r] - dv[e]);
+          pb[r >> 3][r & 7] = (__bf16)pr;
+          dsb[r >> 3][r & 7] = (__bf16)ds;
+        }
+      }
+      // hand P, dS to the consumer: lane-major, 2 x 16 bytes each
+      unsigned char* xb = xbuf(xs) + pw * (2 * 64 * 32);
+      *reinterpret_cast<bf16x8*>(xb + lane * 32) = pb[0];
+      *reinterpret_cast<bf16x8*>(xb + lane * 32 + 16) = pb[1];
+      *reinterpret_cast<bf16x8*>(xb + 64 * 32 + lane * 32) = dsb[0];
+      *reinterpret_cast<bf16x8*>(xb + 64 * 32 + lane * 32 + 16) = dsb[1];
+    };
+    if (n_phases > 0) barrier_no_fence();   // the consumers' first tile loads have landed
+    run_phases([&](auto kc, int k) __attribute__((always_inline)) {
+      constexpr int K = decltype(kc)::value;   // k % NSLOT (NSLOT is even: k % 2 == K % 2)
+      if (k < total) produce(IC<K>{}, IC<K>{});
+      wait_lgkmcnt0();   // exchange writes done, slot reads done
+      barrier_no_fence();
     });
-  };
-
-  using Yes = std::integral_constant<bool, true>;
-  using No = std::integral_constant<bool, false>;
-  if (total > 0) {
-    body(IC<0>{}, No{}, 0);
-    int t = 1;
-    for (; t + NSLOT - 1 < total; t += NSLOT)   // t % NSLOT == 1
-      static_for<NSLOT>([&](auto k) __attribute__((always_inline)) {
-        body(IC<(decltype(k)::value + 1) % NSLOT>{}, Yes{}, t + decltype(k)::value);
-      });
-    static_for<NSLOT - 1>([&](auto k) __attribute__((always_inline)) {
-      if (t + decltype(k)::value < total) body(IC<(decltype(k)::value + 1) % NSLOT>{}, Yes{}, t + decltype(k)::value);
-    });
-    switch ((total - 1) % NSLOT) {
-      case 0: drain(IC<0>{}); break;
-      case 1: drain(IC<1>{}); break;
-      case 2: drain(IC<2>{}); break;
-      case 3: drain(IC<3>{}); break;
-      default: drain(IC<4>{}); break;
-    }
-    wait_vmcnt0();   // the last iterations' loads past the end (zeros into free slots)
+    return;
   }
+
+  // ---- consumer: dV^T += dO^T P, dK^T += Q^T dS; the tile loads ----------
+  f32x16 dvT[NDB], dkT[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dvT[db] = dkT[db] = f32x16{};
+  auto consume = [&](auto slot, auto xs) __attribute__((always_inline)) {
+    const unsigned char* xb = xbuf(xs) + pw * (2 * 64 * 32);
+    const bf16x8 pb0 = *reinterpret_cast<const bf16x8*>(xb + lane * 32);
+    const bf16x8 pb1 = *reinterpret_cast<const bf16x8*>(xb + lane * 32 + 16);
+    const bf16x8 ds0 = *reinterpret_cast<const bf16x8*>(xb + 64 * 32 + lane * 32);
+    const bf16x8 ds1 = *reinterpret_cast<const bf16x8*>(xb + 64 * 32 + lane * 32 + 16);
+#pragma unroll
+    for (int hc = 0; hc < 2; ++hc)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_trfrag<D>(obuf(slot), off, db, hc), hc ? pb1 : pb0,
+                                                          dvT[db], 0, 0, 0);
+        dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_trfrag<D>(qbuf(slot), off, db, hc), hc ? ds1 : ds0,
+                                                          dkT[db], 0, 0, 0);
+      }
+  };
+  if (n_phases > 0) {
+    static_for<LOOK>([&](auto I) __attribute__((always_inline)) { issue(decltype(I)::value, I); });
+    wait_landed();     // tile 0 is in LDS
+    barrier_no_fence();
+    run_phases([&](auto kc, int k) __attribute__((always_inline)) {
+      constexpr int K = decltype(kc)::value;
+      issue(k + LOOK, IC<K + LOOK>{});
+      if (k >= 1) consume(IC<K + NSLOT - 1>{}, IC<K + 1>{});
+      wait_landed();     // tile k + 1 is in LDS for the producers' next phase
+      wait_lgkmcnt0();   // exchange and slot reads done before they are rewritten
+      barrier_no_fence();
+    });
+    wait_vmcnt0();       // loads past the end (zeros into free slots)
+  }
+
   // (A key tile no query sees still writes its zeros on the first launch
   // and its final values on the last.)
   const bool first = G.first != 0;
@@ -804,7 +731,7 @@ hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, 
 
 template <int D, int L>
 hipError_t launch_dkdv_t(const BwdArgs& a, unsigned g, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, L>), dim3(g), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, L>), dim3(g), dim3(kDkdvThreads), 0, s, a);
   return hipGetLastError();
 }
 
