@@ -333,8 +333,8 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   auto qbuf = [](auto I) { return slot_buf<0, decltype(I)::value % NSLOT, T::BYTES>(); };
   auto obuf = [](auto I) { return slot_buf<1, decltype(I)::value % NSLOT, T::BYTES>(); };
   auto rsb = [](auto I) { return reinterpret_cast<float(*)[2]>(slot_buf<2, decltype(I)::value % NSLOT, 8 * kRows>()); };
-  // exchange buffer: per pair, packed P then packed dS, 32 bytes each per lane
-  auto xbuf = [](auto I) { return slot_buf<3, decltype(I)::value % 2, 4 * 2 * 64 * 32>(); };
+  // exchange buffer: per pair 4 KiB (packed P and dS of the pair's tile)
+  auto xbuf = [](auto I) { return slot_buf<3, decltype(I)::value % 2, 4 * 4096>(); };
   const LdsOffsets<D> off(lane);
 
   // ---- consumer side: the tile loads -------------------------------------
@@ -480,12 +480,13 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
           dsb[r >> 3][r & 7] = (__bf16)ds;
         }
       }
-      // hand P, dS to the consumer: lane-major, 2 x 16 bytes each
-      unsigned char* xb = xbuf(xs) + pw * (2 * 64 * 32);
-      *reinterpret_cast<bf16x8*>(xb + lane * 32) = pb[0];
-      *reinterpret_cast<bf16x8*>(xb + lane * 32 + 16) = pb[1];
-      *reinterpret_cast<bf16x8*>(xb + 64 * 32 + lane * 32) = dsb[0];
-      *reinterpret_cast<bf16x8*>(xb + 64 * 32 + lane * 32 + 16) = dsb[1];
+      // hand P, dS to the consumer: four 1 KiB rows (P halves, dS halves),
+      // 16 bytes per lane, consecutive lanes at consecutive 16-byte chunks
+      unsigned char* xb = xbuf(xs) + pw * 4096;
+      *reinterpret_cast<bf16x8*>(xb + lane * 16) = pb[0];
+      *reinterpret_cast<bf16x8*>(xb + 1024 + lane * 16) = pb[1];
+      *reinterpret_cast<bf16x8*>(xb + 2048 + lane * 16) = dsb[0];
+      *reinterpret_cast<bf16x8*>(xb + 3072 + lane * 16) = dsb[1];
     };
     if (n_phases > 0) barrier_no_fence();   // the consumers' first tile loads have landed
     run_phases([&](auto kc, int k) __attribute__((always_inline)) {
@@ -502,11 +503,11 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dvT[db] = dkT[db] = f32x16{};
   auto consume = [&](auto slot, auto xs) __attribute__((always_inline)) {
-    const unsigned char* xb = xbuf(xs) + pw * (2 * 64 * 32);
-    const bf16x8 pb0 = *reinterpret_cast<const bf16x8*>(xb + lane * 32);
-    const bf16x8 pb1 = *reinterpret_cast<const bf16x8*>(xb + lane * 32 + 16);
-    const bf16x8 ds0 = *reinterpret_cast<const bf16x8*>(xb + 64 * 32 + lane * 32);
-    const bf16x8 ds1 = *reinterpret_cast<const bf16x8*>(xb + 64 * 32 + lane * 32 + 16);
+    const unsigned char* xb = xbuf(xs) + pw * 4096;
+    const bf16x8 pb0 = *reinterpret_cast<const bf16x8*>(xb + lane * 16);
+    const bf16x8 pb1 = *reinterpret_cast<const bf16x8*>(xb + 1024 + lane * 16);
+    const bf16x8 ds0 = *reinterpret_cast<const bf16x8*>(xb + 2048 + lane * 16);
+    const bf16x8 ds1 = *reinterpret_cast<const bf16x8*>(xb + 3072 + lane * 16);
 #pragma unroll
     for (int hc = 0; hc < 2; ++hc)
 #pragma unroll
