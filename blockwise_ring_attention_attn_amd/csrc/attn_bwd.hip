@@ -325,7 +325,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   // is read by the producers in phase k and by the consumers in phase k + 1,
   // and the loads of tile k + LOOK are issued in phase k), and two exchange
   // buffers of packed P and dS per pair (written in phase k, read in k + 1).
-  constexpr int LOOK = 2, NSLOT = LOOK + 2;
+  constexpr int LOOK = 4, NSLOT = LOOK + 2;
   constexpr int ROWS_PER_INSTR = 1024 / T::RB;        // tile rows per 1 KiB load instruction
   constexpr int INSTR = T::BYTES / 1024;              // per tensor per tile
   constexpr int PER_WAVE = INSTR / 4;                 // per consumer wave
