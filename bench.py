@@ -286,6 +286,8 @@ def run_backward(args) -> dict:
     return {"metric": "causal ring-attn bwd TFLOP/s (10 d per unmasked pair)", "value": tflops, "unit": "TFLOP/s",
             "ms_per_step": ms, "steps": n, "flops_per_step": flops,
             "pct_bf16_mfma_peak": 100.0 * tflops / MFMA_BF16_PEAK_TFLOPS,
+            "mfma_busy": {k: measured_mfma_busy(f"{k}<128>:backward_prefill_32k", "attn_bwd.hip")
+                          for k in ("bwd_dkdv_kernel", "bwd_dq_kernel")},
             "config": {"workload": "backward of the prefill workload (same shapes, upstream gradient seeded)"}}
 
 
