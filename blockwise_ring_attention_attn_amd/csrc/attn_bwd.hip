@@ -221,31 +221,6 @@ __device__ __forceinline__ void emit_block(float* acc_row, __bf16* out_row, cons
   }
 }
 
-// v_mfma_f32_32x32x16_bf16 as volatile inline asm, so that it keeps its
-// place among a step's other instructions (the builtin is a pure function
-// the optimizer moves freely, and in the dK/dV loop it gathered the MFMAs
-// at the end of the tile, after all the exponentials).  The accumulator
-// lives in VGPRs (_v) or AGPRs (_a); _z starts it from zero.  The compiler
-// does not know these are MFMAs, so a VALU read of the result must come
-// after mfma_settle (18 wait states cover the longest MFMA).
-// (The zero-start form marks its result early-clobber: an MFMA must not
-// write registers it still reads.)
-__device__ __forceinline__ void mfma_v_z(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_a(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
-// The same wait states, with the accumulators passing through them: no VALU
-// read of these results can be scheduled before the wait.
-__device__ __forceinline__ void mfma_settle(f32x16& x, f32x16& y) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y) :: "memory");
-}
-
 // ---------------------------------------------------------------------------
 // dK / dV: one workgroup per (query host, batch, kv head, 128-key tile).  It
 // sweeps, for every query head of the kv head's group, the 32-row query
