@@ -272,16 +272,15 @@ def ring_attn_bwd(q, k, v, out, dout, lse, *, P: int, causal: bool, layout: str 
                   scale: float | None = None, dq=None, dk=None, dv=None, ws=None, stream=None):
     """Gradients of ring_attn_fwd by recomputation over a reverse ring.
 
-    q, out, dout [B, H, N, d]; k, v [B, Hkv, N, d] (bf16); lse [B, H, N] fp32
-    from the forward.  Returns (dq, dk, dv) shaped like q, k, v.
+    q, out, dout [B, H, N, d]; k, v [B, Hkv, N, d] (all bf16 or all fp32);
+    lse [B, H, N] fp32 from the forward.  Returns (dq, dk, dv) shaped like
+    q, k, v, in their dtype.
     """
     torch = _torch()
     lib = load()
     B, H, Hkv, Nq, N, d, code = _qkv(q, k, v)
     if Nq != N:
         raise ValueError("q and k, v must hold the same N tokens")
-    if code != RA_BF16:
-        raise TypeError("ring_attn_bwd supports bfloat16 only")
     _tensor(out, "out", (B, H, N, d), q.dtype)
     _tensor(dout, "dout", (B, H, N, d), q.dtype)
     _tensor(lse, "lse", (B, H, N), torch.float32)

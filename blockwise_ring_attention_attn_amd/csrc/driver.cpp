@@ -725,13 +725,14 @@ struct BwdWs {
   bool overflow;
 };
 
-static BwdWs bwd_ws_layout(int B, int H, int Hkv, long long N, int d, int P) {
+static BwdWs bwd_ws_layout(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype) {
   BwdWs w{};
   SizeAcc a;
-  // two staging buffers of K and V for the reverse ring (bf16, host-major)
+  // two staging buffers of K and V for the reverse ring (input dtype, host-major)
   if (P > 1) {
-    w.off_stage[0] = a.add({(uint64_t)B, (uint64_t)Hkv, (uint64_t)N, (uint64_t)d, 2});
-    w.kv_bytes = a.add({(uint64_t)B, (uint64_t)Hkv, (uint64_t)N, (uint64_t)d, 2}) - w.off_stage[0];
+    const uint64_t es = esize(dtype);
+    w.off_stage[0] = a.add({(uint64_t)B, (uint64_t)Hkv, (uint64_t)N, (uint64_t)d, es});
+    w.kv_bytes = a.add({(uint64_t)B, (uint64_t)Hkv, (uint64_t)N, (uint64_t)d, es}) - w.off_stage[0];
     w.off_stage[1] = a.add({2, w.kv_bytes});
   }
   w.off_rowstat = a.add({(uint64_t)B, (uint64_t)H, (uint64_t)N, 8});
@@ -743,21 +744,21 @@ static BwdWs bwd_ws_layout(int B, int H, int Hkv, long long N, int d, int P) {
   return w;
 }
 
-// The backward kernels read q, dO and the row statistics of a whole
-// (batch, head) plane through buffer descriptors with 32-bit offsets.
+// The bf16 backward kernels read q, dO and the row statistics of a whole
+// (batch, head) plane through buffer descriptors with 32-bit offsets; the
+// fp32 kernels use plain 64-bit addressing.
 ra_status bwd_args(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype, float scale) {
   ra_status st = check_common(B, H, Hkv, N, d, P, dtype, scale);
   if (st != RA_OK) return st;
-  if (dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "ring_attn_bwd supports bf16 only");
-  if ((uint64_t)N * d * esize(dtype) >= kSpanLimit)
-    return fail(RA_EINVAL, "the backward needs one head plane (N * d elements) below 2 GiB");
+  if (dtype == RA_BF16 && (uint64_t)N * d * esize(dtype) >= kSpanLimit)
+    return fail(RA_EINVAL, "the bf16 backward needs one head plane (N * d elements) below 2 GiB");
   return RA_OK;
 }
 
 size_t ring_attn_bwd_ws_bytes(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype) {
   g_err.clear();
   if (bwd_args(B, H, Hkv, N, d, P, dtype, 1.f) != RA_OK) return SIZE_MAX;
-  const BwdWs W = bwd_ws_layout(B, H, Hkv, N, d, P);
+  const BwdWs W = bwd_ws_layout(B, H, Hkv, N, d, P, dtype);
   if (W.overflow) {
     fail(RA_ENOMEM, "workspace size exceeds the 48-bit device address space");
     return SIZE_MAX;
@@ -774,13 +775,15 @@ ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void*
   ra_status st = bwd_args(B, H, Hkv, N, d, P, dtype, scale);
   if (st != RA_OK) return st;
   if ((st = check_layout(layout, N, P)) != RA_OK) return st;
-  const BwdWs W = bwd_ws_layout(B, H, Hkv, N, d, P);
+  const BwdWs W = bwd_ws_layout(B, H, Hkv, N, d, P, dtype);
   if ((st = check_ws(W.overflow, W.total, ws, ws_bytes)) != RA_OK) return st;
   if ((st = check_tensor_align({q, k, v, out, dout, dq, dk, dv}, {lse})) != RA_OK) return st;
+  const bool f32 = dtype == RA_F32;
   const int64_t Bl = N / P;
   const int64_t nqt = (Bl + bwd_dq_rows() - 1) / bwd_dq_rows();
   const int64_t nkt = (Bl + bwd_dkdv_rows() - 1) / bwd_dkdv_rows();
-  if ((int64_t)P * B * H * nqt > 0x7fffffffLL || (int64_t)P * B * Hkv * nkt > 0x7fffffffLL)
+  if ((int64_t)P * B * H * nqt > 0x7fffffffLL || (int64_t)P * B * Hkv * nkt > 0x7fffffffLL ||
+      (f32 && (int64_t)P * B * H * Bl / 4 >= 0x7fffffffLL))
     return fail(RA_EINVAL, "problem too large for one launch");
   const int lay = effective_layout(layout, P);
   hipStream_t cs = static_cast<hipStream_t>(stream);
@@ -810,16 +813,22 @@ ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void*
   a.scale = scale;
   a.n_kvtiles = (int)nkt;
 
-  a.dq_out = static_cast<__bf16*>(dq);
-  a.dk_out = static_cast<__bf16*>(dk);
-  a.dv_out = static_cast<__bf16*>(dv);
+  if (f32) {
+    a.dq_out_f32 = static_cast<float*>(dq);
+    a.dk_out_f32 = static_cast<float*>(dk);
+    a.dv_out_f32 = static_cast<float*>(dv);
+  } else {
+    a.dq_out = static_cast<__bf16*>(dq);
+    a.dk_out = static_cast<__bf16*>(dk);
+    a.dv_out = static_cast<__bf16*>(dv);
+  }
 
   // Launch plan: step s pairs query host r with kv block (r + s) mod P; a
   // launch covers the hosts lo .. hi that have visible work at that step.
   // Step 0 (every host against its own block, which holds the diagonal)
   // has work for every host, so its launch writes the accumulators instead
   // of adding to them, and the last active step of a host (kv block) writes
-  // its dQ (dK, dV) in bf16: no separate clear or conversion pass.
+  // its dQ (dK, dV) in the output dtype: no separate clear or conversion pass.
   static_assert(kMaxP <= 64, "the last-step masks hold one bit per host");
   std::vector<int> lo_s(P, -1), hi_s(P, -1), last_q(P, -1), last_kv(P, -1);
   for (int s = 0; s < P; ++s)
@@ -850,11 +859,16 @@ ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void*
   if (staged && (st = get_ctx(&ctx)) != RA_OK) return st;
   std::unique_lock<std::mutex> enq;
   if (staged) enq = std::unique_lock<std::mutex>(ctx->enqueue);
-  const size_t row_bytes = (size_t)d * 2;
+  const size_t row_bytes = (size_t)d * esize(dtype);
   const int64_t planes = (int64_t)B * Hkv;
   const size_t host_bytes = (size_t)planes * Bl * row_bytes;
-  RA_HIP(launch_bwd_prep(out, dout, lse, const_cast<float*>(a.rowstat), (int64_t)B * H * N, d, cs),
-         "prep launch");
+  if (f32)
+    RA_HIP(launch_bwd_prep_f32(static_cast<const float*>(out), static_cast<const float*>(dout), lse,
+                               const_cast<float*>(a.rowstat), (int64_t)B * H * N, d, cs),
+           "prep launch");
+  else
+    RA_HIP(launch_bwd_prep(out, dout, lse, const_cast<float*>(a.rowstat), (int64_t)B * H * N, d, cs),
+           "prep launch");
   if (staged) {
     RA_HIP(hipEventRecord(ctx->fork, cs), "hipEventRecord");
     RA_HIP(hipStreamWaitEvent(ctx->copy, ctx->fork, 0), "hipStreamWaitEvent");
@@ -904,8 +918,8 @@ ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void*
     a.s.k = use_stage ? static_cast<const void*>(wsb + W.off_stage[i & 1]) : k;
     a.s.v = use_stage ? static_cast<const void*>(wsb + W.off_stage[i & 1] + W.kv_bytes) : v;
     RA_HIP(launch_spin(staged ? g_delay_compute_us : 0, cs), "delay");
-    RA_HIP(launch_bwd_dkdv(a, d, cs), "dK/dV kernel launch");
-    RA_HIP(launch_bwd_dq(a, d, cs), "dQ kernel launch");
+    RA_HIP(f32 ? launch_bwd_dkdv_f32(a, d, cs) : launch_bwd_dkdv(a, d, cs), "dK/dV kernel launch");
+    RA_HIP(f32 ? launch_bwd_dq_f32(a, d, cs) : launch_bwd_dq(a, d, cs), "dQ kernel launch");
     if (staged && i + 2 < n) RA_HIP(hipEventRecord(ctx->done[i & 1], cs), "hipEventRecord");
   }
   return RA_OK;

@@ -76,6 +76,10 @@ struct BwdArgs {
   // (q_rank * B + b) * Hkv + hkv of Lkv rows, in block order.  The dK / dV
   // accumulators always stay at the natural rows of the block.
   int kv_staged;
+  // fp32 backward: the final fp32 gradients (the bf16 outputs above unused)
+  float* dq_out_f32;
+  float* dk_out_f32;
+  float* dv_out_f32;
 };
 
 struct MergeArgs {
@@ -130,5 +134,11 @@ hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, 
                            hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, int d, hipStream_t s);
+// Backward (fp32): the same steps with fp32 inputs, arithmetic and outputs
+// (one wavefront per row; k / v rows in place or in host-major staging).
+hipError_t launch_bwd_prep_f32(const float* out, const float* dout, const float* lse, float* rowstat, int64_t rows,
+                               int d, hipStream_t s);
+hipError_t launch_bwd_dkdv_f32(const BwdArgs& a, int d, hipStream_t s);
+hipError_t launch_bwd_dq_f32(const BwdArgs& a, int d, hipStream_t s);
 
 }  // namespace ra

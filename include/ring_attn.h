@@ -235,12 +235,16 @@ ra_status ring_attn_decode_noalloc(const void* q, const void* k, const void* v, 
  *
  * q, out, dout, dq [B, H, N, d]; k, v, dk, dv [B, Hkv, N, d]; lse [B, H, N]
  * float32 as written by ring_attn_fwd for the same inputs (out and lse are
- * the forward's results); all in natural token order, element type bf16
- * (RA_F32 returns RA_EUNSUPPORTED).  With grouped-query attention dk, dv
- * sum the contributions of every query head of the group.  causal, layout,
- * scale, P: as for ring_attn_fwd; the result does not depend on layout or P
- * up to rounding.  dq, dk, dv are overwritten.  ws: at least
- * ring_attn_bwd_ws_bytes(...) bytes (fp32 accumulators and delta).
+ * the forward's results); all in natural token order, all of element type
+ * dtype.  RA_BF16: bf16 MFMA products with P and dS rounded to bf16 as
+ * operands, fp32 accumulation, bf16 gradients; one head plane (N * d) must
+ * stay below 2 GiB.  RA_F32: fp32 inputs, arithmetic and gradients (a
+ * plain, untuned path).  With grouped-query attention dk, dv sum the
+ * contributions of every query head of the group.  causal, layout, scale,
+ * P: as for ring_attn_fwd; the result does not depend on layout or P up to
+ * rounding.  dq, dk, dv are overwritten.  ws: at least
+ * ring_attn_bwd_ws_bytes(...) bytes (staging buffers for the reverse ring,
+ * fp32 accumulators and the row statistics).
  * ---------------------------------------------------------------------- */
 size_t ring_attn_bwd_ws_bytes(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype);
 ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,

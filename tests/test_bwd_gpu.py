@@ -1,4 +1,4 @@
-"""GPU parity of ring_attn_bwd (bf16) against the fp64 backward oracle.
+"""GPU parity of ring_attn_bwd (bf16 and fp32) against the fp64 backward oracle.
 
 The pages fix no tolerance for gradients, so each element is checked
 against a bound derived from the arithmetic of the bf16 path (it is stated
@@ -16,6 +16,12 @@ gradient entry is at most
 plus e |ref| for the output rounding, with e = 2^-8 (twice the bf16 unit
 roundoff, covering the fp32 exp / lse / accumulation terms).  The test
 asserts |got - ref| <= 2 * bound + 1e-6 everywhere.
+
+The fp32 path rounds nothing to bf16: the same bound with e = 2^-12 covers
+its fp32 dot products over d <= 128 terms (d u |s|), the forward's fp32 row
+sum over N <= 1024 keys behind lse (N u) and the gradients' sums over
+N <= 1024 terms (N u), u = 2^-24, with room to spare (2^-12 = 2.4e-4 against
+their 1.7e-4); a stray bf16 rounding (2^-9) would exceed it.
 """
 import math
 
@@ -29,17 +35,17 @@ from _util import from_dev, host_vals, to_dev
 
 pytestmark = pytest.mark.gpu
 
-EPS = 2.0 ** -8
+EPS = {"bf16": 2.0 ** -8, "f32": 2.0 ** -12}
 
 
-def _inputs(seed, B, H, Hkv, N, d):
-    print(f"\n[bwd case] seed={seed} B={B} H={H}/{Hkv} N={N} d={d}", flush=True)
-    q, k, v = synth.qkv(seed, B, H, Hkv, N, d, "bf16")
-    do = synth.tensor(seed, synth.TENSOR_DOUT, B, H, N, d, "bf16")
+def _inputs(seed, B, H, Hkv, N, d, dtype="bf16"):
+    print(f"\n[bwd case] seed={seed} B={B} H={H}/{Hkv} N={N} d={d} {dtype}", flush=True)
+    q, k, v = synth.qkv(seed, B, H, Hkv, N, d, dtype)
+    do = synth.tensor(seed, synth.TENSOR_DOUT, B, H, N, d, dtype)
     return q, k, v, do
 
 
-def _bounds(qh, kh, vh, doh, parts, B, H, Hkv, scale, dq_ref, dk_ref, dv_ref):
+def _bounds(qh, kh, vh, doh, parts, B, H, Hkv, scale, dq_ref, dk_ref, dv_ref, EPS):
     """Element-wise error bounds of the bf16 path (see the module docstring)."""
     group = H // Hkv
     bq = np.zeros_like(dq_ref)
@@ -62,23 +68,23 @@ def _bounds(qh, kh, vh, doh, parts, B, H, Hkv, scale, dq_ref, dk_ref, dv_ref):
     return bq, bk, bv
 
 
-def _run(seed, B, H, Hkv, N, d, P, causal, layout):
+def _run(seed, B, H, Hkv, N, d, P, causal, layout, dtype="bf16"):
     import torch
-    q, k, v, do = _inputs(seed, B, H, Hkv, N, d)
-    qd, kd, vd, dod = (to_dev(x, "bf16") for x in (q, k, v, do))
+    q, k, v, do = _inputs(seed, B, H, Hkv, N, d, dtype)
+    qd, kd, vd, dod = (to_dev(x, dtype) for x in (q, k, v, do))
     out, lse = ra.ring_attn_fwd(qd, kd, vd, P=P, causal=causal, layout=layout)
     dq, dk, dv = ra.ring_attn_bwd(qd, kd, vd, out, dod, lse, P=P, causal=causal, layout=layout)
     torch.cuda.synchronize()
     return q, k, v, do, from_dev(dq), from_dev(dk), from_dev(dv)
 
 
-def _check(seed, B, H, Hkv, N, d, P, causal, layout):
-    q, k, v, do, dq, dk, dv = _run(seed, B, H, Hkv, N, d, P, causal, layout)
-    qh, kh, vh, doh = (host_vals(x, "bf16") for x in (q, k, v, do))
+def _check(seed, B, H, Hkv, N, d, P, causal, layout, dtype="bf16"):
+    q, k, v, do, dq, dk, dv = _run(seed, B, H, Hkv, N, d, P, causal, layout, dtype)
+    qh, kh, vh, doh = (host_vals(x, dtype) for x in (q, k, v, do))
     scale = 1.0 / math.sqrt(d)
     dq_r, dk_r, dv_r, parts = oracle.attention_bwd(qh, kh, vh, doh, scale=scale, causal=causal, parts=True)
-    bq, bk, bv = _bounds(qh, kh, vh, doh, parts, B, H, Hkv, scale, dq_r, dk_r, dv_r)
-    what = f"bwd B={B} H={H}/{Hkv} N={N} d={d} P={P} causal={causal} {layout}"
+    bq, bk, bv = _bounds(qh, kh, vh, doh, parts, B, H, Hkv, scale, dq_r, dk_r, dv_r, EPS[dtype])
+    what = f"bwd B={B} H={H}/{Hkv} N={N} d={d} P={P} causal={causal} {layout} {dtype}"
     for name, got, ref, bnd in (("dq", dq, dq_r, bq), ("dk", dk, dk_r, bk), ("dv", dv, dv_r, bv)):
         assert np.all(np.isfinite(got)), f"{what}: non-finite {name}"
         err = np.abs(got - ref)
@@ -119,3 +125,19 @@ def test_bwd_layout_and_P_invariance():
         for a, b in zip(got, outs[0]):
             scale = np.abs(b).max()
             assert np.abs(a - b).max() <= 2e-2 * scale
+
+
+def test_bwd_fp32_single_head_noncausal_P4():
+    """The fp32 workload's shape (one head, N=1024, d=64, non-causal, P=4
+    ring blocks of 256) through the fp32 backward."""
+    _check(46, 1, 1, 1, 1024, 64, 4, False, "contiguous", "f32")
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
+def test_bwd_fp32_causal_gqa_layouts(layout):
+    """fp32, GQA 2:1, d = 128, P = 8, blocks of 66 rows."""
+    _check(47, 1, 4, 2, 16 * 33, 128, 8, True, layout, "f32")
+
+
+def test_bwd_fp32_batched_ragged():
+    _check(48, 2, 2, 1, 3 * 101, 64, 3, True, "striped", "f32")

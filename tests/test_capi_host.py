@@ -71,8 +71,8 @@ def test_ws_queries_flag_invalid_arguments(lib, args, frag):
 
 
 def test_other_ws_queries_flag_invalid_arguments(lib):
-    assert lib.ring_attn_bwd_ws_bytes(1, 2, 1, 64, 64, 4, ra.RA_F32) == SIZE_MAX
-    assert b"bf16 only" in lib.ra_last_error()
+    assert lib.ring_attn_bwd_ws_bytes(1, 2, 1, 64, 64, 4, 7) == SIZE_MAX
+    assert b"unknown dtype" in lib.ra_last_error()
     assert lib.ring_attn_bwd_ws_bytes(1, 2, 1, 65, 64, 4, ra.RA_BF16) == SIZE_MAX
     assert lib.ring_attn_bwd_ws_bytes(1, 1, 1, 1 << 24, 128, 8, ra.RA_BF16) == SIZE_MAX  # 4 GiB plane
     assert b"below 2 GiB" in lib.ra_last_error()
@@ -214,7 +214,7 @@ def _bwd(lib, **kw):
     (dict(N=65), ra.RA_EINVAL, "multiple of P"),
     (dict(H=3, Hkv=2), ra.RA_EINVAL, "multiple of Hkv"),
     (dict(P=65, N=65 * 4), ra.RA_EINVAL, "P must be"),
-    (dict(dtype=0), ra.RA_EUNSUPPORTED, "bf16 only"),
+    (dict(dtype=7), ra.RA_EINVAL, "unknown dtype"),
     (dict(ws_bytes=16), ra.RA_EINVAL, "workspace too small"),
     (dict(ws=None), ra.RA_EINVAL, "null workspace"),
     (dict(ws=100), ra.RA_EINVAL, "aligned"),
@@ -234,6 +234,18 @@ def test_bwd_ws_bytes_cover_fp32_gradients():
     assert need + stage <= got <= need + stage + (1 << 16)
     got1 = ra.load().ring_attn_bwd_ws_bytes(B, H, Hkv, N, d, 1, ra.RA_BF16)
     assert need <= got1 <= need + (1 << 16)
+
+
+def test_bwd_fp32_ws_bytes_and_plane_limit():
+    """The fp32 backward stages K and V in fp32 (4-byte elements) and, since
+    its kernels address with 64-bit pointers, has no 2 GiB plane limit."""
+    B, H, Hkv, N, d, P = 1, 4, 2, 4096, 64, 4
+    need = 4 * (B * H * N * d + 2 * B * Hkv * N * d + 2 * B * H * N)
+    stage = 2 * 2 * (B * Hkv * N * d * 4)
+    got = ra.load().ring_attn_bwd_ws_bytes(B, H, Hkv, N, d, P, ra.RA_F32)
+    assert need + stage <= got <= need + stage + (1 << 16)
+    lib = ra.load()
+    assert lib.ring_attn_bwd_ws_bytes(1, 1, 1, 1 << 24, 128, 8, ra.RA_F32) not in (0, SIZE_MAX)  # 8 GiB plane
 
 
 @pytest.mark.parametrize("kw,frag", [
@@ -341,8 +353,10 @@ def test_binding_rejects_bad_step_merge_finalize_decode_backward_arguments():
         ra.ring_attn_bwd(qb, kb, kb, qb, qb, lse, P=4, causal=True, dk=_t(1, 2, 64, 64))
     with pytest.raises(TypeError, match="lse must be"):
         ra.ring_attn_bwd(qb, kb, kb, qb, qb, lse.bfloat16(), P=4, causal=True)
-    with pytest.raises(TypeError, match="bfloat16 only"):
-        ra.ring_attn_bwd(qb.float(), kb.float(), kb.float(), qb.float(), qb.float(), lse, P=4, causal=True)
+    with pytest.raises(TypeError, match="k must be"):
+        ra.ring_attn_bwd(qb.float(), kb, kb, qb.float(), qb.float(), lse, P=4, causal=True)
+    with pytest.raises(TypeError, match="dq must be"):
+        ra.ring_attn_bwd(qb.float(), kb.float(), kb.float(), qb.float(), qb.float(), lse, P=4, causal=True, dq=qb)
     with pytest.raises(ValueError, match="device tensor"):
         ra.ring_attn_bwd(qb, kb, kb, qb, qb, lse, P=4, causal=True)
 

@@ -104,9 +104,11 @@ def test_step_state_checkpoint_resume():
     assert np.array_equal(out_full[0], out_res[0]) and np.array_equal(out_full[1], out_res[1])
 
 
-def _bwd_inputs(seed, B, H, Hkv, N, d, P, layout):
-    qd, kd, vd = _inputs(seed, B, H, Hkv, N, d)
-    do = to_dev(synth.tensor(seed, synth.TENSOR_DOUT, B, H, N, d, "bf16"), "bf16")
+def _bwd_inputs(seed, B, H, Hkv, N, d, P, layout, dtype="bf16"):
+    print(f"\n[driver bwd] seed={seed} B={B} H={H}/{Hkv} N={N} d={d} {dtype}", flush=True)
+    q, k, v = synth.qkv(seed, B, H, Hkv, N, d, dtype)
+    qd, kd, vd = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    do = to_dev(synth.tensor(seed, synth.TENSOR_DOUT, B, H, N, d, dtype), dtype)
     out, lse = ra.ring_attn_fwd(qd, kd, vd, P=P, causal=True, layout=layout)
     return qd, kd, vd, out, do, lse
 
@@ -166,3 +168,35 @@ def test_fwd_staged_equals_in_place(layout):
                                                          causal=True, layout=layout)]
     for a, b in zip(ref + ref_s, got + got_s):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("layout,delays", [("contiguous", (2000, 0)), ("zigzag", (0, 2000))])
+def test_bwd_fp32_reverse_ring_staging(layout, delays):
+    """The fp32 backward stages fp32 K and V blocks; staged under delays is
+    bitwise the in-place backward."""
+    args = _bwd_inputs(28, 1, 4, 2, 8 * 66, 64, 8, layout, "f32")
+    kw = dict(P=8, causal=True, layout=layout)
+    try:
+        ra.debug_set_staging(False)
+        ref = [from_dev(t) for t in ra.ring_attn_bwd(*args, **kw)]
+        ra.debug_set_staging(True)
+        ra.debug_set_delays(*delays)
+        got = [from_dev(t) for t in ra.ring_attn_bwd(*args, **kw)]
+    finally:
+        ra.debug_set_staging(True)
+        ra.debug_set_delays(0, 0)
+    for a, b in zip(ref, got):
+        assert np.all(np.isfinite(b)) and np.array_equal(a, b)
+
+
+def test_bwd_fp32_ignores_stale_workspace():
+    import torch
+    B, H, Hkv, N, d, P = 1, 2, 1, 8 * 40, 128, 8
+    args = _bwd_inputs(29, B, H, Hkv, N, d, P, "striped", "f32")
+    nb = ra.load().ring_attn_bwd_ws_bytes(B, H, Hkv, N, d, P, ra.RA_F32)
+    ws0 = torch.zeros(nb, dtype=torch.uint8, device="cuda:0")
+    wsn = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda:0")
+    a = [from_dev(t) for t in ra.ring_attn_bwd(*args, P=P, causal=True, layout="striped", ws=ws0)]
+    b = [from_dev(t) for t in ra.ring_attn_bwd(*args, P=P, causal=True, layout="striped", ws=wsn)]
+    for x, y in zip(a, b):
+        assert np.all(np.isfinite(y)) and np.array_equal(x, y)
