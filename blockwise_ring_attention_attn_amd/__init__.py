@@ -380,8 +380,6 @@ def _decode_args(q, k, v, out, lse):
     B, H, Hkv, one, L, d, code = _qkv(q, k, v)
     if one != 1:
         raise ValueError("q must be [B, H, 1, d]")
-    if code != RA_BF16:
-        raise TypeError("decode supports bfloat16 only")
     out, lse = _outputs(q, out, lse, (B, H))
     _devices(q=q, k=k, v=v)
     return B, H, Hkv, L, d, code, out, lse
@@ -389,7 +387,8 @@ def _decode_args(q, k, v, out, lse):
 
 def ring_attn_decode(q, k, v, *, P: int, scale: float | None = None, out=None, lse=None, ws=None,
                      stream=None):
-    """Split-KV decode: q [B, H, 1, d]; k, v [B, Hkv, L, d] -> (out [B, H, 1, d], lse [B, H])."""
+    """Split-KV decode: q [B, H, 1, d]; k, v [B, Hkv, L, d] (all bf16 or all
+    fp32) -> (out [B, H, 1, d] in their dtype, lse [B, H] fp32)."""
     lib = load()
     B, H, Hkv, L, d, code, out, lse = _decode_args(q, k, v, out, lse)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)

@@ -1030,7 +1030,6 @@ void decode_split(int B, int Hkv, long long L, int P, int64_t* chunk, int* cpb) 
 ra_status decode_args(int B, int H, int Hkv, long long L, int d, int P, ra_dtype dtype, float scale) {
   ra_status st = check_common(B, H, Hkv, L, d, P, dtype, scale);
   if (st != RA_OK) return st;
-  if (dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "decode supports bf16 only");
   if (H / Hkv > 16) return fail(RA_EINVAL, "H/Hkv must be <= 16 (got %d)", H / Hkv);
   return RA_OK;
 }
@@ -1060,7 +1059,8 @@ DecodeWs decode_ws_layout(int B, int H, int Hkv, long long L, int d, int P) {
 // Shared by ring_attn_decode and ring_attn_decode_noalloc: argument checks
 // past the workspace, then the partial and merge launches on `stream`.
 ra_status decode_launch(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Hkv,
-                        long long L, int d, int P, float scale, const DecodeWs& W, void* wsb_, void* stream) {
+                        long long L, int d, int P, float scale, ra_dtype dtype, const DecodeWs& W, void* wsb_,
+                        void* stream) {
   ra_status st = check_tensor_align({q, k, v, out}, {lse});
   if (st != RA_OK) return st;
   if ((int64_t)B * Hkv * P * W.cpb > 0x7fffffffLL) return fail(RA_EINVAL, "problem too large");
@@ -1082,12 +1082,14 @@ ra_status decode_launch(const void* q, const void* k, const void* v, void* out, 
   a.scale_log2 = scale * 1.4426950408889634f;
   hipStream_t cs = static_cast<hipStream_t>(stream);
   {
-    const double bytes = 2.0 * B * Hkv * (double)L * d * 2 + (double)B * H * d * 2 +
+    const double es = (double)esize(dtype);
+    const double bytes = 2.0 * B * Hkv * (double)L * d * es + (double)B * H * d * es +
                          (double)B * H * a.S * (d + 1) * 4;
     ProfScope ps(cs, bytes, 1);
-    RA_HIP(launch_decode_partial(a, d, 1, cs), "decode partial launch");
+    if (dtype == RA_BF16) RA_HIP(launch_decode_partial(a, d, 1, cs), "decode partial launch");
+    else RA_HIP(launch_decode_partial_f32(a, d, cs), "decode partial launch");
   }
-  RA_HIP(launch_decode_merge(a, d, 1, cs), "decode merge launch");
+  RA_HIP(launch_decode_merge(a, d, dtype == RA_BF16 ? 1 : 0, cs), "decode merge launch");
   return RA_OK;
 }
 
@@ -1116,7 +1118,7 @@ ra_status ring_attn_decode(const void* q, const void* k, const void* v, void* ou
   const DecodeWs W = decode_ws_layout(B, H, Hkv, L, d, P);
   if ((st = check_ws(W.overflow, W.total, ws, ws_bytes)) != RA_OK) return st;
   if (!ws) return fail(RA_EINVAL, "null workspace");
-  return decode_launch(q, k, v, out, lse, B, H, Hkv, L, d, P, scale, W, ws, stream);
+  return decode_launch(q, k, v, out, lse, B, H, Hkv, L, d, P, scale, dtype, W, ws, stream);
 }
 
 ra_status ring_attn_decode_noalloc(const void* q, const void* k, const void* v, void* out, float* lse, int B,
@@ -1134,7 +1136,7 @@ ra_status ring_attn_decode_noalloc(const void* q, const void* k, const void* v, 
   void* scratch = nullptr;
   size_t scratch_bytes = 0;
   RA_HIP(decode_scratch(&scratch, &scratch_bytes), "hipGetSymbolAddress(decode scratch)");
-  return decode_launch(q, k, v, out, lse, B, H, Hkv, L, d, P, scale, W, scratch, stream);
+  return decode_launch(q, k, v, out, lse, B, H, Hkv, L, d, P, scale, dtype, W, scratch, stream);
 }
 
 ra_status ra_debug_set_delays(int compute_us, int copy_us) {

@@ -116,6 +116,9 @@ hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, int out_bf16, hipStream_t s);
 hipError_t launch_decode_partial(const DecodeArgs& a, int d, int bf16, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs& a, int d, int bf16, hipStream_t s);
+// fp32 partial pass: the same grid, split order and partial layout as
+// launch_decode_partial (four waves per split, one partial per wave).
+hipError_t launch_decode_partial_f32(const DecodeArgs& a, int d, hipStream_t s);
 // Size of the static decode scratch (ring_attn_decode_noalloc).
 constexpr size_t kDecodeScratchBytes = 64ull << 20;
 // Device address and size of the static decode scratch on the current

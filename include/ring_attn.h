@@ -197,9 +197,13 @@ ra_status lse_merge(float* o_a, float* lse_a, const float* o_b, const float* lse
  * are merged with the lse_merge rule, chunks within a ring block first, then
  * the ring blocks in order.
  *
- * q, out [B, H, 1, d]; k, v [B, Hkv, L, d]; lse [B, H] float32.  The query
- * sees every cached key (no mask).  Requires L % P == 0 and H / Hkv <= 16.
- * ws: at least ring_attn_decode_ws_bytes(...) bytes.
+ * q, out [B, H, 1, d]; k, v [B, Hkv, L, d], all of element type dtype;
+ * lse [B, H] float32.  RA_BF16: bf16 MFMA products with the weights rounded
+ * to bf16 as the P V operand, fp32 accumulation.  RA_F32: fp32 throughout (a
+ * plain, untuned partial pass).  The partials are fp32 for both, so the
+ * workspace does not depend on dtype.  The query sees every cached key (no
+ * mask).  Requires L % P == 0 and H / Hkv <= 16.  ws: at least
+ * ring_attn_decode_ws_bytes(...) bytes.
  * ---------------------------------------------------------------------- */
 size_t ring_attn_decode_ws_bytes(int B, int H, int Hkv, long long L, int d, int P);
 ra_status ring_attn_decode(const void* q, const void* k, const void* v, void* out, float* lse,

@@ -164,8 +164,10 @@ def test_merge_decode_reject_invalid(lib):
     assert lib.lse_merge(None, 1, 1, 1, 4, 8, None) == ra.RA_EINVAL
     assert lib.lse_merge(1, 1, 1, 1, 4, 0, None) == ra.RA_EINVAL
     assert lib.ring_attn_finalize(1, 1, 1, 1, 1, 4, 2000, 1, None) == ra.RA_EINVAL
-    # decode: f32 unsupported, group > 16, L % P
-    assert lib.ring_attn_decode(1, 1, 1, 1, 1, 1, 32, 1, 64, 64, 4, 0.1, 0, None, 256, 1 << 30) == ra.RA_EUNSUPPORTED
+    # decode: unknown dtype, group > 16 (bf16 and fp32), L % P
+    assert lib.ring_attn_decode(1, 1, 1, 1, 1, 1, 4, 1, 64, 64, 4, 0.1, 7, None, 256, 1 << 30) == ra.RA_EINVAL
+    assert b"unknown dtype" in lib.ra_last_error()
+    assert lib.ring_attn_decode(1, 1, 1, 1, 1, 1, 32, 1, 64, 64, 4, 0.1, 0, None, 256, 1 << 30) == ra.RA_EINVAL
     assert lib.ring_attn_decode(1, 1, 1, 1, 1, 1, 32, 1, 64, 64, 4, 0.1, 1, None, 256, 1 << 30) == ra.RA_EINVAL
     assert lib.ring_attn_decode(1, 1, 1, 1, 1, 1, 4, 1, 66, 64, 4, 0.1, 1, None, 256, 1 << 30) == ra.RA_EINVAL
 

@@ -275,16 +275,16 @@ def test_lse_merge_against_oracle():
     assert np.all(from_dev(ta)[5:10] == 0) and np.all(np.isneginf(from_dev(tla)[5:10]))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("B,H,Hkv,L,d,P", [(2, 8, 2, 8 * 1000, 128, 8), (3, 4, 4, 4 * 77, 64, 4),
                                            (1, 16, 1, 2 * 4096, 128, 2), (2, 2, 2, 1, 128, 1)])
-def test_decode_against_oracle(B, H, Hkv, L, d, P):
+def test_decode_against_oracle(B, H, Hkv, L, d, P, dtype):
     import torch
-    dtype = "bf16"
     q, k, v = _case(12, B, H, Hkv, L, d, dtype, Nq=1)
     out, lse = ra.ring_attn_decode(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), P=P)
     torch.cuda.synchronize()
     Ow, Lw = oracle.decode(host_vals(q, dtype), host_vals(k, dtype), host_vals(v, dtype))
-    assert_close(from_dev(out), from_dev(lse), Ow, Lw[:, :, 0], dtype, f"decode B={B} H={H}/{Hkv} L={L}")
+    assert_close(from_dev(out), from_dev(lse), Ow, Lw[:, :, 0], dtype, f"decode B={B} H={H}/{Hkv} L={L} {dtype}")
 
 
 @pytest.mark.parametrize("L,P", [(24, 8), (200, 4), (1000, 8)])
