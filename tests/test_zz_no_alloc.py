@@ -1,6 +1,7 @@
 """ring_attn_decode_noalloc (static scratch, no workspace) against
 ring_attn_decode (caller workspace): the same kernels, so the results must
-be bit-identical, and both within the bf16 tolerance of the fp64 oracle.
+be bit-identical, and both within the tolerance of the fp64 oracle (bf16
+and fp32).
 Two calls in a row, the second with a smaller input (the scratch keeps the
 first call's partials; every call rewrites the ones it reads)."""
 import numpy as np
@@ -14,20 +15,21 @@ from _util import assert_close, from_dev, host_vals, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _one(seed, B, H, Hkv, L, d, P):
+def _one(seed, B, H, Hkv, L, d, P, dtype="bf16"):
     import torch
-    print(f"\n[noalloc] B={B} H={H}/{Hkv} L={L} d={d} P={P}", flush=True)
-    q, k, v = synth.qkv(seed, B, H, Hkv, L, d, "bf16", Nq=1)
-    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    print(f"\n[noalloc] B={B} H={H}/{Hkv} L={L} d={d} P={P} {dtype}", flush=True)
+    q, k, v = synth.qkv(seed, B, H, Hkv, L, d, dtype, Nq=1)
+    qd, kd, vd = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
     out_ws, lse_ws = ra.ring_attn_decode(qd, kd, vd, P=P)
     out = torch.full_like(qd, float("nan"))
     lse = torch.full((B, H), float("nan"), device=qd.device)
     ra.ring_attn_decode_noalloc(qd, kd, vd, P=P, out=out, lse=lse)
     torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.int16), out_ws.view(torch.int16))
+    bits = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(out.view(bits), out_ws.view(bits))
     assert torch.equal(lse, lse_ws)
-    Ow, Lw = oracle.decode(host_vals(q, "bf16"), host_vals(k, "bf16"), host_vals(v, "bf16"))
-    assert_close(from_dev(out), from_dev(lse), Ow, Lw[:, :, 0], "bf16", f"decode_noalloc B={B} L={L}")
+    Ow, Lw = oracle.decode(host_vals(q, dtype), host_vals(k, dtype), host_vals(v, dtype))
+    assert_close(from_dev(out), from_dev(lse), Ow, Lw[:, :, 0], dtype, f"decode_noalloc B={B} L={L} {dtype}")
 
 
 def test_noalloc_matches_workspace_decode_twice():
@@ -35,3 +37,8 @@ def test_noalloc_matches_workspace_decode_twice():
     # 262144-key cache), then a smaller problem that reuses the array
     _one(31, 16, 32, 8, 8192, 128, 8)
     _one(32, 2, 8, 2, 8 * 1000, 64, 8)
+
+
+def test_noalloc_fp32_matches_workspace_decode_twice():
+    _one(33, 4, 8, 2, 4 * 2048, 128, 4, "f32")
+    _one(34, 1, 4, 4, 8 * 100, 64, 8, "f32")
