@@ -27,7 +27,13 @@
  *  - `stream` is a hipStream_t (passed as void*; NULL = the null stream).
  *    Every call is asynchronous with respect to the host.  Calls that use a
  *    second stream internally fork it from `stream` and join it back before
- *    returning, so callers see ordinary single-stream semantics.
+ *    returning, so callers see ordinary single-stream semantics.  A call
+ *    allocates, frees, synchronizes and clears nothing once the library has
+ *    set up its per-device stream and events (on the first call that stages
+ *    key/value blocks), so a later call may be captured into a HIP graph on
+ *    `stream`; the second stream joins the capture through the fork event.
+ *    The graph replays the call with the pointers and sizes it was captured
+ *    with.
  *  - Errors: a call returns RA_OK or an error code BEFORE launching anything
  *    when an argument is invalid (RA_EINVAL: null pointer, N % P != 0,
  *    H % Hkv != 0, unsupported d, workspace too small, ...).  RA_ENOMEM:

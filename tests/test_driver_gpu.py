@@ -200,3 +200,70 @@ def test_bwd_fp32_ignores_stale_workspace():
     b = [from_dev(t) for t in ra.ring_attn_bwd(*args, P=P, causal=True, layout="striped", ws=wsn)]
     for x, y in zip(a, b):
         assert np.all(np.isfinite(y)) and np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("op", ["fwd", "share", "bwd", "decode"])
+def test_graph_capture_replays(op):
+    """The calls allocate nothing and order their two streams with events, so
+    a caller can capture one into a HIP graph (the staging copies on the
+    library's second stream join the capture through the fork event).  Each
+    of three replays, with outputs overwritten by eager fills and the device
+    synchronized in between, is bitwise the eager call."""
+    import torch
+    B, H, Hkv, N, d, P = 1, 4, 2, 8 * 256, 128, 8
+    print(f"\n[graph] {op}", flush=True)
+    q, k, v = synth.qkv(31, B, H, Hkv, N, d, "bf16")
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    dev = qd.device
+    if op == "fwd":
+        ws = torch.empty(ra.ring_attn_fwd_ws_bytes(B, H, Hkv, N, d, P, ra.RA_BF16), dtype=torch.uint8, device=dev)
+        outs = (torch.empty_like(qd), torch.empty((B, H, N), dtype=torch.float32, device=dev))
+
+        def call():
+            ra.ring_attn_fwd(qd, kd, vd, P=P, causal=True, layout="striped", out=outs[0], lse=outs[1], ws=ws)
+    elif op == "share":
+        qs = qd[:, :, :N // P].contiguous()
+        ws = torch.empty(ra.load().ring_attn_fwd_share_ws_bytes(B, H, Hkv, N, d, P, ra.RA_BF16), dtype=torch.uint8,
+                         device=dev)
+        outs = (torch.empty_like(qs), torch.empty((B, H, N // P), dtype=torch.float32, device=dev))
+
+        def call():
+            ra.ring_attn_fwd_share(qs, kd, vd, P=P, rank=5, causal=True, layout="contiguous", out=outs[0],
+                                   lse=outs[1], ws=ws)
+    elif op == "bwd":
+        do = to_dev(synth.tensor(31, synth.TENSOR_DOUT, B, H, N, d, "bf16"), "bf16")
+        o, lse = ra.ring_attn_fwd(qd, kd, vd, P=P, causal=True, layout="zigzag")
+        ws = torch.empty(ra.load().ring_attn_bwd_ws_bytes(B, H, Hkv, N, d, P, ra.RA_BF16), dtype=torch.uint8,
+                         device=dev)
+        outs = (torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd))
+
+        def call():
+            ra.ring_attn_bwd(qd, kd, vd, o, do, lse, P=P, causal=True, layout="zigzag", dq=outs[0], dk=outs[1],
+                             dv=outs[2], ws=ws)
+    else:
+        q1 = qd[:, :, :1].contiguous()
+        ws = torch.empty(ra.ring_attn_decode_ws_bytes(B, H, Hkv, N, d, P), dtype=torch.uint8, device=dev)
+        outs = (torch.empty_like(q1), torch.empty((B, H), dtype=torch.float32, device=dev))
+
+        def call():
+            ra.ring_attn_decode(q1, kd, vd, P=P, out=outs[0], lse=outs[1], ws=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()   # eager, on a side stream (the library sets up its per-device stream and events here)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = [from_dev(t) for t in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for r in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [from_dev(t) for t in outs]
+        for a, b in zip(ref, got):
+            assert np.array_equal(a, b), f"{op}: replay {r} differs from the eager call"
