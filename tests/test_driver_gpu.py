@@ -267,3 +267,46 @@ def test_graph_capture_replays(op):
         got = [from_dev(t) for t in outs]
         for a, b in zip(ref, got):
             assert np.array_equal(a, b), f"{op}: replay {r} differs from the eager call"
+
+
+def test_concurrent_calls_from_two_threads():
+    """Two host threads, each with its own stream, inputs and workspace, run
+    staged forward rings at the same time (ctypes releases the interpreter
+    lock, so the enqueues interleave in the library; the per-device copy
+    stream and its events are shared).  Every result is bitwise the one the
+    same call gives alone."""
+    import threading
+    import torch
+    B, H, Hkv, N, d, P = 1, 4, 2, 8 * 256, 128, 8
+    cases = []
+    for i, layout in enumerate(("contiguous", "striped")):
+        q, k, v = synth.qkv(40 + i, B, H, Hkv, N, d, "bf16")
+        qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+        ref = [from_dev(t) for t in ra.ring_attn_fwd(qd, kd, vd, P=P, causal=True, layout=layout)]
+        ws = torch.empty(ra.ring_attn_fwd_ws_bytes(B, H, Hkv, N, d, P, ra.RA_BF16), dtype=torch.uint8,
+                         device=qd.device)
+        cases.append(dict(q=qd, k=kd, v=vd, layout=layout, ref=ref, ws=ws, stream=torch.cuda.Stream(), got=[]))
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(c):
+        try:
+            with torch.cuda.stream(c["stream"]):
+                for _ in range(4):
+                    o, lse = ra.ring_attn_fwd(c["q"], c["k"], c["v"], P=P, causal=True, layout=c["layout"],
+                                              ws=c["ws"], stream=c["stream"])
+                    c["got"].append((o, lse))
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(c,)) for c in cases]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for c in cases:
+        assert len(c["got"]) == 4
+        for o, lse in c["got"]:
+            assert np.array_equal(from_dev(o), c["ref"][0]) and np.array_equal(from_dev(lse), c["ref"][1])
