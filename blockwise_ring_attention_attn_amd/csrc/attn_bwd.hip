@@ -300,7 +300,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   // is read by the producers in phase k and by the consumers in phase k + 1,
   // and the loads of tile k + LOOK are issued in phase k), and two exchange
   // buffers of packed P and dS per pair (written in phase k, read in k + 1).
-  constexpr int LOOK = 4, NSLOT = LOOK + 2;
+  constexpr int LOOK = 2, NSLOT = LOOK + 2;
   constexpr int ROWS_PER_INSTR = 1024 / T::RB;        // tile rows per 1 KiB load instruction
   constexpr int INSTR = T::BYTES / 1024;              // per tensor per tile
   constexpr int PER_WAVE = INSTR / 4;                 // per consumer wave
@@ -423,12 +423,25 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
     auto produce = [&](auto slot, auto xs) __attribute__((always_inline)) {
       const int row0 = (qt0 + cs_qt) * kRows;
       cs_qt = cs_qt + 1 == nqt ? 0 : cs_qt + 1;
+      // Q and dO fragments read two MFMA steps (four MFMAs) ahead of use
+      constexpr int RA = 2;
       f32x16 sc = f32x16{}, dpc = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(qbuf(slot), off, ks), kf[ks], sc, 0, 0, 0);
-        dpc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(obuf(slot), off, ks), vf[ks], dpc, 0, 0, 0);
-      }
+      bf16x8 qa[RA], oa[RA];
+      static_for<RA>([&](auto I) __attribute__((always_inline)) {
+        qa[decltype(I)::value] = read_rowfrag<D>(qbuf(slot), off, decltype(I)::value);
+        oa[decltype(I)::value] = read_rowfrag<D>(obuf(slot), off, decltype(I)::value);
+      });
+      static_for<KS>([&](auto T_) __attribute__((always_inline)) {
+        constexpr int t = decltype(T_)::value;
+        const bf16x8 a = qa[t % RA], o = oa[t % RA];
+        if constexpr (t + RA < KS) {
+          qa[t % RA] = read_rowfrag<D>(qbuf(slot), off, t + RA);
+          oa[t % RA] = read_rowfrag<D>(obuf(slot), off, t + RA);
+        }
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[t], sc, 0, 0, 0);
+        dpc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, vf[t], dpc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
       if (A.causal && llim<LAYOUT>(A, w.q_rank, w.kv_rank, row0) < pair_last_key) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -618,12 +631,25 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
     if (t + LOOK < ntiles) issue(t + LOOK, IC<SF>{});   // its slot held tile t-1, done before the barrier
     const unsigned char* kt = kbuf(IC<SL>{});
     const unsigned char* vt = vbuf(IC<SL>{});
+    // K and V fragments read two MFMA steps (four MFMAs) ahead of use
+    constexpr int RA = 2;
     f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(kt, off, ks), qf[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rowfrag<D>(vt, off, ks), of[ks], dp, 0, 0, 0);
-    }
+    bf16x8 ka[RA], va[RA];
+    static_for<RA>([&](auto I) __attribute__((always_inline)) {
+      ka[decltype(I)::value] = read_rowfrag<D>(kt, off, decltype(I)::value);
+      va[decltype(I)::value] = read_rowfrag<D>(vt, off, decltype(I)::value);
+    });
+    static_for<KS>([&](auto T_) __attribute__((always_inline)) {
+      constexpr int t = decltype(T_)::value;
+      const bf16x8 a = ka[t % RA], b = va[t % RA];
+      if constexpr (t + RA < KS) {
+        ka[t % RA] = read_rowfrag<D>(kt, off, t + RA);
+        va[t % RA] = read_rowfrag<D>(vt, off, t + RA);
+      }
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, of[t], dp, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
     // causal limit per element, only on the tiles past the wave's fully
     // visible prefix (the limits do not decrease along the rows)
     if (t * kRows + kRows - 1 > wave_first_lim) {
