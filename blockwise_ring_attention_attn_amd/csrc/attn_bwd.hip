@@ -496,15 +496,25 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
     const bf16x8 pb1 = *reinterpret_cast<const bf16x8*>(xb + 1024 + lane * 16);
     const bf16x8 ds0 = *reinterpret_cast<const bf16x8*>(xb + 2048 + lane * 16);
     const bf16x8 ds1 = *reinterpret_cast<const bf16x8*>(xb + 3072 + lane * 16);
-#pragma unroll
-    for (int hc = 0; hc < 2; ++hc)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_trfrag<D>(obuf(slot), off, db, hc), hc ? pb1 : pb0,
-                                                          dvT[db], 0, 0, 0);
-        dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_trfrag<D>(qbuf(slot), off, db, hc), hc ? ds1 : ds0,
-                                                          dkT[db], 0, 0, 0);
+    // dO^T and Q^T fragments read two steps (four MFMAs) ahead of use
+    constexpr int NST = 2 * NDB, RA = 2;
+    bf16x8 ta[RA], tb[RA];
+    static_for<RA>([&](auto I) __attribute__((always_inline)) {
+      constexpr int st = decltype(I)::value;
+      ta[st] = read_trfrag<D>(obuf(slot), off, st % NDB, st / NDB);
+      tb[st] = read_trfrag<D>(qbuf(slot), off, st % NDB, st / NDB);
+    });
+    static_for<NST>([&](auto T_) __attribute__((always_inline)) {
+      constexpr int st = decltype(T_)::value, db = st % NDB, hc = st / NDB;
+      const bf16x8 a = ta[st % RA], b = tb[st % RA];
+      if constexpr (st + RA < NST) {
+        ta[st % RA] = read_trfrag<D>(obuf(slot), off, (st + RA) % NDB, (st + RA) / NDB);
+        tb[st % RA] = read_trfrag<D>(qbuf(slot), off, (st + RA) % NDB, (st + RA) / NDB);
       }
+      dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, hc ? pb1 : pb0, dvT[db], 0, 0, 0);
+      dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, hc ? ds1 : ds0, dkT[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
   if (n_phases > 0) {
     static_for<LOOK>([&](auto I) __attribute__((always_inline)) { issue(decltype(I)::value, I); });
