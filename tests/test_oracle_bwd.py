@@ -3,7 +3,6 @@ than itself: central finite differences of the (separately pinned) forward
 oracle, exact invariants of the softmax Jacobian, special cases with closed
 forms, and the grouped-query identity.  CPU only.
 """
-import math
 
 import numpy as np
 import pytest

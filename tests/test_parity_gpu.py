@@ -6,7 +6,6 @@ binding).  Tolerances: fp32 max|dO|, max|dlse| <= 1e-5; bf16 max|dO| <= 1e-2,
 max|dlse| <= 1e-3.
 """
 import math
-import sys
 
 import numpy as np
 import pytest

@@ -4,7 +4,6 @@ be bit-identical, and both within the tolerance of the fp64 oracle (bf16
 and fp32).
 Two calls in a row, the second with a smaller input (the scratch keeps the
 first call's partials; every call rewrites the ones it reads)."""
-import numpy as np
 import pytest
 
 import blockwise_ring_attention_attn_amd as ra
