@@ -39,12 +39,14 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 METRIC = "causal ring-attn fwd TFLOP/s + % bf16 MFMA peak; split-KV decode HBM GB/s"
 
-PREFILL = dict(B=1, H=32, Hkv=32, N=32768, d=128, P=8, layout="contiguous", causal=True, seed=2)
-# The two other full-size forward workloads, measured beside the headline one
-# (same kernel, other shapes): the striped GQA ring, and the last rank's share
-# of a 1,048,576-token ring (its q block against all eight kv blocks).
-STRIPED = dict(B=1, H=8, Hkv=2, N=131072, d=128, P=8, layout="striped", causal=True, seed=3)
+# The headline workload: the last rank's share of a 1,048,576-token ring (its
+# q block against all eight kv blocks), the largest that fits one GPU.
 SHARE = dict(B=1, H=4, Hkv=4, N=1048576, d=128, P=8, rank=7, layout="contiguous", causal=True, seed=4)
+# The two other full-size forward workloads, measured beside it (same kernel,
+# other shapes): the causal contiguous 32k prefill (whose backward the bench
+# also times) and the striped GQA ring.
+PREFILL = dict(B=1, H=32, Hkv=32, N=32768, d=128, P=8, layout="contiguous", causal=True, seed=2)
+STRIPED = dict(B=1, H=8, Hkv=2, N=131072, d=128, P=8, layout="striped", causal=True, seed=3)
 DECODE = dict(B=16, H=32, Hkv=8, L=262144, d=128, P=8, seed=5)
 
 
