@@ -6,11 +6,12 @@
 // (cmlonder.com) for the decode-time KV-cache footprint that makes this
 // pass bound by HBM bandwidth.
 //
-// The pass streams every key/value row from HBM exactly once and uses it
-// for all H/Hkv query heads of its group.  Scores S^T = K Q^T run on
+// The pass streams every key/value row from HBM once per sub-group of 16
+// query heads of its group (once in all for H/Hkv <= 16) and uses it for
+// all heads of the sub-group.  Scores S^T = K Q^T run on
 // v_mfma_f32_16x16x32_bf16 with K as the A operand loaded straight from
-// global memory (16 contiguous bytes per lane) and the group's query heads
-// as the 16 MFMA columns (only H/Hkv of them are real).  V goes through a
+// global memory (16 contiguous bytes per lane) and the sub-group's query
+// heads as the 16 MFMA columns (the columns past the group are zero).  V goes through a
 // per-wave LDS transpose so that O^T = V^T P^T runs on the same MFMA with P
 // taken straight from the score registers.  Each wavefront writes one
 // normalized partial (O, lse); a second kernel merges the partials of each
@@ -56,12 +57,16 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs A) {
   const int lc = lane & 15;    // MFMA column = query head within the group
   unsigned short* vt = vt_all[wave];
 
-  // blockIdx -> (b, hkv, split) with the split index fastest.
+  // blockIdx -> (b, hkv, sub-group, split) with the split index fastest; a
+  // sub-group is 16 query heads of the kv head's group (the MFMA columns).
   const int S_blk = A.P * A.chunks_per_block;
   const int split = blockIdx.x % S_blk;
-  const int bh = blockIdx.x / S_blk;
+  const int rest = blockIdx.x / S_blk;
+  const int sg = rest % A.sub_groups;
+  const int bh = rest / A.sub_groups;
   const int hkv = bh % A.Hkv;
   const int b = bh / A.Hkv;
+  const int hq = sg * 16 + lc;   // this lane column's query head within the group
   const int p = split / A.chunks_per_block;
   const int cidx = split % A.chunks_per_block;
   int64_t k_begin = (int64_t)p * A.block + (int64_t)cidx * A.chunk;
@@ -77,8 +82,8 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs A) {
   // Query heads of the group as B operand columns (zero beyond the group).
   bf16x8 qf[D / 32];
   {
-    const bool live = lc < A.group;
-    const int h = hkv * A.group + (live ? lc : 0);
+    const bool live = hq < A.group;
+    const int h = hkv * A.group + (live ? hq : 0);
     const unsigned short* Q = reinterpret_cast<const unsigned short*>(A.q) +
                               ((int64_t)b * A.H + h) * D;
 #pragma unroll
@@ -231,8 +236,8 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs A) {
   l_tot += __shfl_xor(l_tot, 32);
   float lb_tot = lb_run + __shfl_xor(lb_run, 16);
   lb_tot += __shfl_xor(lb_tot, 32);
-  if (lc >= A.group) return;
-  const int h = hkv * A.group + lc;
+  if (hq >= A.group) return;
+  const int h = hkv * A.group + hq;
   const int S_all = A.S;
   const int sidx = split * kWaves + wave;
   const int64_t pidx = ((int64_t)b * A.H + h) * S_all + sidx;
@@ -336,7 +341,7 @@ hipError_t decode_scratch(void** ptr, size_t* bytes) {
 
 hipError_t launch_decode_partial(const DecodeArgs& a, int d, int bf16, hipStream_t s) {
   if (!bf16) return hipErrorInvalidValue;
-  const int64_t g = (int64_t)a.B * a.Hkv * a.P * a.chunks_per_block;
+  const int64_t g = (int64_t)a.B * a.Hkv * a.sub_groups * a.P * a.chunks_per_block;
   if (g <= 0) return hipSuccess;
   if (d == 128) hipLaunchKernelGGL(decode_partial_kernel<128>, dim3((unsigned)g), dim3(256), 0, s, a);
   else if (d == 64) hipLaunchKernelGGL(decode_partial_kernel<64>, dim3((unsigned)g), dim3(256), 0, s, a);

@@ -1030,7 +1030,6 @@ void decode_split(int B, int Hkv, long long L, int P, int64_t* chunk, int* cpb) 
 ra_status decode_args(int B, int H, int Hkv, long long L, int d, int P, ra_dtype dtype, float scale) {
   ra_status st = check_common(B, H, Hkv, L, d, P, dtype, scale);
   if (st != RA_OK) return st;
-  if (H / Hkv > 16) return fail(RA_EINVAL, "H/Hkv must be <= 16 (got %d)", H / Hkv);
   return RA_OK;
 }
 
@@ -1043,9 +1042,13 @@ struct DecodeWs {
   bool overflow;
 };
 
+// Query heads per kv head are processed in sub-groups of 16 (the MFMA
+// columns of the bf16 partial pass); each sub-group reads its kv head's rows.
+int decode_sub_groups(int H, int Hkv) { return (H / Hkv + 15) / 16; }
+
 DecodeWs decode_ws_layout(int B, int H, int Hkv, long long L, int d, int P) {
   DecodeWs w{};
-  decode_split(B, Hkv, L, P, &w.chunk, &w.cpb);
+  decode_split(B, Hkv * decode_sub_groups(H, Hkv), L, P, &w.chunk, &w.cpb);
   const int64_t S = (int64_t)P * w.cpb * kDecodeWaves;
   w.S = S > 0x7fffffffLL ? 0 : (int)S;
   SizeAcc a;
@@ -1063,7 +1066,8 @@ ra_status decode_launch(const void* q, const void* k, const void* v, void* out, 
                         void* stream) {
   ra_status st = check_tensor_align({q, k, v, out}, {lse});
   if (st != RA_OK) return st;
-  if ((int64_t)B * Hkv * P * W.cpb > 0x7fffffffLL) return fail(RA_EINVAL, "problem too large");
+  if ((int64_t)B * Hkv * decode_sub_groups(H, Hkv) * P * W.cpb > 0x7fffffffLL)
+    return fail(RA_EINVAL, "problem too large");
   DeviceCtx* ctx = nullptr;
   if ((st = get_ctx(&ctx)) != RA_OK) return st;
   DecodeArgs a{};
@@ -1074,6 +1078,7 @@ ra_status decode_launch(const void* q, const void* k, const void* v, void* out, 
   a.lse_part = reinterpret_cast<float*>(wsb + W.off_lse);
   a.out = out; a.lse = lse;
   a.B = B; a.H = H; a.Hkv = Hkv; a.group = H / Hkv;
+  a.sub_groups = decode_sub_groups(H, Hkv);
   a.L = L;
   a.chunk = W.chunk;
   a.block = L / P;

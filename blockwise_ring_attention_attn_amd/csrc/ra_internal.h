@@ -105,6 +105,7 @@ struct DecodeArgs {
   int64_t block;          // keys per ring block (L / P)
   int chunks_per_block, P, S;
   float scale_log2;
+  int sub_groups;         // ceil(group / 16): query heads per kv head in sub-groups of 16
 };
 
 // Launchers (return hipError_t of the launch).

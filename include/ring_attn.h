@@ -208,7 +208,10 @@ ra_status lse_merge(float* o_a, float* lse_a, const float* o_b, const float* lse
  * to bf16 as the P V operand, fp32 accumulation.  RA_F32: fp32 throughout (a
  * plain, untuned partial pass).  The partials are fp32 for both, so the
  * workspace does not depend on dtype.  The query sees every cached key (no
- * mask).  Requires L % P == 0 and H / Hkv <= 16.  ws: at least
+ * mask).  Requires L % P == 0.  The query heads of a kv head are handled in
+ * sub-groups of 16, each reading the kv head's rows (so K and V are read
+ * once for H / Hkv <= 16, and once per 16 query heads beyond that, e.g.
+ * twice for multi-query attention with 32 heads).  ws: at least
  * ring_attn_decode_ws_bytes(...) bytes.
  * ---------------------------------------------------------------------- */
 size_t ring_attn_decode_ws_bytes(int B, int H, int Hkv, long long L, int d, int P);

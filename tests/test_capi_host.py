@@ -76,7 +76,7 @@ def test_other_ws_queries_flag_invalid_arguments(lib):
     assert lib.ring_attn_bwd_ws_bytes(1, 2, 1, 65, 64, 4, ra.RA_BF16) == SIZE_MAX
     assert lib.ring_attn_bwd_ws_bytes(1, 1, 1, 1 << 24, 128, 8, ra.RA_BF16) == SIZE_MAX  # 4 GiB plane
     assert b"below 2 GiB" in lib.ra_last_error()
-    assert lib.ring_attn_decode_ws_bytes(1, 32, 1, 64, 64, 4) == SIZE_MAX  # group of 32 > 16
+    assert lib.ring_attn_decode_ws_bytes(1, 32, 1, 64, 96, 4) == SIZE_MAX  # d = 96
     assert lib.ring_attn_decode_ws_bytes(1, 4, 1, 66, 64, 4) == SIZE_MAX
     with pytest.raises(ra.RingAttnError):
         ra.ring_attn_decode_ws_bytes(1, 4, 1, 66, 64, 4)
@@ -164,11 +164,12 @@ def test_merge_decode_reject_invalid(lib):
     assert lib.lse_merge(None, 1, 1, 1, 4, 8, None) == ra.RA_EINVAL
     assert lib.lse_merge(1, 1, 1, 1, 4, 0, None) == ra.RA_EINVAL
     assert lib.ring_attn_finalize(1, 1, 1, 1, 1, 4, 2000, 1, None) == ra.RA_EINVAL
-    # decode: unknown dtype, group > 16 (bf16 and fp32), L % P
+    # decode: unknown dtype, H % Hkv, d (bf16 and fp32), L % P
     assert lib.ring_attn_decode(1, 1, 1, 1, 1, 1, 4, 1, 64, 64, 4, 0.1, 7, None, 256, 1 << 30) == ra.RA_EINVAL
     assert b"unknown dtype" in lib.ra_last_error()
-    assert lib.ring_attn_decode(1, 1, 1, 1, 1, 1, 32, 1, 64, 64, 4, 0.1, 0, None, 256, 1 << 30) == ra.RA_EINVAL
-    assert lib.ring_attn_decode(1, 1, 1, 1, 1, 1, 32, 1, 64, 64, 4, 0.1, 1, None, 256, 1 << 30) == ra.RA_EINVAL
+    assert lib.ring_attn_decode(1, 1, 1, 1, 1, 1, 32, 3, 64, 64, 4, 0.1, 1, None, 256, 1 << 30) == ra.RA_EINVAL
+    assert lib.ring_attn_decode(1, 1, 1, 1, 1, 1, 32, 1, 64, 96, 4, 0.1, 0, None, 256, 1 << 30) == ra.RA_EINVAL
+    assert lib.ring_attn_decode(1, 1, 1, 1, 1, 1, 32, 1, 64, 96, 4, 0.1, 1, None, 256, 1 << 30) == ra.RA_EINVAL
     assert lib.ring_attn_decode(1, 1, 1, 1, 1, 1, 4, 1, 66, 64, 4, 0.1, 1, None, 256, 1 << 30) == ra.RA_EINVAL
 
 
@@ -236,6 +237,18 @@ def test_bwd_ws_bytes_cover_fp32_gradients():
     assert need + stage <= got <= need + stage + (1 << 16)
     got1 = ra.load().ring_attn_bwd_ws_bytes(B, H, Hkv, N, d, 1, ra.RA_BF16)
     assert need <= got1 <= need + (1 << 16)
+
+
+def test_decode_ws_bytes_count_query_head_sub_groups():
+    """Query heads beyond 16 per kv head are decoded in sub-groups of 16; the
+    partials stay one per (batch, head, split), so the workspace for a
+    multi-query group of 32 equals that of 32 kv heads with one query each
+    at the same number of splits per ring block."""
+    lib = ra.load()
+    nb_mqa = lib.ring_attn_decode_ws_bytes(2, 32, 1, 4096, 128, 4)
+    assert nb_mqa not in (0, SIZE_MAX)
+    nb_mha = lib.ring_attn_decode_ws_bytes(2, 32, 32, 4096, 128, 4)
+    assert nb_mqa <= nb_mha   # fewer workgroup planes -> at least as many splits per block, never more partials
 
 
 def test_bwd_fp32_ws_bytes_and_plane_limit():

@@ -276,8 +276,12 @@ def test_lse_merge_against_oracle():
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("B,H,Hkv,L,d,P", [(2, 8, 2, 8 * 1000, 128, 8), (3, 4, 4, 4 * 77, 64, 4),
-                                           (1, 16, 1, 2 * 4096, 128, 2), (2, 2, 2, 1, 128, 1)])
+                                           (1, 16, 1, 2 * 4096, 128, 2), (2, 2, 2, 1, 128, 1),
+                                           (2, 32, 1, 4 * 512, 128, 4), (1, 40, 2, 8 * 300, 64, 8)])
 def test_decode_against_oracle(B, H, Hkv, L, d, P, dtype):
+    """Decode against the oracle, including multi-query attention (32 query
+    heads on one kv head: two sub-groups of 16) and a group of 20 (a full
+    sub-group and one of 4)."""
     import torch
     q, k, v = _case(12, B, H, Hkv, L, d, dtype, Nq=1)
     out, lse = ra.ring_attn_decode(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), P=P)
