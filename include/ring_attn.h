@@ -52,8 +52,8 @@
  *    one (batch, kv head) plane must stay below 2 GiB (N / P * d * 2 bytes);
  *    whole planes may be larger (a striped ring whose plane is 2 GiB or more
  *    stages its first step's blocks instead of reading them in place).
- *    ring_attn_bwd needs one head plane below 2 GiB; decode has no such
- *    limit (64-bit addressing).
+ *    The bf16 ring_attn_bwd needs one head plane below 2 GiB; the fp32
+ *    backward and decode have no such limit (64-bit addressing).
  */
 #ifndef RING_ATTN_H
 #define RING_ATTN_H
