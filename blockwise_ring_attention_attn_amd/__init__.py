@@ -25,7 +25,7 @@ EXPORTS = (
     "ring_attn_fwd_share_ws_bytes", "ring_attn_fwd_share",
     "ring_attn_step", "ring_attn_finalize", "lse_merge",
     "ring_attn_decode_ws_bytes", "ring_attn_decode", "ring_attn_decode_noalloc",
-    "ring_attn_bwd_ws_bytes", "ring_attn_bwd",
+    "ring_attn_bwd_ws_bytes", "ring_attn_bwd", "ring_attn_bwd_share_ws_bytes", "ring_attn_bwd_share",
     "ra_last_error", "ra_version", "ra_debug_set_delays", "ra_prof_enable", "ra_prof_reset", "ra_prof_read",
     "ra_diag_mfma_loop", "ra_debug_set_staging",
 )
@@ -86,6 +86,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.ring_attn_bwd_ws_bytes.restype = st
     lib.ring_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, ll, i, i, i, i, f, i, vp, vp, st]
     lib.ring_attn_bwd.restype = i
+    lib.ring_attn_bwd_share_ws_bytes.argtypes = [i, i, i, ll, i, i, i]
+    lib.ring_attn_bwd_share_ws_bytes.restype = st
+    lib.ring_attn_bwd_share.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, ll, i, i, i, i, i, f, i, vp,
+                                        vp, st]
+    lib.ring_attn_bwd_share.restype = i
     lib.ra_last_error.argtypes = []
     lib.ra_last_error.restype = ctypes.c_char_p
     lib.ra_version.argtypes = []
@@ -297,6 +302,40 @@ def ring_attn_bwd(q, k, v, out, dout, lse, *, P: int, causal: bool, layout: str 
     _check(lib.ring_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
                              _ptr(dv), B, H, Hkv, N, d, P, int(bool(causal)), LAYOUTS[layout], scale, code,
                              _stream(stream), _ptr(wst) if wst is not None else None, nb))
+    return dq, dk, dv
+
+
+def ring_attn_bwd_share(q, k, v, out, dout, lse, *, P: int, rank: int, causal: bool, layout: str = "contiguous",
+                        scale: float | None = None, dq=None, dk=None, dv=None, ws=None, stream=None):
+    """One device's share of the backward (see ring_attn.h).
+
+    q, out, dout [B, H, N/P, d] and lse [B, H, N/P] of host `rank` (as
+    ring_attn_fwd_share takes and returns them); k, v [B, Hkv, N, d].
+    Returns (dq [B, H, N/P, d], dk, dv [B, Hkv, N, d]): the rank's query
+    gradient and its contribution to every key's gradient.
+    """
+    torch = _torch()
+    lib = load()
+    B, H, Hkv, Nq, N, d, code = _qkv(q, k, v)
+    if Nq * P != N:
+        raise ValueError("q must hold N / P rows")
+    _tensor(out, "out", (B, H, Nq, d), q.dtype)
+    _tensor(dout, "dout", (B, H, Nq, d), q.dtype)
+    _tensor(lse, "lse", (B, H, Nq), torch.float32)
+    for g, like, nm in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        if g is not None:
+            _tensor(g, nm, tuple(like.shape), like.dtype)
+    _devices(q=q, k=k, v=v, out=out, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    nb = _ws_size(lib.ring_attn_bwd_share_ws_bytes(B, H, Hkv, N, d, P, code))
+    wst = _workspace(nb, q, ws)
+    _check(lib.ring_attn_bwd_share(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq),
+                                   _ptr(dk), _ptr(dv), B, H, Hkv, N, d, P, rank, int(bool(causal)),
+                                   LAYOUTS[layout], scale, code, _stream(stream),
+                                   _ptr(wst) if wst is not None else None, nb))
     return dq, dk, dv
 
 

@@ -324,11 +324,13 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   // range (they read zeros); a tile index past the last one loads zeros.
   // Consumer 0 also loads the tile's row statistics (lse2, delta): 256 bytes,
   // lane l: row l / 2, statistic l % 2.
-  const int64_t plane_elems = G.n_tok * D;
-  const unsigned rec_rows = (unsigned)(G.n_tok * T::RB);
-  const unsigned rec_rs = (unsigned)(G.n_tok * 8);
+  const bool qc = G.q_compact != 0;
+  const int64_t q_plane_rows = qc ? (int64_t)A.Lq : G.n_tok;   // rows per (b, h) plane of q, dout, row statistics
+  const int64_t plane_elems = q_plane_rows * D;
+  const unsigned rec_rows = (unsigned)(q_plane_rows * T::RB);
+  const unsigned rec_rs = (unsigned)(q_plane_rows * 8);
   constexpr bool kAffine = LAYOUT != 2;
-  const int row_stride = LAYOUT == 1 ? A.P : 1;
+  const int row_stride = (LAYOUT == 1 && !qc) ? A.P : 1;
   int voff_row[PER_WAVE], rr_row[PER_WAVE], qchunk[PER_WAVE];
 #pragma unroll
   for (int u = 0; u < PER_WAVE; ++u) {
@@ -343,7 +345,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   unsigned short* qbase = const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(A.q)) + qplane0 * plane_elems;
   unsigned short* obase =
       const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(G.dout)) + qplane0 * plane_elems;
-  float* rbase = const_cast<float*>(G.rowstat) + qplane0 * G.n_tok * 2;
+  float* rbase = const_cast<float*>(G.rowstat) + qplane0 * q_plane_rows * 2;
   auto issue = [&](int it, auto slot) __attribute__((always_inline)) {
     const bool valid = it < total;
     const int row0 = (qt0 + is_qt) * kRows;
@@ -351,7 +353,8 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(obase, 0, rec_rows, 0x00020000);
     const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(rbase, 0, rec_rs, 0x00020000);
     if (kAffine && valid && row0 + kRows <= A.Lq) {
-      const unsigned nat0 = LAYOUT == 0 ? (unsigned)(w.q_rank * A.Lq + row0) : (unsigned)(row0 * A.P + w.q_rank);
+      const unsigned nat0 = qc ? (unsigned)row0
+                               : LAYOUT == 0 ? (unsigned)(w.q_rank * A.Lq + row0) : (unsigned)(row0 * A.P + w.q_rank);
 #pragma unroll
       for (int u = 0; u < PER_WAVE; ++u) {
         const int ins = cw * PER_WAVE + u;
@@ -364,13 +367,15 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
       for (int u = 0; u < PER_WAVE; ++u) {
         const int ins = cw * PER_WAVE + u;
         const int i = row0 + rr_row[u];
-        const int voff = (valid && i < A.Lq) ? lrow<LAYOUT>(w.q_rank, i, A.Lq, A.P) * T::RB + qchunk[u] : (int)rec_rows;
+        const int src = qc ? i : lrow<LAYOUT>(w.q_rank, i, A.Lq, A.P);
+        const int voff = (valid && i < A.Lq) ? src * T::RB + qchunk[u] : (int)rec_rows;
         lds_load16(rq, qbuf(slot) + ins * 1024, voff, 0u);
         lds_load16(ro, obuf(slot) + ins * 1024, voff, 0u);
       }
       if (cw == 0) {
         const int i = row0 + (lane >> 1);
-        const int voff = (valid && i < A.Lq) ? lrow<LAYOUT>(w.q_rank, i, A.Lq, A.P) * 8 + 4 * (lane & 1) : (int)rec_rs;
+        const int src = qc ? i : lrow<LAYOUT>(w.q_rank, i, A.Lq, A.P);
+        const int voff = (valid && i < A.Lq) ? src * 8 + 4 * (lane & 1) : (int)rec_rs;
         lds_load4(rr, &rsb(slot)[0][0], voff, 0u);
       }
     }
@@ -378,7 +383,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
       is_qt = 0;
       qbase += plane_elems;
       obase += plane_elems;
-      rbase += G.n_tok * 2;
+      rbase += q_plane_rows * 2;
     }
   };
   // Loads a consumer may leave in flight at the end of a phase: those of the
@@ -411,7 +416,8 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
     bf16x8 kf[KS], vf[KS];
     {
       const int64_t src_row =
-          G.kv_staged ? ((int64_t)w.q_rank * A.B * A.Hkv + kv_plane) * A.Lkv + (key_ok ? my_key : 0) : key_row;
+          G.kv_staged ? ((int64_t)(w.q_rank - G.stage_host0) * A.B * A.Hkv + kv_plane) * A.Lkv + (key_ok ? my_key : 0)
+                      : key_row;
       load_row_frags<D>(kf, reinterpret_cast<const unsigned short*>(A.k), src_row, key_ok, half);
       load_row_frags<D>(vf, reinterpret_cast<const unsigned short*>(A.v), src_row, key_ok, half);
     }
@@ -533,7 +539,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
 
   // (A key tile no query sees still writes its zeros on the first launch
   // and its final values on the last.)
-  const bool first = G.first != 0;
+  const bool first = G.kv_first != 0;
   const bool fin = ((G.kv_fin >> w.kv_rank) & 1ull) != 0;
   if (!key_ok || (total == 0 && !first && !fin)) return;
   float* dk_row = G.dk_acc + key_row * D;
@@ -571,7 +577,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
   const int ntiles = (int)((kv_end + kRows - 1) / kRows);
 
   const int64_t qplane = (int64_t)w.b * A.H + w.h;
-  const int64_t qrow = row_ok ? nat_row<LAYOUT>(A, qplane, G.n_tok, w.q_rank, my_row, A.Lq) : 0;
+  const int64_t qrow = !row_ok ? 0
+                       : G.q_compact ? qplane * A.Lq + my_row
+                                     : nat_row<LAYOUT>(A, qplane, G.n_tok, w.q_rank, my_row, A.Lq);
   bf16x8 qf[KS], of[KS];
   load_row_frags<D>(qf, reinterpret_cast<const unsigned short*>(A.q), qrow, row_ok, half);
   load_row_frags<D>(of, reinterpret_cast<const unsigned short*>(G.dout), qrow, row_ok, half);
@@ -597,7 +605,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs G) {
   // K / V rows: in place, the plane of the natural-order arrays (block row j
   // at its token's row); staged, the host's compact block (row j at j)
   const bool staged = G.kv_staged != 0;
-  const int64_t kv_base = staged ? ((int64_t)w.q_rank * A.B * A.Hkv + kv_plane) * A.Lkv : kv_plane * G.n_tok;
+  const int64_t kv_base =
+      staged ? ((int64_t)(w.q_rank - G.stage_host0) * A.B * A.Hkv + kv_plane) * A.Lkv : kv_plane * G.n_tok;
   const unsigned rec_rows = (unsigned)((staged ? (int64_t)A.Lkv : G.n_tok) * T::RB);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<unsigned short*>(reinterpret_cast<const unsigned short*>(A.k)) + kv_base * D, 0, rec_rows,

@@ -82,8 +82,17 @@ __device__ __forceinline__ Work pair_work(const StepArgs& A, int64_t rest, int h
 __device__ __forceinline__ int64_t kv_read_row(const BwdArgs& G, const Work& w, int64_t j) {
   const StepArgs& A = G.s;
   const int64_t plane = (int64_t)w.b * A.Hkv + w.hkv;
-  if (G.kv_staged) return ((int64_t)w.q_rank * A.B * A.Hkv + plane) * A.Lkv + j;
+  if (G.kv_staged) return ((int64_t)(w.q_rank - G.stage_host0) * A.B * A.Hkv + plane) * A.Lkv + j;
   return plane * G.n_tok + host_row(A.layout, w.kv_rank, j, A.Lkv, A.P);
+}
+
+// Row of query i (head h) of the pair's query host in q, dout, dq and the
+// row statistics: the natural-order arrays, or the host's compact block.
+__device__ __forceinline__ int64_t q_read_row(const BwdArgs& G, const Work& w, int h, int64_t i) {
+  const StepArgs& A = G.s;
+  const int64_t plane = (int64_t)w.b * A.H + h;
+  if (G.q_compact) return plane * A.Lq + i;
+  return plane * G.n_tok + host_row(A.layout, w.q_rank, i, A.Lq, A.P);
 }
 
 // Add `v` (this launch's contribution to one element) into its fp32
@@ -107,7 +116,7 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dq_f32_kernel(BwdArgs G, int6
   const int64_t i = gw % A.Lq;
   const Work w = pair_work(A, gw / A.Lq, A.H);
   const int64_t lim = key_limit(A, w, i);
-  const int64_t qrow = ((int64_t)w.b * A.H + w.h) * G.n_tok + host_row(A.layout, w.q_rank, i, A.Lq, A.P);
+  const int64_t qrow = q_read_row(G, w, w.h, i);
   const float* q = static_cast<const float*>(A.q) + qrow * D;
   const float* go = static_cast<const float*>(G.dout) + qrow * D;
   const float* kb = static_cast<const float*>(A.k);
@@ -179,9 +188,8 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dkdv_f32_kernel(BwdArgs G, in
   const float c = A.scale_log2;
   for (int g = 0; g < group; ++g) {
     const int h = w.hkv * group + g;
-    const int64_t qplane = ((int64_t)w.b * A.H + h) * G.n_tok;
     for (int64_t i = i0; i < A.Lq; ++i) {
-      const int64_t qrow = qplane + host_row(A.layout, w.q_rank, i, A.Lq, A.P);
+      const int64_t qrow = q_read_row(G, w, h, i);
       const float* q = static_cast<const float*>(A.q) + qrow * D;
       const float* go = static_cast<const float*>(G.dout) + qrow * D;
       float qv[NC], ov[NC], s = 0.f, dp = 0.f;
@@ -203,7 +211,7 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dkdv_f32_kernel(BwdArgs G, in
       }
     }
   }
-  const bool first = G.first != 0, fin = ((G.kv_fin >> w.kv_rank) & 1ull) != 0;
+  const bool first = G.kv_first != 0, fin = ((G.kv_fin >> w.kv_rank) & 1ull) != 0;
 #pragma unroll
   for (int e = 0; e < NC; ++e) {
     const int64_t idx = acc_row * D + lane + 64 * e;

@@ -907,7 +907,7 @@ ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void*
     a.s.host_lo = lo_s[s];
     a.s.n_hosts = hi_s[s] - lo_s[s] + 1;
     a.s.kv_shift = -s;
-    a.first = s == 0;
+    a.first = a.kv_first = s == 0;
     a.q_fin = a.kv_fin = 0;
     for (int r = 0; r < P; ++r) {
       if (last_q[r] == s) a.q_fin |= 1ull << r;
@@ -921,6 +921,166 @@ ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void*
     RA_HIP(f32 ? launch_bwd_dkdv_f32(a, d, cs) : launch_bwd_dkdv(a, d, cs), "dK/dV kernel launch");
     RA_HIP(f32 ? launch_bwd_dq_f32(a, d, cs) : launch_bwd_dq(a, d, cs), "dQ kernel launch");
     if (staged && i + 2 < n) RA_HIP(hipEventRecord(ctx->done[i & 1], cs), "hipEventRecord");
+  }
+  return RA_OK;
+}
+
+// One device's share of the backward: host `rank` keeps its query block
+// (q, out, dout, lse, dq: compact [B, H, Bl, ...]) and meets kv block
+// (rank + s) mod P at step s; dk, dv [B, Hkv, N, d] receive this host's
+// contribution to every key (the sum over the P shares is the full dK, dV;
+// a block the host never sees gets zeros).  Each step writes a different
+// kv block, so the dK / dV kernels write their results directly; dQ is
+// accumulated in fp32 over the host's active steps.  Blocks after the
+// host's own are staged into one of two slot buffers on the copy stream
+// while the previous step computes, as in the forward share.
+struct BwdShareWs {
+  size_t off_stage[2], kv_bytes;
+  size_t off_rowstat, off_dq, total;
+  bool overflow;
+};
+
+static BwdShareWs bwd_share_ws_layout(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype) {
+  BwdShareWs w{};
+  SizeAcc a;
+  const uint64_t Bl = (uint64_t)(N / P);
+  if (P > 1) {
+    const uint64_t es = esize(dtype);
+    w.off_stage[0] = a.add({(uint64_t)B, (uint64_t)Hkv, Bl, (uint64_t)d, es});
+    w.kv_bytes = a.add({(uint64_t)B, (uint64_t)Hkv, Bl, (uint64_t)d, es}) - w.off_stage[0];
+    w.off_stage[1] = a.add({2, w.kv_bytes});
+  }
+  w.off_rowstat = a.add({(uint64_t)B, (uint64_t)H, Bl, 8});
+  w.off_dq = a.add({(uint64_t)B, (uint64_t)H, Bl, (uint64_t)d, 4});
+  w.total = (size_t)a.total;
+  w.overflow = a.bad;
+  return w;
+}
+
+size_t ring_attn_bwd_share_ws_bytes(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype) {
+  g_err.clear();
+  if (bwd_args(B, H, Hkv, N, d, P, dtype, 1.f) != RA_OK) return SIZE_MAX;
+  const BwdShareWs W = bwd_share_ws_layout(B, H, Hkv, N, d, P, dtype);
+  if (W.overflow) {
+    fail(RA_ENOMEM, "workspace size exceeds the 48-bit device address space");
+    return SIZE_MAX;
+  }
+  return W.total;
+}
+
+ra_status ring_attn_bwd_share(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, long long N,
+                              int d, int P, int rank, int causal, ra_layout layout, float scale, ra_dtype dtype,
+                              void* stream, void* ws, size_t ws_bytes) {
+  g_err.clear();
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv) return fail(RA_EINVAL, "null tensor pointer");
+  ra_status st = bwd_args(B, H, Hkv, N, d, P, dtype, scale);
+  if (st != RA_OK) return st;
+  if ((st = check_layout(layout, N, P)) != RA_OK) return st;
+  if (rank < 0 || rank >= P) return fail(RA_EINVAL, "rank %d out of [0, %d)", rank, P);
+  const BwdShareWs W = bwd_share_ws_layout(B, H, Hkv, N, d, P, dtype);
+  if ((st = check_ws(W.overflow, W.total, ws, ws_bytes)) != RA_OK) return st;
+  if ((st = check_tensor_align({q, k, v, out, dout, dq, dk, dv}, {lse})) != RA_OK) return st;
+  const bool f32 = dtype == RA_F32;
+  const int64_t Bl = N / P;
+  const int64_t nqt = (Bl + bwd_dq_rows() - 1) / bwd_dq_rows();
+  const int64_t nkt = (Bl + bwd_dkdv_rows() - 1) / bwd_dkdv_rows();
+  if ((int64_t)B * H * nqt > 0x7fffffffLL || (int64_t)B * Hkv * nkt > 0x7fffffffLL ||
+      (f32 && (int64_t)B * H * Bl / 4 >= 0x7fffffffLL))
+    return fail(RA_EINVAL, "problem too large for one launch");
+  const int lay = effective_layout(layout, P);
+  hipStream_t cs = static_cast<hipStream_t>(stream);
+  char* wsb = static_cast<char*>(ws);
+
+  BwdArgs a{};
+  a.s.q = q;
+  a.s.q_plane_rows = Bl;
+  a.s.kv_plane_rows = N;
+  a.s.B = B; a.s.H = H; a.s.Hkv = Hkv;
+  a.s.Lq = (int)Bl; a.s.Lkv = (int)Bl;
+  a.s.P = P;
+  a.s.layout = lay;
+  a.s.q_mode = ROWS_COMPACT;
+  a.s.kv_mode = ROWS_HOST_KV;
+  a.s.causal = causal ? 1 : 0;
+  a.s.n_qtiles = (int)nqt;
+  a.s.scale_log2 = scale * 1.4426950408889634f;
+  a.s.host_lo = rank;
+  a.s.n_hosts = 1;
+  a.dout = dout;
+  a.rowstat = reinterpret_cast<float*>(wsb + W.off_rowstat);
+  a.dq_acc = reinterpret_cast<float*>(wsb + W.off_dq);
+  a.n_tok = N;
+  a.scale = scale;
+  a.n_kvtiles = (int)nkt;
+  a.q_compact = 1;
+  a.kv_first = 1;
+  a.stage_host0 = rank;
+  if (f32) {
+    a.dq_out_f32 = static_cast<float*>(dq);
+    a.dk_out_f32 = static_cast<float*>(dk);
+    a.dv_out_f32 = static_cast<float*>(dv);
+  } else {
+    a.dq_out = static_cast<__bf16*>(dq);
+    a.dk_out = static_cast<__bf16*>(dk);
+    a.dv_out = static_cast<__bf16*>(dv);
+  }
+
+  // Every step launches the dK / dV kernel (a block the host does not see
+  // gets its zeros from it); the dQ kernel runs on the active steps only.
+  std::vector<int> active;
+  for (int s = 0; s < P; ++s)
+    if (pair_active(lay, a.s.causal, P, rank, (rank + s) % P, Bl, Bl)) active.push_back(s);
+  if (active.empty() || active[0] != 0) return fail(RA_EUNSUPPORTED, "internal: host %d has no diagonal work", rank);
+  const int n = (int)active.size();
+  const bool staged = g_staging && n > 1;
+  DeviceCtx* ctx = nullptr;
+  if (staged && (st = get_ctx(&ctx)) != RA_OK) return st;
+  std::unique_lock<std::mutex> enq;
+  if (staged) enq = std::unique_lock<std::mutex>(ctx->enqueue);
+  const size_t row_bytes = (size_t)d * esize(dtype);
+  const int64_t planes = (int64_t)B * Hkv;
+  if (f32)
+    RA_HIP(launch_bwd_prep_f32(static_cast<const float*>(out), static_cast<const float*>(dout), lse,
+                               const_cast<float*>(a.rowstat), (int64_t)B * H * Bl, d, cs),
+           "prep launch");
+  else
+    RA_HIP(launch_bwd_prep(out, dout, lse, const_cast<float*>(a.rowstat), (int64_t)B * H * Bl, d, cs),
+           "prep launch");
+  if (staged) {
+    RA_HIP(hipEventRecord(ctx->fork, cs), "hipEventRecord");
+    RA_HIP(hipStreamWaitEvent(ctx->copy, ctx->fork, 0), "hipStreamWaitEvent");
+  }
+  int i = 0;  // index of the next active step
+  for (int s = 0; s < P; ++s) {
+    const int blk = (rank + s) % P;
+    const bool on = i < n && active[i] == s;
+    if (on && staged && i + 1 < n) {
+      // copy stream: the block of the next active step into slot (i + 1) & 1
+      const int blk1 = (rank + active[i + 1]) % P;
+      if (i >= 1) RA_HIP(hipStreamWaitEvent(ctx->copy, ctx->done[(i - 1) & 1], 0), "hipStreamWaitEvent");
+      RA_HIP(launch_spin(g_delay_copy_us, ctx->copy), "delay");
+      char* kd = wsb + W.off_stage[(i + 1) & 1];
+      RA_HIP(gather_block(kd, k, lay, planes, N, Bl, P, blk1, row_bytes, ctx->copy), "staging copy");
+      RA_HIP(gather_block(kd + W.kv_bytes, v, lay, planes, N, Bl, P, blk1, row_bytes, ctx->copy), "staging copy");
+      RA_HIP(hipEventRecord(ctx->copied[(i + 1) & 1], ctx->copy), "hipEventRecord");
+    }
+    if (on && staged && i >= 1) RA_HIP(hipStreamWaitEvent(cs, ctx->copied[i & 1], 0), "hipStreamWaitEvent");
+    const bool use_stage = on && staged && i >= 1;
+    a.kv_staged = use_stage ? 1 : 0;
+    a.s.k = use_stage ? static_cast<const void*>(wsb + W.off_stage[i & 1]) : k;
+    a.s.v = use_stage ? static_cast<const void*>(wsb + W.off_stage[i & 1] + W.kv_bytes) : v;
+    a.s.kv_shift = -s;
+    a.first = i == 0;
+    a.q_fin = (on && i == n - 1) ? 1ull << rank : 0;
+    a.kv_fin = 1ull << blk;
+    RA_HIP(launch_spin(on && staged ? g_delay_compute_us : 0, cs), "delay");
+    RA_HIP(f32 ? launch_bwd_dkdv_f32(a, d, cs) : launch_bwd_dkdv(a, d, cs), "dK/dV kernel launch");
+    if (on) {
+      RA_HIP(f32 ? launch_bwd_dq_f32(a, d, cs) : launch_bwd_dq(a, d, cs), "dQ kernel launch");
+      if (staged && i + 2 < n) RA_HIP(hipEventRecord(ctx->done[i & 1], cs), "hipEventRecord");
+      ++i;
+    }
   }
   return RA_OK;
 }

@@ -80,6 +80,14 @@ struct BwdArgs {
   float* dq_out_f32;
   float* dk_out_f32;
   float* dv_out_f32;
+  // One device's share (ring_attn_bwd_share): q, dout, dq and the row
+  // statistics hold only the query host's rows, compact (plane stride Lq
+  // rows, row i of the block at i) when q_compact != 0; the kv side writes
+  // instead of adding when kv_first != 0 (the full backward sets it equal to
+  // `first`); a staging buffer's first slot belongs to host stage_host0.
+  int q_compact;
+  int kv_first;
+  int stage_host0;
 };
 
 struct MergeArgs {

@@ -266,6 +266,34 @@ ra_status ring_attn_bwd(const void* q, const void* k, const void* v, const void*
                         size_t ws_bytes);
 
 /* ------------------------------------------------------------------------
+ * ring_attn_bwd_share -- one device's share of the ring backward
+ * ([TKG] §7 with the ring of [TKG] §2): host `rank` keeps its queries, its
+ * forward output and row statistics, and meets kv block (rank + s) mod P at
+ * step s = 0..P-1, each later block staged on a second stream while the
+ * previous step computes.  The gradient formulas are those of
+ * ring_attn_bwd, restricted to the host's queries.
+ *
+ * q, out, dout, dq [B, H, N/P, d] and lse [B, H, N/P] hold the rank's
+ * query tokens in the order the layout gives them (as for
+ * ring_attn_fwd_share, whose out and lse they are); k, v [B, Hkv, N, d]
+ * hold the whole sequence in natural order.  dq is the rank's query
+ * gradient.  dk, dv [B, Hkv, N, d] (natural order) receive this rank's
+ * contribution to every key's gradient: zeros for keys the rank's queries
+ * never see; the sum over rank = 0..P-1 of the shares' dk (dv) is
+ * ring_attn_bwd's dk (dv) up to rounding.  In a real ring those partial
+ * sums travel with their kv block; here each lands at its block's rows.
+ * dtype, causal, layout, scale, P and the bf16 head-plane limit: as for
+ * ring_attn_bwd.  dq, dk, dv are overwritten.  ws: at least
+ * ring_attn_bwd_share_ws_bytes(...) bytes (two staging slots of one block,
+ * the fp32 dq accumulator and the row statistics of the rank's rows).
+ * ---------------------------------------------------------------------- */
+size_t ring_attn_bwd_share_ws_bytes(int B, int H, int Hkv, long long N, int d, int P, ra_dtype dtype);
+ra_status ring_attn_bwd_share(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, long long N,
+                              int d, int P, int rank, int causal, ra_layout layout, float scale, ra_dtype dtype,
+                              void* stream, void* ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------
  * Diagnostics.
  * ra_last_error: message of the last failed call on this thread ("" if none).
  * ra_version: library version string.

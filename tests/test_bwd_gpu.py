@@ -141,3 +141,99 @@ def test_bwd_fp32_causal_gqa_layouts(layout):
 
 def test_bwd_fp32_batched_ragged():
     _check(48, 2, 2, 1, 3 * 101, 64, 3, True, "striped", "f32")
+
+
+# ---------------------------------------------------------------------------
+# One device's share of the backward: host `rank`'s query rows against the
+# whole sequence; the oracle is the plain backward of those rows (their
+# global positions) against every key, whose dk, dv are exactly that rank's
+# contribution.
+# ---------------------------------------------------------------------------
+def _share_inputs(seed, B, H, Hkv, N, d, P, rank, layout, dtype):
+    q, k, v, do = _inputs(seed, B, H, Hkv, N, d, dtype)
+    pos = oracle.host_positions(N, P, layout)[rank]
+    qb = np.ascontiguousarray(q[:, :, pos])
+    dob = np.ascontiguousarray(do[:, :, pos])
+    return qb, k, v, dob, pos
+
+
+def _run_share(qb, k, v, dob, P, rank, causal, layout, dtype):
+    import torch
+    qd, kd, vd, dod = (to_dev(x, dtype) for x in (qb, k, v, dob))
+    out, lse = ra.ring_attn_fwd_share(qd, kd, vd, P=P, rank=rank, causal=causal, layout=layout)
+    dq, dk, dv = ra.ring_attn_bwd_share(qd, kd, vd, out, dod, lse, P=P, rank=rank, causal=causal, layout=layout)
+    torch.cuda.synchronize()
+    return from_dev(dq), from_dev(dk), from_dev(dv)
+
+
+def _check_share(seed, B, H, Hkv, N, d, P, rank, causal, layout, dtype="bf16"):
+    print(f"  share rank={rank} P={P} causal={causal} {layout}", flush=True)
+    qb, k, v, dob, pos = _share_inputs(seed, B, H, Hkv, N, d, P, rank, layout, dtype)
+    dq, dk, dv = _run_share(qb, k, v, dob, P, rank, causal, layout, dtype)
+    qh, kh, vh, doh = (host_vals(x, dtype) for x in (qb, k, v, dob))
+    scale = 1.0 / math.sqrt(d)
+    dq_r, dk_r, dv_r, parts = oracle.attention_bwd(qh, kh, vh, doh, scale=scale, causal=causal, q_pos=pos,
+                                                   parts=True)
+    bq, bk, bv = _bounds(qh, kh, vh, doh, parts, B, H, Hkv, scale, dq_r, dk_r, dv_r, EPS[dtype])
+    what = f"bwd_share B={B} H={H}/{Hkv} N={N} d={d} P={P} rank={rank} causal={causal} {layout} {dtype}"
+    for name, got, ref, bnd in (("dq", dq, dq_r, bq), ("dk", dk, dk_r, bk), ("dv", dv, dv_r, bv)):
+        assert np.all(np.isfinite(got)), f"{what}: non-finite {name}"
+        err = np.abs(got - ref)
+        ratio = float((err / (2 * bnd + 1e-6)).max())
+        print(f"  {name}: max|err|={err.max():.3e} worst err/bound={ratio:.3f}")
+        assert ratio <= 1.0, f"{what}: {name} exceeds its bound (err/bound {ratio:.3f})"
+    if causal:
+        # keys after the rank's last query get exactly zero
+        late = np.arange(N) > pos.max()
+        assert not dk[:, :, late].any() and not dv[:, :, late].any()
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("layout,rank", [("contiguous", 0), ("contiguous", 7), ("contiguous", 3),
+                                         ("striped", 5), ("zigzag", 2)])
+def test_bwd_share_causal_gqa(layout, rank):
+    """GQA 2:1, d = 128, P = 8, blocks of 130 rows (ragged against every
+    tile).  Contiguous rank 0 sees only its own block (the other seven
+    blocks get zeros); rank 7 sees all eight."""
+    _check_share(51, 1, 4, 2, 16 * 65, 128, 8, rank, True, layout)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_share_noncausal(d):
+    _check_share(52, 2, 2, 1, 4 * 100, d, 4, 1, False, "contiguous")
+
+
+def test_bwd_share_ragged_small():
+    _check_share(53, 1, 2, 1, 3 * 7, 64, 3, 2, True, "striped")
+
+
+@pytest.mark.parametrize("layout,rank", [("contiguous", 6), ("zigzag", 1)])
+def test_bwd_share_fp32(layout, rank):
+    _check_share(54, 1, 4, 2, 8 * 34, 64, 8, rank, True, layout, "f32")
+
+
+def test_bwd_shares_sum_to_the_full_backward():
+    """Summed over the P ranks, the shares' dk and dv are the full
+    backward's (within the bf16 rounding of the summands), and each rank's
+    dq is the full dq at that rank's rows."""
+    import torch
+    B, H, Hkv, N, d, P, layout = 1, 4, 2, 8 * 128, 128, 8, "striped"
+    q, k, v, do = _inputs(55, B, H, Hkv, N, d, "bf16")
+    qd, kd, vd, dod = (to_dev(x, "bf16") for x in (q, k, v, do))
+    out, lse = ra.ring_attn_fwd(qd, kd, vd, P=P, causal=True, layout=layout)
+    dq_f, dk_f, dv_f = (from_dev(t) for t in ra.ring_attn_bwd(qd, kd, vd, out, dod, lse, P=P, causal=True,
+                                                                layout=layout))
+    dk_sum = np.zeros_like(dk_f)
+    dv_sum = np.zeros_like(dv_f)
+    for rank, pos in enumerate(oracle.host_positions(N, P, layout)):
+        idx = torch.from_numpy(pos).to(qd.device)
+        sl = [t.index_select(2, idx).contiguous() for t in (qd, out, dod)]
+        dq, dk, dv = ra.ring_attn_bwd_share(sl[0], kd, vd, sl[1], sl[2], lse.index_select(2, idx).contiguous(),
+                                            P=P, rank=rank, causal=True, layout=layout)
+        torch.cuda.synchronize()
+        dq = from_dev(dq)
+        assert np.abs(dq - dq_f[:, :, pos]).max() <= 2e-2 * np.abs(dq_f).max()
+        dk_sum += from_dev(dk)
+        dv_sum += from_dev(dv)
+    for got, ref in ((dk_sum, dk_f), (dv_sum, dv_f)):
+        assert np.abs(got - ref).max() <= 3e-2 * np.abs(ref).max()

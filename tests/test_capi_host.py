@@ -239,6 +239,51 @@ def test_bwd_ws_bytes_cover_fp32_gradients():
     assert need <= got1 <= need + (1 << 16)
 
 
+def _bwd_share(lib, **kw):
+    a = dict(q=1, k=1, v=1, out=1, dout=1, lse=1, dq=1, dk=1, dv=1, B=1, H=2, Hkv=1, N=64, d=64, P=4, rank=1,
+             causal=1, layout=0, scale=0.125, dtype=1, stream=None, ws=256, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.ring_attn_bwd_share(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["dq"], a["dk"],
+                                   a["dv"], a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["P"], a["rank"],
+                                   a["causal"], a["layout"], a["scale"], a["dtype"], a["stream"], a["ws"],
+                                   a["ws_bytes"])
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(lse=None), "null"),
+    (dict(dk=None), "null"),
+    (dict(rank=4), "rank 4 out of"),
+    (dict(rank=-1), "rank -1 out of"),
+    (dict(N=66), "multiple of P"),
+    (dict(d=96), "64 or 128"),
+    (dict(layout=2, N=68), "multiple of 2P"),
+    (dict(ws_bytes=16), "workspace too small"),
+    (dict(ws=None), "null workspace"),
+    (dict(ws=100), "aligned"),
+    (dict(q=256, k=512, v=776, out=1024, dout=1280, dq=1536, dk=1792, dv=2048, lse=2304), "16-byte"),
+])
+def test_bwd_share_rejects_invalid(lib, kw, frag):
+    assert _bwd_share(lib, **kw) == ra.RA_EINVAL
+    assert frag in lib.ra_last_error().decode()
+
+
+def test_bwd_share_ws_bytes():
+    """One device's share of the backward holds two staging slots of one kv
+    block (K and V), the fp32 dq accumulator and the row statistics of the
+    rank's N/P rows; nothing for dk / dv (each step writes its block's
+    gradients directly)."""
+    lib = ra.load()
+    for dtype, es in ((ra.RA_BF16, 2), (ra.RA_F32, 4)):
+        B, H, Hkv, N, d, P = 1, 4, 1, 8 * 131072, 128, 8
+        Bl = N // P
+        need = 4 * (B * H * Bl * d + 2 * B * H * Bl) + 2 * 2 * (B * Hkv * Bl * d * es)
+        got = lib.ring_attn_bwd_share_ws_bytes(B, H, Hkv, N, d, P, dtype)
+        assert need <= got <= need + (1 << 16)
+        got1 = lib.ring_attn_bwd_share_ws_bytes(B, H, Hkv, N // P, d, 1, dtype)
+        assert 4 * (B * H * Bl * d + 2 * B * H * Bl) <= got1 <= 4 * (B * H * Bl * d + 2 * B * H * Bl) + (1 << 16)
+    assert lib.ring_attn_bwd_share_ws_bytes(1, 1, 1, 1 << 24, 128, 8, ra.RA_BF16) == SIZE_MAX   # 4 GiB kv plane
+
+
 def test_decode_ws_bytes_count_query_head_sub_groups():
     """Query heads beyond 16 per kv head are decoded in sub-groups of 16; the
     partials stay one per (batch, head, split), so the workspace for a

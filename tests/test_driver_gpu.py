@@ -202,7 +202,59 @@ def test_bwd_fp32_ignores_stale_workspace():
         assert np.all(np.isfinite(y)) and np.array_equal(x, y)
 
 
-@pytest.mark.parametrize("op", ["fwd", "share", "bwd", "decode"])
+def _bwd_share_inputs(seed, B, H, Hkv, N, d, P, rank, layout, dtype="bf16"):
+    print(f"\n[driver bwd share] seed={seed} B={B} H={H}/{Hkv} N={N} d={d} rank={rank} {layout} {dtype}", flush=True)
+    q, k, v = synth.qkv(seed, B, H, Hkv, N, d, dtype, Nq=N // P)
+    qd, kd, vd = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    do = to_dev(synth.tensor(seed, synth.TENSOR_DOUT, B, H, N // P, d, dtype), dtype)
+    out, lse = ra.ring_attn_fwd_share(qd, kd, vd, P=P, rank=rank, causal=True, layout=layout)
+    return qd, kd, vd, out, do, lse
+
+
+@pytest.mark.parametrize("layout,rank,delays", [("contiguous", 7, (2000, 0)), ("contiguous", 4, (0, 2000)),
+                                                ("striped", 2, (0, 2000)), ("zigzag", 5, (2000, 0))])
+def test_bwd_share_staging(layout, rank, delays):
+    """One device's share of the backward with its kv blocks staged on the
+    copy stream (under injected delays on either stream) is bitwise the
+    share that reads every block in place, and a workspace full of NaN
+    bytes changes nothing."""
+    import torch
+    B, H, Hkv, N, d, P = 1, 4, 2, 8 * 192, 128, 8
+    args = _bwd_share_inputs(32, B, H, Hkv, N, d, P, rank, layout)
+    kw = dict(P=P, rank=rank, causal=True, layout=layout)
+    try:
+        ra.debug_set_staging(False)
+        ref = [from_dev(t) for t in ra.ring_attn_bwd_share(*args, **kw)]
+        ra.debug_set_staging(True)
+        ra.debug_set_delays(*delays)
+        got = [from_dev(t) for t in ra.ring_attn_bwd_share(*args, **kw)]
+    finally:
+        ra.debug_set_staging(True)
+        ra.debug_set_delays(0, 0)
+    nb = ra.load().ring_attn_bwd_share_ws_bytes(B, H, Hkv, N, d, P, ra.RA_BF16)
+    wsn = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda:0")
+    stale = [from_dev(t) for t in ra.ring_attn_bwd_share(*args, **kw, ws=wsn)]
+    for a, b, c in zip(ref, got, stale):
+        assert np.all(np.isfinite(b)) and np.array_equal(a, b) and np.array_equal(a, c)
+
+
+def test_bwd_share_fp32_staging():
+    args = _bwd_share_inputs(33, 1, 2, 1, 8 * 40, 64, 8, 6, "striped", "f32")
+    kw = dict(P=8, rank=6, causal=True, layout="striped")
+    try:
+        ra.debug_set_staging(False)
+        ref = [from_dev(t) for t in ra.ring_attn_bwd_share(*args, **kw)]
+        ra.debug_set_staging(True)
+        ra.debug_set_delays(0, 2000)
+        got = [from_dev(t) for t in ra.ring_attn_bwd_share(*args, **kw)]
+    finally:
+        ra.debug_set_staging(True)
+        ra.debug_set_delays(0, 0)
+    for a, b in zip(ref, got):
+        assert np.all(np.isfinite(b)) and np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("op", ["fwd", "share", "bwd", "bwd_share", "decode"])
 def test_graph_capture_replays(op):
     """The calls allocate nothing and order their two streams with events, so
     a caller can capture one into a HIP graph (the staging copies on the
@@ -240,6 +292,17 @@ def test_graph_capture_replays(op):
         def call():
             ra.ring_attn_bwd(qd, kd, vd, o, do, lse, P=P, causal=True, layout="zigzag", dq=outs[0], dk=outs[1],
                              dv=outs[2], ws=ws)
+    elif op == "bwd_share":
+        qs = qd[:, :, :N // P].contiguous()
+        do = to_dev(synth.tensor(31, synth.TENSOR_DOUT, B, H, N // P, d, "bf16"), "bf16")
+        o, lse = ra.ring_attn_fwd_share(qs, kd, vd, P=P, rank=6, causal=True, layout="contiguous")
+        ws = torch.empty(ra.load().ring_attn_bwd_share_ws_bytes(B, H, Hkv, N, d, P, ra.RA_BF16),
+                         dtype=torch.uint8, device=dev)
+        outs = (torch.empty_like(qs), torch.empty_like(kd), torch.empty_like(vd))
+
+        def call():
+            ra.ring_attn_bwd_share(qs, kd, vd, o, do, lse, P=P, rank=6, causal=True, layout="contiguous",
+                                   dq=outs[0], dk=outs[1], dv=outs[2], ws=ws)
     else:
         q1 = qd[:, :, :1].contiguous()
         ws = torch.empty(ra.ring_attn_decode_ws_bytes(B, H, Hkv, N, d, P), dtype=torch.uint8, device=dev)
