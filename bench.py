@@ -21,6 +21,8 @@ resident in HBM.  Prints ONE JSON line:
                P=8): algorithmic HBM GB/s, with its kernel's roofline
   backward     ring_attn_bwd on the 32k prefill workload: TFLOP/s at 10 d
                FLOPs per unmasked pair per query head
+  backward_share  ring_attn_bwd_share on the headline workload (rank 7's
+               share of the 1M-token ring), same FLOP count
 """
 from __future__ import annotations
 
@@ -292,6 +294,50 @@ def run_backward(args) -> dict:
             "config": {"workload": "backward of the prefill workload (same shapes, upstream gradient seeded)"}}
 
 
+def run_backward_share(args) -> dict:
+    """ring_attn_bwd_share on the headline workload: rank 7's query block
+    (after its forward share) against all 1,048,576 keys."""
+    import torch
+    import blockwise_ring_attention_attn_amd as ra
+    import synth
+    c = SHARE
+    B, H, Hkv, N, d, P = c["B"], c["H"], c["Hkv"], c["N"], c["d"], c["P"]
+    Bl = N // P
+    qd = upload(synth.tensor(c["seed"], synth.TENSOR_Q, B, H, Bl, d, "bf16"), "bf16")
+    kd = upload(synth.tensor(c["seed"], synth.TENSOR_K, B, Hkv, N, d, "bf16"), "bf16")
+    vd = upload(synth.tensor(c["seed"], synth.TENSOR_V, B, Hkv, N, d, "bf16"), "bf16")
+    dod = upload(synth.tensor(c["seed"], synth.TENSOR_DOUT, B, H, Bl, d, "bf16"), "bf16")
+    stream = torch.cuda.current_stream()
+    kw = dict(P=P, rank=c["rank"], causal=c["causal"], layout=c["layout"], stream=stream)
+    out, lse = ra.ring_attn_fwd_share(qd, kd, vd, **kw)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    nb = ra.load().ring_attn_bwd_share_ws_bytes(B, H, Hkv, N, d, P, ra.RA_BF16)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda:0")
+
+    def step():
+        ra.ring_attn_bwd_share(qd, kd, vd, out, dod, lse, dq=dq, dk=dk, dv=dv, ws=ws, **kw)
+
+    step()
+    torch.cuda.synchronize()
+    n = max(2, args.steps // 8)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(n):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / n
+    flops = 2.5 * share_flops(c)
+    tflops = flops / (ms * 1e-3) / 1e12
+    del qd, kd, vd, dod, out, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return {"metric": "causal ring-attn bwd TFLOP/s (10 d per unmasked pair)", "value": tflops, "unit": "TFLOP/s",
+            "ms_per_step": ms, "steps": n, "flops_per_step": flops,
+            "pct_bf16_mfma_peak": 100.0 * tflops / MFMA_BF16_PEAK_TFLOPS,
+            "config": {"workload": "backward of rank 7's share of the 1,048,576-token ring (ring_attn_bwd_share; "
+                                   "same shapes as the headline, upstream gradient seeded)"}}
+
+
 def run_decode(args) -> dict:
     import torch
     import blockwise_ring_attention_attn_amd as ra
@@ -445,8 +491,8 @@ def main():
     ap.add_argument("--no-other-forward", action="store_true",
                     help="skip the 32k prefill and striped GQA forward workloads")
     ap.add_argument("--calib-iters", type=int, default=8192)
-    ap.add_argument("--only", choices=("prefill", "decode", "backward", "striped", "share", "mfma_calib",
-                                       "staging_cost"),
+    ap.add_argument("--only", choices=("prefill", "decode", "backward", "backward_share", "striped", "share",
+                                       "mfma_calib", "staging_cost"),
                     default=None,
                     help="run one workload only (profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -473,6 +519,9 @@ def main():
         return
     if args.only == "backward":
         print(json.dumps(run_backward(args)), flush=True)
+        return
+    if args.only == "backward_share":
+        print(json.dumps(run_backward_share(args)), flush=True)
         return
     if args.only in ("striped", "share", "prefill"):
         c, share = {"striped": (STRIPED, False), "share": (SHARE, True), "prefill": (PREFILL, False)}[args.only]
@@ -510,6 +559,7 @@ def main():
         line["decode"] = run_decode(args)
     if not args.no_backward:
         line["backward"] = run_backward(args)
+        line["backward_share"] = run_backward_share(args)
     print(json.dumps(line), flush=True)
 
 

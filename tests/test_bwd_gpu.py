@@ -36,6 +36,16 @@ from _util import from_dev, host_vals, to_dev
 pytestmark = pytest.mark.gpu
 
 EPS = {"bf16": 2.0 ** -8, "f32": 2.0 ** -12}
+# The element-wise bounds add |dS| |k| over every visible key and loosen as
+# the key count grows (the terms' rounding errors largely cancel), so each
+# gradient is also held, as a whole, to a normwise relative error: about
+# five times the rounding of the results (bf16 2^-9, fp32 2^-24 times the
+# key count), far below the share of one kv block out of P.
+NORMWISE = {"bf16": 1e-2, "f32": 1e-4}
+
+
+def _normwise(got, ref):
+    return float(np.linalg.norm((got - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-30))
 
 
 def _inputs(seed, B, H, Hkv, N, d, dtype="bf16"):
@@ -90,8 +100,10 @@ def _check(seed, B, H, Hkv, N, d, P, causal, layout, dtype="bf16"):
         err = np.abs(got - ref)
         ratio = float((err / (2 * bnd + 1e-6)).max())
         rel = float(err.max() / max(np.abs(ref).max(), 1e-30))
-        print(f"  {name}: max|err|={err.max():.3e} rel={rel:.2e} worst err/bound={ratio:.3f}")
+        nw = _normwise(got, ref)
+        print(f"  {name}: max|err|={err.max():.3e} rel={rel:.2e} normwise={nw:.2e} worst err/bound={ratio:.3f}")
         assert ratio <= 1.0, f"{what}: {name} exceeds its bound (err/bound {ratio:.3f})"
+        assert nw <= NORMWISE[dtype], f"{what}: {name} normwise relative error {nw:.2e}"
     return dq, dk, dv
 
 
@@ -180,8 +192,10 @@ def _check_share(seed, B, H, Hkv, N, d, P, rank, causal, layout, dtype="bf16"):
         assert np.all(np.isfinite(got)), f"{what}: non-finite {name}"
         err = np.abs(got - ref)
         ratio = float((err / (2 * bnd + 1e-6)).max())
-        print(f"  {name}: max|err|={err.max():.3e} worst err/bound={ratio:.3f}")
+        nw = _normwise(got, ref)
+        print(f"  {name}: max|err|={err.max():.3e} normwise={nw:.2e} worst err/bound={ratio:.3f}")
         assert ratio <= 1.0, f"{what}: {name} exceeds its bound (err/bound {ratio:.3f})"
+        assert nw <= NORMWISE[dtype], f"{what}: {name} normwise relative error {nw:.2e}"
     if causal:
         # keys after the rank's last query get exactly zero
         late = np.arange(N) > pos.max()
