@@ -334,6 +334,8 @@ def run_backward_share(args) -> dict:
     return {"metric": "causal ring-attn bwd TFLOP/s (10 d per unmasked pair)", "value": tflops, "unit": "TFLOP/s",
             "ms_per_step": ms, "steps": n, "flops_per_step": flops,
             "pct_bf16_mfma_peak": 100.0 * tflops / MFMA_BF16_PEAK_TFLOPS,
+            "mfma_busy": {k: measured_mfma_busy(f"{k}<128>:backward_share_1m", "attn_bwd.hip")
+                          for k in ("bwd_dkdv_kernel", "bwd_dq_kernel")},
             "config": {"workload": "backward of rank 7's share of the 1,048,576-token ring (ring_attn_bwd_share; "
                                    "same shapes as the headline, upstream gradient seeded)"}}
 
