@@ -251,3 +251,19 @@ def test_bwd_shares_sum_to_the_full_backward():
         dv_sum += from_dev(dv)
     for got, ref in ((dk_sum, dk_f), (dv_sum, dv_f)):
         assert np.abs(got - ref).max() <= 3e-2 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_share_of_one_host_is_the_full_backward(dtype):
+    """With P = 1 the one share is the whole backward: bitwise the same
+    gradients as ring_attn_bwd (the same kernels over the same rows)."""
+    import torch
+    B, H, Hkv, N, d = 1, 4, 2, 300, 64
+    q, k, v, do = _inputs(56, B, H, Hkv, N, d, dtype)
+    qd, kd, vd, dod = (to_dev(x, dtype) for x in (q, k, v, do))
+    out, lse = ra.ring_attn_fwd(qd, kd, vd, P=1, causal=True)
+    full = ra.ring_attn_bwd(qd, kd, vd, out, dod, lse, P=1, causal=True)
+    share = ra.ring_attn_bwd_share(qd, kd, vd, out, dod, lse, P=1, rank=0, causal=True)
+    torch.cuda.synchronize()
+    for a, b in zip(full, share):
+        assert np.array_equal(from_dev(a), from_dev(b))

@@ -284,6 +284,26 @@ def test_bwd_share_ws_bytes():
     assert lib.ring_attn_bwd_share_ws_bytes(1, 1, 1, 1 << 24, 128, 8, ra.RA_BF16) == SIZE_MAX   # 4 GiB kv plane
 
 
+def test_binding_rejects_bad_backward_share_arguments():
+    import torch
+    f32 = torch.float32
+    qs, k = _t(1, 2, 16, 64), _t(1, 1, 64, 64)          # rank block of N / P = 16 rows, P = 4
+    lse = _t(1, 2, 16, dtype=f32)
+    with pytest.raises(ValueError, match="q must hold N / P rows"):
+        ra.ring_attn_bwd_share(_t(1, 2, 32, 64), k, k, _t(1, 2, 32, 64), _t(1, 2, 32, 64), _t(1, 2, 32, dtype=f32),
+                               P=4, rank=1, causal=True)
+    with pytest.raises(ValueError, match="out must have shape"):
+        ra.ring_attn_bwd_share(qs, k, k, _t(1, 2, 64, 64), qs, lse, P=4, rank=1, causal=True)
+    with pytest.raises(ValueError, match="lse must have shape"):
+        ra.ring_attn_bwd_share(qs, k, k, qs, qs, _t(1, 2, 64, dtype=f32), P=4, rank=1, causal=True)
+    with pytest.raises(ValueError, match="dk must have shape"):
+        ra.ring_attn_bwd_share(qs, k, k, qs, qs, lse, P=4, rank=1, causal=True, dk=_t(1, 1, 16, 64))
+    with pytest.raises(TypeError, match="dv must be"):
+        ra.ring_attn_bwd_share(qs, k, k, qs, qs, lse, P=4, rank=1, causal=True, dv=_t(1, 1, 64, 64, dtype=f32))
+    with pytest.raises(ValueError, match="device tensor"):
+        ra.ring_attn_bwd_share(qs, k, k, qs, qs, lse, P=4, rank=1, causal=True)
+
+
 def test_decode_ws_bytes_count_query_head_sub_groups():
     """Query heads beyond 16 per kv head are decoded in sub-groups of 16; the
     partials stay one per (batch, head, split), so the workspace for a
