@@ -317,8 +317,11 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   // order, so the next call's head and query tile are kept (no division per
   // tile).  Lane l of load instruction i fills LDS slot 64 i + l of the tile:
   // row ROWS_PER_INSTR i + l / CPR, chunk slot l % CPR holding logical chunk
-  // (l % CPR) ^ dswz(row).  Contiguous and striped tiles are arithmetic
-  // sequences of natural rows: the row base goes into the scalar offset and
+  // (l % CPR) ^ dswz(row).  Q, dO and the row statistics are read from the
+  // natural-order arrays (N rows per plane) or, for one device's share, from
+  // the host's compact block (Lq rows per plane, block row i at row i).
+  // Contiguous and striped tiles, and every compact tile, are arithmetic
+  // sequences of rows: the row base goes into the scalar offset and
   // each lane's vector offset is a constant.  Zigzag tiles and a head's ragged
   // last tile take per-lane offsets, rows past the block out of the buffer's
   // range (they read zeros); a tile index past the last one loads zeros.
