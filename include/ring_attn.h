@@ -16,7 +16,8 @@
  *      lse     [B, H,   Nq]      float32, natural log of the scaled logits
  *    Query head h reads kv head floor(h * Hkv / H) (grouped-query attention,
  *    consecutive groups).  d must be 64 or 128.
- *  - All pointers named q, k, v, out, lse, m, l, o, ws are DEVICE pointers
+ *  - All pointers named q, k, v, out, lse, m, l, o, dout, dq, dk, dv, ws are
+ *    DEVICE pointers
  *    owned by the caller; the library never allocates device memory inside a
  *    call and never frees caller memory.  Scratch state lives in `ws`, a
  *    caller-allocated device workspace of at least the size reported by the
@@ -52,8 +53,9 @@
  *    one (batch, kv head) plane must stay below 2 GiB (N / P * d * 2 bytes);
  *    whole planes may be larger (a striped ring whose plane is 2 GiB or more
  *    stages its first step's blocks instead of reading them in place).
- *    The bf16 ring_attn_bwd needs one head plane below 2 GiB; the fp32
- *    backward and decode have no such limit (64-bit addressing).
+ *    The bf16 ring_attn_bwd and ring_attn_bwd_share need one head plane
+ *    (N * d * 2 bytes) below 2 GiB; the fp32 backward and decode have no
+ *    such limit (64-bit addressing).
  */
 #ifndef RING_ATTN_H
 #define RING_ATTN_H
