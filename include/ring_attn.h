@@ -17,9 +17,8 @@
  *    Query head h reads kv head floor(h * Hkv / H) (grouped-query attention,
  *    consecutive groups).  d must be 64 or 128.
  *  - All pointers named q, k, v, out, lse, m, l, o, dout, dq, dk, dv, ws are
- *    DEVICE pointers
- *    owned by the caller; the library never allocates device memory inside a
- *    call and never frees caller memory.  Scratch state lives in `ws`, a
+ *    DEVICE pointers owned by the caller; the library never allocates device
+ *    memory inside a call and never frees caller memory.  Scratch state lives in `ws`, a
  *    caller-allocated device workspace of at least the size reported by the
  *    matching *_ws_bytes() query, aligned to 256 bytes.  Tensor pointers
  *    (q, k, v, out, o, dout, dq, dk, dv) must be 16-byte aligned and the
