@@ -26,6 +26,7 @@ EXPORTS = (
     "ring_attn_step", "ring_attn_finalize", "lse_merge",
     "ring_attn_decode_ws_bytes", "ring_attn_decode", "ring_attn_decode_noalloc",
     "ring_attn_bwd_ws_bytes", "ring_attn_bwd", "ring_attn_bwd_share_ws_bytes", "ring_attn_bwd_share",
+    "ring_attn_bwd_prep", "ring_attn_bwd_step",
     "ra_last_error", "ra_version", "ra_debug_set_delays", "ra_prof_enable", "ra_prof_reset", "ra_prof_read",
     "ra_diag_mfma_loop", "ra_debug_set_staging",
 )
@@ -91,6 +92,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.ring_attn_bwd_share.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, ll, i, i, i, i, i, f, i, vp,
                                         vp, st]
     lib.ring_attn_bwd_share.restype = i
+    lib.ring_attn_bwd_prep.argtypes = [vp, vp, vp, vp, ll, i, i, vp]
+    lib.ring_attn_bwd_prep.restype = i
+    lib.ring_attn_bwd_step.argtypes = [vp, vp, vp, ra_kv_block, vp, vp, vp, ctypes.POINTER(ra_mask_desc), vp]
+    lib.ring_attn_bwd_step.restype = i
     lib.ra_last_error.argtypes = []
     lib.ra_last_error.restype = ctypes.c_char_p
     lib.ra_version.argtypes = []
@@ -337,6 +342,55 @@ def ring_attn_bwd_share(q, k, v, out, dout, lse, *, P: int, rank: int, causal: b
                                    LAYOUTS[layout], scale, code, _stream(stream),
                                    _ptr(wst) if wst is not None else None, nb))
     return dq, dk, dv
+
+
+def ring_attn_bwd_prep(out, dout, lse, *, rowstat=None, stream=None):
+    """Row statistics of a query block for ring_attn_bwd_step (see ring_attn.h).
+
+    out, dout [B, H, Lq, d] (bf16 or fp32), lse [B, H, Lq] fp32 from the
+    forward.  Returns rowstat [B, H, Lq, 2] fp32 (lse * log2 e, dO . O).
+    """
+    torch = _torch()
+    lib = load()
+    _tensor(out, "out")
+    code = _dtype_code(out)
+    if out.dim() != 4:
+        raise ValueError("out must be 4-D: [B, H, Lq, d]")
+    B, H, Lq, d = out.shape
+    _tensor(dout, "dout", tuple(out.shape), out.dtype)
+    _tensor(lse, "lse", (B, H, Lq), torch.float32)
+    if rowstat is not None:
+        _tensor(rowstat, "rowstat", (B, H, Lq, 2), torch.float32)
+    _devices(out=out, dout=dout, lse=lse, rowstat=rowstat)
+    if rowstat is None:
+        rowstat = torch.empty((B, H, Lq, 2), dtype=torch.float32, device=out.device)
+    _check(lib.ring_attn_bwd_prep(_ptr(out), _ptr(dout), _ptr(lse), _ptr(rowstat), B * H * Lq, d, code,
+                                  _stream(stream)))
+    return rowstat
+
+
+def ring_attn_bwd_step(q_blk, k_blk, v_blk, dout_blk, rowstat, dq_acc, dk_acc, dv_acc, *, causal: bool,
+                       layout: str = "contiguous", P: int = 1, q_rank: int = 0, kv_rank: int = 0,
+                       scale: float | None = None, stream=None):
+    """One (query block, kv block) pair of a ring backward, added in place
+    into the fp32 accumulators dq_acc [B, H, Lq, d] and dk_acc, dv_acc
+    [B, Hkv, Lkv, d] (see ring_attn.h).  rowstat from ring_attn_bwd_prep."""
+    torch = _torch()
+    lib = load()
+    B, H, Hkv, Lq, Lkv, d, code = _qkv(q_blk, k_blk, v_blk)
+    _tensor(dout_blk, "dout_blk", tuple(q_blk.shape), q_blk.dtype)
+    _tensor(rowstat, "rowstat", (B, H, Lq, 2), torch.float32)
+    _tensor(dq_acc, "dq_acc", (B, H, Lq, d), torch.float32)
+    _tensor(dk_acc, "dk_acc", (B, Hkv, Lkv, d), torch.float32)
+    _tensor(dv_acc, "dv_acc", (B, Hkv, Lkv, d), torch.float32)
+    _devices(q_blk=q_blk, k_blk=k_blk, v_blk=v_blk, dout_blk=dout_blk, rowstat=rowstat, dq_acc=dq_acc,
+             dk_acc=dk_acc, dv_acc=dv_acc)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    md = ra_mask_desc(B, H, Hkv, d, Lq, Lkv, scale, code, int(bool(causal)), LAYOUTS[layout], P,
+                      q_rank, kv_rank)
+    _check(lib.ring_attn_bwd_step(_ptr(q_blk), _ptr(dout_blk), _ptr(rowstat), ra_kv_block(_ptr(k_blk), _ptr(v_blk)),
+                                  _ptr(dq_acc), _ptr(dk_acc), _ptr(dv_acc), ctypes.byref(md), _stream(stream)))
+    return dq_acc, dk_acc, dv_acc
 
 
 def init_state(B, H, Lq, d, device):

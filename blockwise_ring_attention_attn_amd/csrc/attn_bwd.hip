@@ -279,7 +279,11 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
   const int my_key = key0 + pw * 32 + col;
   const bool key_ok = my_key < A.Lkv;
   const int64_t kv_plane = (int64_t)w.b * A.Hkv + w.hkv;
-  const int64_t key_row = key_ok ? nat_row<LAYOUT>(A, kv_plane, G.n_tok, w.kv_rank, my_key, A.Lkv) : 0;
+  // this key's row in the dK / dV accumulators and outputs (and in the
+  // natural-order K / V when they are read in place)
+  const int64_t key_row = !key_ok        ? 0
+                          : G.kv_compact ? kv_plane * A.Lkv + my_key
+                                         : nat_row<LAYOUT>(A, kv_plane, G.n_tok, w.kv_rank, my_key, A.Lkv);
 
   // first query row that sees any key of the workgroup (the limit is
   // non-decreasing in the row)

@@ -168,7 +168,8 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dkdv_f32_kernel(BwdArgs G, in
   const int group = A.H / A.Hkv;
   const int64_t plane = (int64_t)w.b * A.Hkv + w.hkv;
   const int64_t kr = kv_read_row(G, w, j) * D;
-  const int64_t acc_row = plane * G.n_tok + host_row(A.layout, w.kv_rank, j, A.Lkv, A.P);
+  const int64_t acc_row =
+      G.kv_compact ? plane * A.Lkv + j : plane * G.n_tok + host_row(A.layout, w.kv_rank, j, A.Lkv, A.P);
   float kv[NC], vv[NC], dk[NC], dv[NC];
 #pragma unroll
   for (int e = 0; e < NC; ++e) {

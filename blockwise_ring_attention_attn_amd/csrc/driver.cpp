@@ -1085,11 +1085,9 @@ ra_status ring_attn_bwd_share(const void* q, const void* k, const void* v, const
   return RA_OK;
 }
 
-ra_status ring_attn_step(const void* q_blk, ra_kv_block kv_blk, float* m, float* l, float* o,
-                         const ra_mask_desc* md, void* stream) {
-  g_err.clear();
-  if (!md) return fail(RA_EINVAL, "null mask_desc");
-  if (!q_blk || !kv_blk.k || !kv_blk.v || !m || !l || !o) return fail(RA_EINVAL, "null tensor pointer");
+// Checks of a (query block, kv block) pair's description shared by the
+// forward and backward step calls.
+static ra_status check_mask_desc(const ra_mask_desc* md) {
   if (md->B < 1 || md->H < 1 || md->Hkv < 1 || md->H % md->Hkv)
     return fail(RA_EINVAL, "bad head counts B=%d H=%d Hkv=%d", md->B, md->H, md->Hkv);
   if (md->d != 64 && md->d != 128) return fail(RA_EINVAL, "head dim d must be 64 or 128 (got %d)", md->d);
@@ -1109,6 +1107,18 @@ ra_status ring_attn_step(const void* q_blk, ra_kv_block kv_blk, float* m, float*
     if (sp != RA_OK) return sp;
   }
   if (!(md->scale > 0.f) || !std::isfinite(md->scale)) return fail(RA_EINVAL, "scale must be finite and > 0");
+  return RA_OK;
+}
+
+ra_status ring_attn_step(const void* q_blk, ra_kv_block kv_blk, float* m, float* l, float* o,
+                         const ra_mask_desc* md, void* stream) {
+  g_err.clear();
+  if (!md) return fail(RA_EINVAL, "null mask_desc");
+  if (!q_blk || !kv_blk.k || !kv_blk.v || !m || !l || !o) return fail(RA_EINVAL, "null tensor pointer");
+  {
+    const ra_status mdst = check_mask_desc(md);
+    if (mdst != RA_OK) return mdst;
+  }
   {
     const ra_status al = check_tensor_align({q_blk, kv_blk.k, kv_blk.v, o}, {m, l});
     if (al != RA_OK) return al;
@@ -1166,6 +1176,97 @@ ra_status lse_merge(float* o_a, float* lse_a, const float* o_b, const float* lse
   if (!o_a || !lse_a || !o_b || !lse_b) return fail(RA_EINVAL, "null tensor pointer");
   MergeArgs a{o_a, lse_a, o_b, lse_b, rows, d};
   RA_HIP(launch_lse_merge(a, static_cast<hipStream_t>(stream)), "lse_merge launch");
+  return RA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Backward building blocks for a caller's own ring ([TKG] §7): the row
+// statistics of a query block, then one (query block, kv block) pair's
+// gradient contributions added into caller-owned fp32 accumulators.
+// ---------------------------------------------------------------------------
+ra_status ring_attn_bwd_prep(const void* out, const void* dout, const float* lse, float* rowstat, long long rows,
+                             int d, ra_dtype dtype, void* stream) {
+  g_err.clear();
+  if (rows < 0) return fail(RA_EINVAL, "rows must be >= 0");
+  if (d != 64 && d != 128) return fail(RA_EINVAL, "head dim d must be 64 or 128 (got %d)", d);
+  if (!dtype_ok(dtype)) return fail(RA_EINVAL, "unknown dtype %d", (int)dtype);
+  if (rows == 0) return RA_OK;  // nothing to do; empty tensors may carry null pointers
+  if (!out || !dout || !lse || !rowstat) return fail(RA_EINVAL, "null tensor pointer");
+  {
+    const ra_status al = check_tensor_align({out, dout, rowstat}, {lse});
+    if (al != RA_OK) return al;
+  }
+  hipStream_t cs = static_cast<hipStream_t>(stream);
+  if (dtype == RA_F32)
+    RA_HIP(launch_bwd_prep_f32(static_cast<const float*>(out), static_cast<const float*>(dout), lse, rowstat,
+                               (int64_t)rows, d, cs),
+           "prep launch");
+  else
+    RA_HIP(launch_bwd_prep(out, dout, lse, rowstat, (int64_t)rows, d, cs), "prep launch");
+  return RA_OK;
+}
+
+ra_status ring_attn_bwd_step(const void* q_blk, const void* dout_blk, const float* rowstat, ra_kv_block kv_blk,
+                             float* dq_acc, float* dk_acc, float* dv_acc, const ra_mask_desc* md, void* stream) {
+  g_err.clear();
+  if (!md) return fail(RA_EINVAL, "null mask_desc");
+  if (!q_blk || !dout_blk || !rowstat || !kv_blk.k || !kv_blk.v || !dq_acc || !dk_acc || !dv_acc)
+    return fail(RA_EINVAL, "null tensor pointer");
+  {
+    const ra_status mdst = check_mask_desc(md);
+    if (mdst != RA_OK) return mdst;
+  }
+  // the bf16 kernels read a query block's plane (Q, dO) through 32-bit
+  // buffer offsets, as they read a key/value block
+  if (md->dtype == RA_BF16 && (uint64_t)md->Lq * md->d * esize(md->dtype) >= kSpanLimit)
+    return fail(RA_EINVAL, "the bf16 backward needs one query block plane (Lq * d elements) below 2 GiB");
+  {
+    const ra_status al = check_tensor_align({q_blk, dout_blk, rowstat, kv_blk.k, kv_blk.v, dq_acc, dk_acc, dv_acc}, {});
+    if (al != RA_OK) return al;
+  }
+  const bool f32 = md->dtype == RA_F32;
+  const int64_t nqt = (md->Lq + bwd_dq_rows() - 1) / bwd_dq_rows();
+  const int64_t nkt = (md->Lkv + bwd_dkdv_rows() - 1) / bwd_dkdv_rows();
+  if ((int64_t)md->B * md->H * nqt > 0x7fffffffLL || (int64_t)md->B * md->Hkv * nkt > 0x7fffffffLL ||
+      (f32 && ((int64_t)md->B * md->H * md->Lq / 4 >= 0x7fffffffLL ||
+               (int64_t)md->B * md->Hkv * md->Lkv / 4 >= 0x7fffffffLL)))
+    return fail(RA_EINVAL, "problem too large for one launch");
+  if (!pair_active(md->layout, md->causal, md->P, md->q_rank, md->kv_rank, md->Lq, md->Lkv)) return RA_OK;
+  BwdArgs a{};
+  a.s.q = q_blk;
+  a.s.k = kv_blk.k;
+  a.s.v = kv_blk.v;
+  a.s.q_plane_rows = md->Lq;
+  a.s.kv_plane_rows = md->Lkv;
+  a.s.B = md->B; a.s.H = md->H; a.s.Hkv = md->Hkv;
+  a.s.Lq = (int)md->Lq; a.s.Lkv = (int)md->Lkv;
+  a.s.P = md->P;
+  a.s.layout = md->layout;
+  a.s.host_lo = md->q_rank;
+  a.s.n_hosts = 1;
+  a.s.kv_shift = md->q_rank - md->kv_rank;
+  a.s.q_mode = ROWS_COMPACT;
+  a.s.kv_mode = ROWS_COMPACT;
+  a.s.causal = md->causal ? 1 : 0;
+  a.s.n_qtiles = (int)nqt;
+  a.s.scale_log2 = md->scale * 1.4426950408889634f;
+  a.dout = dout_blk;
+  a.rowstat = rowstat;
+  a.dq_acc = dq_acc;
+  a.dk_acc = dk_acc;
+  a.dv_acc = dv_acc;
+  a.n_tok = md->Lkv;
+  a.scale = md->scale;
+  a.n_kvtiles = (int)nkt;
+  a.first = a.kv_first = 0;   // add into the caller's accumulators
+  a.q_fin = a.kv_fin = 0;     // and keep the sums in fp32
+  a.kv_staged = 1;            // the kv block is compact, as a staged block
+  a.stage_host0 = md->q_rank;
+  a.q_compact = 1;
+  a.kv_compact = 1;
+  hipStream_t cs = static_cast<hipStream_t>(stream);
+  RA_HIP(f32 ? launch_bwd_dkdv_f32(a, md->d, cs) : launch_bwd_dkdv(a, md->d, cs), "dK/dV kernel launch");
+  RA_HIP(f32 ? launch_bwd_dq_f32(a, md->d, cs) : launch_bwd_dq(a, md->d, cs), "dQ kernel launch");
   return RA_OK;
 }
 

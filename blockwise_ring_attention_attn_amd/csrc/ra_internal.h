@@ -73,8 +73,9 @@ struct BwdArgs {
   // Where the kernels read K and V: 0 in place from the natural-order
   // arrays (rows of kv block kv_rank); 1 from a host-major staging buffer
   // (s.k / s.v), where query host q_rank's current block is plane
-  // (q_rank * B + b) * Hkv + hkv of Lkv rows, in block order.  The dK / dV
-  // accumulators always stay at the natural rows of the block.
+  // ((q_rank - stage_host0) * B + b) * Hkv + hkv of Lkv rows, in block
+  // order.  The dK / dV accumulators stay at the natural rows of the block
+  // unless kv_compact is set.
   int kv_staged;
   // fp32 backward: the final fp32 gradients (the bf16 outputs above unused)
   float* dq_out_f32;
@@ -88,6 +89,10 @@ struct BwdArgs {
   int q_compact;
   int kv_first;
   int stage_host0;
+  // Rows of the dK / dV accumulators: 0 the natural rows of the block
+  // (n_tok per plane); 1 compact, Lkv per plane and block row j at row j
+  // (one ring step on caller-owned block accumulators, ring_attn_bwd_step).
+  int kv_compact;
 };
 
 struct MergeArgs {

@@ -295,6 +295,40 @@ ra_status ring_attn_bwd_share(const void* q, const void* k, const void* v, const
                               void* stream, void* ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------
+ * Backward building blocks for a caller's own ring ([TKG] §7), the
+ * counterparts of ring_attn_step: each host keeps its query block, its
+ * forward output and lse, and as the kv blocks pass by adds one pair's
+ * gradient contributions; the dK, dV sums travel on with their block.
+ *
+ * ring_attn_bwd_prep -- the row statistics a query block's backward steps
+ * read: for each of `rows` rows, rowstat[row][0] = lse * log2(e) (+inf where
+ * lse = -inf, so that the row contributes nothing) and rowstat[row][1] =
+ * delta = sum_c dO[row][c] * O[row][c].  out, dout [rows, d] in `dtype`
+ * (16-byte aligned), lse [rows] fp32, rowstat [rows][2] fp32 (16-byte
+ * aligned; overwritten).  rows = 0 does nothing.
+ *
+ * ring_attn_bwd_step -- one (query block, kv block) pair, positions and
+ * mask as described by mask_desc (the fields and checks of
+ * ring_attn_step), ADDED into caller-owned fp32 accumulators (zero them
+ * before the first step):
+ *   dq_acc [B, H,   Lq,  d] += scale dS K
+ *   dk_acc [B, Hkv, Lkv, d] += scale dS^T Q   (all query heads of the group)
+ *   dv_acc [B, Hkv, Lkv, d] += P^T dO
+ * with P = exp(S - lse) recomputed from the scores and dS = P (dO V^T -
+ * delta), the formulas of ring_attn_bwd.  q_blk, dout_blk [B, H, Lq, d]
+ * and k, v of kv_blk [B, Hkv, Lkv, d] in mask_desc->dtype, rowstat
+ * [B, H, Lq][2] from ring_attn_bwd_prep on the block's out, dout and lse.
+ * Every pointer 16-byte aligned.  bf16: one query or key/value block plane
+ * below 2 GiB.  A pair with no visible key launches nothing.  Steps that
+ * add into the same accumulators must be ordered (one stream).
+ * ---------------------------------------------------------------------- */
+ra_status ring_attn_bwd_prep(const void* out, const void* dout, const float* lse, float* rowstat, long long rows,
+                             int d, ra_dtype dtype, void* stream);
+ra_status ring_attn_bwd_step(const void* q_blk, const void* dout_blk, const float* rowstat, ra_kv_block kv_blk,
+                             float* dq_acc, float* dk_acc, float* dv_acc, const ra_mask_desc* mask_desc,
+                             void* stream);
+
+/* ------------------------------------------------------------------------
  * Diagnostics.
  * ra_last_error: message of the last failed call on this thread ("" if none).
  * ra_version: library version string.

@@ -267,3 +267,78 @@ def test_bwd_share_of_one_host_is_the_full_backward(dtype):
     torch.cuda.synchronize()
     for a, b in zip(full, share):
         assert np.array_equal(from_dev(a), from_dev(b))
+
+
+# ---------------------------------------------------------------------------
+# The backward building blocks: a ring backward composed on the host from
+# ring_attn_bwd_prep and ring_attn_bwd_step over every (query block, kv
+# block) pair, with per-block fp32 accumulators, against the oracle.
+# ---------------------------------------------------------------------------
+def _ring_by_steps(seed, B, H, Hkv, N, d, P, causal, layout, dtype="bf16"):
+    import torch
+    q, k, v, do = _inputs(seed, B, H, Hkv, N, d, dtype)
+    qd, kd, vd, dod = (to_dev(x, dtype) for x in (q, k, v, do))
+    out, lse = ra.ring_attn_fwd(qd, kd, vd, P=P, causal=causal, layout=layout)
+    pos = oracle.host_positions(N, P, layout)
+    idx = [torch.from_numpy(p).to(qd.device) for p in pos]
+    blk = lambda t, r: t.index_select(2, idx[r]).contiguous()
+    qs = [blk(qd, r) for r in range(P)]
+    dos = [blk(dod, r) for r in range(P)]
+    ks, vs = [blk(kd, r) for r in range(P)], [blk(vd, r) for r in range(P)]
+    rst = [ra.ring_attn_bwd_prep(blk(out, r), dos[r], lse.index_select(2, idx[r]).contiguous()) for r in range(P)]
+    Bl = N // P
+    f32 = torch.float32
+    dq = [torch.zeros((B, H, Bl, d), dtype=f32, device=qd.device) for _ in range(P)]
+    dk = [torch.zeros((B, Hkv, Bl, d), dtype=f32, device=qd.device) for _ in range(P)]
+    dv = [torch.zeros((B, Hkv, Bl, d), dtype=f32, device=qd.device) for _ in range(P)]
+    for s in range(P):          # reverse ring: host r meets kv block (r + s) mod P
+        for r in range(P):
+            j = (r + s) % P
+            ra.ring_attn_bwd_step(qs[r], ks[j], vs[j], dos[r], rst[r], dq[r], dk[j], dv[j], causal=causal,
+                                  layout=layout, P=P, q_rank=r, kv_rank=j)
+    torch.cuda.synchronize()
+    full = [np.zeros((B, H, N, d)), np.zeros((B, Hkv, N, d)), np.zeros((B, Hkv, N, d))]
+    for r in range(P):
+        full[0][:, :, pos[r]] = from_dev(dq[r])
+        full[1][:, :, pos[r]] = from_dev(dk[r])
+        full[2][:, :, pos[r]] = from_dev(dv[r])
+    return q, k, v, do, full
+
+
+@pytest.mark.parametrize("layout,causal,dtype", [("contiguous", True, "bf16"), ("striped", True, "bf16"),
+                                                 ("zigzag", True, "bf16"), ("contiguous", False, "bf16"),
+                                                 ("zigzag", True, "f32")])
+def test_bwd_steps_compose_the_ring_backward(layout, causal, dtype):
+    """GQA 2:1, d = 128 (64 for fp32), P = 4 ring blocks of 130 rows."""
+    d = 128 if dtype == "bf16" else 64
+    B, H, Hkv, N, P = 1, 4, 2, 4 * 130, 4
+    q, k, v, do, (dq, dk, dv) = _ring_by_steps(57, B, H, Hkv, N, d, P, causal, layout, dtype)
+    qh, kh, vh, doh = (host_vals(x, dtype) for x in (q, k, v, do))
+    scale = 1.0 / math.sqrt(d)
+    dq_r, dk_r, dv_r, parts = oracle.attention_bwd(qh, kh, vh, doh, scale=scale, causal=causal, parts=True)
+    bq, bk, bv = _bounds(qh, kh, vh, doh, parts, B, H, Hkv, scale, dq_r, dk_r, dv_r, EPS[dtype])
+    what = f"bwd steps {layout} causal={causal} {dtype}"
+    for name, got, ref, bnd in (("dq", dq, dq_r, bq), ("dk", dk, dk_r, bk), ("dv", dv, dv_r, bv)):
+        assert np.all(np.isfinite(got)), f"{what}: non-finite {name}"
+        err = np.abs(got - ref)
+        ratio = float((err / (2 * bnd + 1e-6)).max())
+        nw = _normwise(got, ref)
+        print(f"  {name}: max|err|={err.max():.3e} normwise={nw:.2e} worst err/bound={ratio:.3f}")
+        assert ratio <= 1.0, f"{what}: {name} exceeds its bound (err/bound {ratio:.3f})"
+        assert nw <= NORMWISE[dtype], f"{what}: {name} normwise relative error {nw:.2e}"
+
+
+def test_bwd_step_of_an_invisible_pair_changes_nothing():
+    """Contiguous causal: host 0's queries see nothing of kv block 3; the
+    step launches nothing and the accumulators keep their values."""
+    import torch
+    B, H, Hkv, Bl, d, P = 1, 2, 1, 64, 64, 4
+    q, k, v, do = _inputs(58, B, H, Hkv, Bl, d, "bf16")
+    qd, kd, vd, dod = (to_dev(x, "bf16") for x in (q, k, v, do))
+    rst = torch.zeros((B, H, Bl, 2), dtype=torch.float32, device=qd.device)
+    accs = [torch.full((B, H, Bl, d), 7.0, device=qd.device), torch.full((B, Hkv, Bl, d), 7.0, device=qd.device),
+            torch.full((B, Hkv, Bl, d), 7.0, device=qd.device)]
+    ra.ring_attn_bwd_step(qd, kd, vd, dod, rst, *accs, causal=True, P=P, q_rank=0, kv_rank=3)
+    torch.cuda.synchronize()
+    for a in accs:
+        assert bool((a == 7.0).all())

@@ -160,6 +160,61 @@ def test_step_rejects_invalid(lib):
     assert b"zigzag" in lib.ra_last_error()
 
 
+def test_bwd_step_and_prep_reject_invalid(lib):
+    kvb = ra.ra_kv_block(256, 512)
+    md = ra.ra_mask_desc(1, 2, 1, 64, 16, 16, 0.125, ra.RA_BF16, 1, 0, 4, 1, 0)
+    ok = dict(q=768, do=1024, rs=1280, dq=1536, dk=1792, dv=2048)
+
+    def step(md_ref, **kw):
+        a = dict(ok, **kw)
+        return lib.ring_attn_bwd_step(a["q"], a["do"], a["rs"], kvb, a["dq"], a["dk"], a["dv"], md_ref, None)
+
+    assert step(None) == ra.RA_EINVAL and b"mask_desc" in lib.ra_last_error()
+    assert step(ctypes.byref(md), rs=None) == ra.RA_EINVAL and b"null" in lib.ra_last_error()
+    assert step(ctypes.byref(md), dv=None) == ra.RA_EINVAL
+    assert step(ctypes.byref(md), dk=1800) == ra.RA_EINVAL and b"16-byte" in lib.ra_last_error()
+    bad = ra.ra_mask_desc(1, 2, 1, 64, 16, 16, 0.125, ra.RA_BF16, 1, 0, 4, 5, 0)       # q_rank >= P
+    assert step(ctypes.byref(bad)) == ra.RA_EINVAL and b"ring" in lib.ra_last_error()
+    bad = ra.ra_mask_desc(1, 2, 1, 96, 16, 16, 0.125, ra.RA_BF16, 1, 0, 4, 1, 0)       # d
+    assert step(ctypes.byref(bad)) == ra.RA_EINVAL and b"64 or 128" in lib.ra_last_error()
+    bad = ra.ra_mask_desc(1, 2, 1, 64, 15, 15, 0.125, ra.RA_BF16, 1, 2, 4, 1, 0)       # zigzag causal, odd length
+    assert step(ctypes.byref(bad)) == ra.RA_EINVAL and b"zigzag" in lib.ra_last_error()
+    bad = ra.ra_mask_desc(1, 1, 1, 128, 1 << 23, 16, 0.125, ra.RA_BF16, 0, 0, 1, 0, 0)  # 2 GiB query plane
+    assert step(ctypes.byref(bad)) == ra.RA_EINVAL and b"query block plane" in lib.ra_last_error()
+    # prep: rows, d, dtype, pointers, alignment; zero rows is a no-op
+    assert lib.ring_attn_bwd_prep(256, 512, 768, 1024, -1, 64, 1, None) == ra.RA_EINVAL
+    assert lib.ring_attn_bwd_prep(256, 512, 768, 1024, 8, 80, 1, None) == ra.RA_EINVAL
+    assert lib.ring_attn_bwd_prep(256, 512, 768, 1024, 8, 64, 5, None) == ra.RA_EINVAL
+    assert lib.ring_attn_bwd_prep(256, None, 768, 1024, 8, 64, 1, None) == ra.RA_EINVAL
+    assert lib.ring_attn_bwd_prep(256, 512, 768, 1032, 8, 64, 1, None) == ra.RA_EINVAL
+    assert b"16-byte" in lib.ra_last_error()
+    assert lib.ring_attn_bwd_prep(None, None, None, None, 0, 64, 1, None) == ra.RA_OK
+
+
+def test_binding_rejects_bad_backward_step_arguments():
+    import torch
+    f32 = torch.float32
+    q, k = _t(1, 2, 16, 64), _t(1, 1, 16, 64)
+    rs = _t(1, 2, 16, 2, dtype=f32)
+    dq, dk = _t(1, 2, 16, 64, dtype=f32), _t(1, 1, 16, 64, dtype=f32)
+    with pytest.raises(ValueError, match="rowstat must have shape"):
+        ra.ring_attn_bwd_step(q, k, k, q, _t(1, 2, 16, dtype=f32), dq, dk, dk.clone(), causal=True)
+    with pytest.raises(TypeError, match="dq_acc must be"):
+        ra.ring_attn_bwd_step(q, k, k, q, rs, q, dk, dk.clone(), causal=True)
+    with pytest.raises(ValueError, match="dk_acc must have shape"):
+        ra.ring_attn_bwd_step(q, k, k, q, rs, dq, _t(1, 2, 16, 64, dtype=f32), dk, causal=True)
+    with pytest.raises(ValueError, match="dout_blk must have shape"):
+        ra.ring_attn_bwd_step(q, k, k, _t(1, 2, 8, 64), rs, dq, dk, dk.clone(), causal=True)
+    with pytest.raises(ValueError, match="device tensor"):
+        ra.ring_attn_bwd_step(q, k, k, q, rs, dq, dk, dk.clone(), causal=True)
+    with pytest.raises(ValueError, match="lse must have shape"):
+        ra.ring_attn_bwd_prep(q, q, _t(1, 2, 8, dtype=f32))
+    with pytest.raises(TypeError, match="dout must be"):
+        ra.ring_attn_bwd_prep(q, q.float(), _t(1, 2, 16, dtype=f32))
+    with pytest.raises(ValueError, match="device tensor"):
+        ra.ring_attn_bwd_prep(q, q, _t(1, 2, 16, dtype=f32))
+
+
 def test_merge_decode_reject_invalid(lib):
     assert lib.lse_merge(None, 1, 1, 1, 4, 8, None) == ra.RA_EINVAL
     assert lib.lse_merge(1, 1, 1, 1, 4, 0, None) == ra.RA_EINVAL
