@@ -342,3 +342,23 @@ def test_bwd_step_of_an_invisible_pair_changes_nothing():
     torch.cuda.synchronize()
     for a in accs:
         assert bool((a == 7.0).all())
+
+
+@pytest.mark.parametrize("layout,dtype", [("contiguous", "bf16"), ("zigzag", "bf16"), ("striped", "f32")])
+def test_bwd_steps_are_bitwise_the_ring_backward(layout, dtype):
+    """The composed steps add the same products in the same order as
+    ring_attn_bwd (its first step writes 0 + x, its last rounds the fp32
+    sum once), so rounding their fp32 accumulators like it gives bitwise
+    its gradients."""
+    import torch
+    B, H, Hkv, N, d, P = 1, 4, 2, 4 * 96, 128, 4
+    q, k, v, do, (dq, dk, dv) = _ring_by_steps(59, B, H, Hkv, N, d, P, True, layout, dtype)
+    qd, kd, vd, dod = (to_dev(x, dtype) for x in (q, k, v, do))
+    out, lse = ra.ring_attn_fwd(qd, kd, vd, P=P, causal=True, layout=layout)
+    ref = ra.ring_attn_bwd(qd, kd, vd, out, dod, lse, P=P, causal=True, layout=layout)
+    torch.cuda.synchronize()
+    for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        g = torch.from_numpy(got.astype(np.float32))
+        if dtype == "bf16":
+            g = g.to(torch.bfloat16)
+        assert np.array_equal(from_dev(g), from_dev(r)), f"{name} differs from ring_attn_bwd"
