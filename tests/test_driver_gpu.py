@@ -254,7 +254,7 @@ def test_bwd_share_fp32_staging():
         assert np.all(np.isfinite(b)) and np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("op", ["fwd", "share", "bwd", "bwd_share", "decode"])
+@pytest.mark.parametrize("op", ["fwd", "share", "bwd", "bwd_share", "bwd_steps", "decode"])
 def test_graph_capture_replays(op):
     """The calls allocate nothing and order their two streams with events, so
     a caller can capture one into a HIP graph (the staging copies on the
@@ -303,6 +303,31 @@ def test_graph_capture_replays(op):
         def call():
             ra.ring_attn_bwd_share(qs, kd, vd, o, do, lse, P=P, rank=6, causal=True, layout="contiguous",
                                    dq=outs[0], dk=outs[1], dv=outs[2], ws=ws)
+    elif op == "bwd_steps":
+        # a caller's own ring backward: prep per query block, the accumulators
+        # cleared by fill kernels, then every (query block, kv block) step
+        Bl = N // P
+        do = to_dev(synth.tensor(31, synth.TENSOR_DOUT, B, H, N, d, "bf16"), "bf16")
+        o, lse = ra.ring_attn_fwd(qd, kd, vd, P=P, causal=True, layout="contiguous")
+        blk = lambda t, r: t[:, :, r * Bl:(r + 1) * Bl].contiguous()
+        qs, os_, dos, ls = ([blk(t, r) for r in range(P)] for t in (qd, o, do, lse))
+        ks, vs = [blk(kd, r) for r in range(P)], [blk(vd, r) for r in range(P)]
+        rst = [torch.empty((B, H, Bl, 2), dtype=torch.float32, device=dev) for _ in range(P)]
+        dq = [torch.empty((B, H, Bl, d), dtype=torch.float32, device=dev) for _ in range(P)]
+        dk = [torch.empty((B, Hkv, Bl, d), dtype=torch.float32, device=dev) for _ in range(P)]
+        dv = [torch.empty((B, Hkv, Bl, d), dtype=torch.float32, device=dev) for _ in range(P)]
+        outs = tuple(rst + dq + dk + dv)
+
+        def call():
+            for t in dq + dk + dv:
+                t.zero_()
+            for r in range(P):
+                ra.ring_attn_bwd_prep(os_[r], dos[r], ls[r], rowstat=rst[r])
+            for s in range(P):
+                for r in range(P):
+                    j = (r + s) % P
+                    ra.ring_attn_bwd_step(qs[r], ks[j], vs[j], dos[r], rst[r], dq[r], dk[j], dv[j], causal=True,
+                                          P=P, q_rank=r, kv_rank=j)
     else:
         q1 = qd[:, :, :1].contiguous()
         ws = torch.empty(ra.ring_attn_decode_ws_bytes(B, H, Hkv, N, d, P), dtype=torch.uint8, device=dev)
