@@ -752,7 +752,9 @@ hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, 
   if (rows <= 0) return hipSuccess;
   if (d != 64 && d != 128) return hipErrorInvalidValue;
   const int64_t per_block = 256 / (d / 8);      // rows per workgroup
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + per_block - 1) / per_block)), dim3(256), 0, s,
+  const int64_t g = (rows + per_block - 1) / per_block;
+  if (g > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)g), dim3(256), 0, s,
                      reinterpret_cast<const __bf16*>(out), reinterpret_cast<const __bf16*>(dout), lse, rowstat, rows, d);
   return hipGetLastError();
 }
@@ -792,6 +794,7 @@ hipError_t launch_dq_d(const BwdArgs& a, unsigned g, hipStream_t s) {
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, hipStream_t s) {
   const int64_t g = (int64_t)a.s.n_hosts * a.s.B * a.s.Hkv * a.n_kvtiles;
   if (g <= 0) return hipSuccess;
+  if (g > 0x7fffffffLL) return hipErrorInvalidValue;
   if (d == 128) return launch_dkdv_d<128>(a, (unsigned)g, s);
   if (d == 64) return launch_dkdv_d<64>(a, (unsigned)g, s);
   return hipErrorInvalidValue;
@@ -800,6 +803,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, hipStream_t s) {
 hipError_t launch_bwd_dq(const BwdArgs& a, int d, hipStream_t s) {
   const int64_t g = (int64_t)a.s.n_hosts * a.s.B * a.s.H * a.s.n_qtiles;
   if (g <= 0) return hipSuccess;
+  if (g > 0x7fffffffLL) return hipErrorInvalidValue;
   if (d == 128) return launch_dq_d<128>(a, (unsigned)g, s);
   if (d == 64) return launch_dq_d<64>(a, (unsigned)g, s);
   return hipErrorInvalidValue;

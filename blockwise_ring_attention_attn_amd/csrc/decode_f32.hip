@@ -115,6 +115,7 @@ __global__ __launch_bounds__(64 * kWavesF) void decode_partial_f32_kernel(Decode
 hipError_t launch_decode_partial_f32(const DecodeArgs& a, int d, hipStream_t s) {
   const int64_t g = (int64_t)a.B * a.Hkv * a.sub_groups * a.P * a.chunks_per_block;
   if (g <= 0) return hipSuccess;
+  if (g > 0x7fffffffLL) return hipErrorInvalidValue;
   if (a.group < 1 || a.sub_groups != (a.group + kMaxGroup - 1) / kMaxGroup) return hipErrorInvalidValue;
   if (d == 128) hipLaunchKernelGGL(decode_partial_f32_kernel<128>, dim3((unsigned)g), dim3(64 * kWavesF), 0, s, a);
   else if (d == 64) hipLaunchKernelGGL(decode_partial_f32_kernel<64>, dim3((unsigned)g), dim3(64 * kWavesF), 0, s, a);

@@ -81,6 +81,7 @@ hipError_t launch_spin(int microseconds, hipStream_t s) {
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
   const int64_t g = (a.rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (g > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)g), dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -88,6 +89,7 @@ hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s) {
 hipError_t launch_finalize(const FinalizeArgs& a, int out_bf16, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
   const int64_t g = (a.rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (g > 0x7fffffffLL) return hipErrorInvalidValue;
   if (out_bf16) hipLaunchKernelGGL(finalize_kernel<true>, dim3((unsigned)g), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(finalize_kernel<false>, dim3((unsigned)g), dim3(256), 0, s, a);
   return hipGetLastError();
