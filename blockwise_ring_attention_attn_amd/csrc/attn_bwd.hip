@@ -444,6 +444,15 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
         qa[decltype(I)::value] = read_rowfrag<D>(qbuf(slot), off, decltype(I)::value);
         oa[decltype(I)::value] = read_rowfrag<D>(obuf(slot), off, decltype(I)::value);
       });
+      // the tile's row statistics, read now so that their latency hides
+      // under the MFMAs: rows 8 g + 4 half + {0, 1} and + {2, 3}
+      float4 rsa[4], rsb4[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int q0 = 8 * g + 4 * half;
+        rsa[g] = *reinterpret_cast<const float4*>(&rsb(slot)[q0][0]);
+        rsb4[g] = *reinterpret_cast<const float4*>(&rsb(slot)[q0 + 2][0]);
+      }
       static_for<KS>([&](auto T_) __attribute__((always_inline)) {
         constexpr int t = decltype(T_)::value;
         const bf16x8 a = qa[t % RA], o = oa[t % RA];
@@ -467,9 +476,8 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdArgs G) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         // row statistics of rows 8 g + 4 half + e
-        const int q0 = 8 * g + 4 * half;
-        const float4 a4 = *reinterpret_cast<const float4*>(&rsb(slot)[q0][0]);
-        const float4 b4 = *reinterpret_cast<const float4*>(&rsb(slot)[q0 + 2][0]);
+        const float4 a4 = rsa[g];
+        const float4 b4 = rsb4[g];
         const float lv[4] = {a4.x, a4.z, b4.x, b4.z};
         const float dv[4] = {a4.y, a4.w, b4.y, b4.w};
 #pragma unroll
