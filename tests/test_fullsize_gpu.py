@@ -8,7 +8,8 @@ max|dlse| <= 1e-3.
 
 Workloads (all bf16, N(0, 1) inputs from the seeded generator):
   prefill   B=1 H=32 N=32768 d=128 causal, contiguous, P=8
-  gqa       B=1 H=8 Hkv=2 N=131072 d=128 causal, striped, P=8
+  gqa       B=1 H=8 Hkv=2 N=131072 d=128 causal, striped, P=8 (forward, and the
+            backward on sampled rows and keys)
   share     rank 7 of a P=8 ring over N=1,048,576: q 131072 tokens, H=4, causal
             (forward, and the backward share on sampled rows and keys)
   decode    B=16 H=32 Hkv=8 L=262144 d=128, P=8 ring blocks
@@ -211,6 +212,79 @@ def test_bwd_share_fullsize_sampled():
             assert ratio <= 1.0, f"bwd share h={h}: {nm} exceeds its bound (err/bound {ratio:.3f})"
             assert nw <= NORMWISE, f"bwd share h={h}: {nm} normwise relative error {nw:.2e}"
         del Pm, dS, O, dD, w, parts
+
+
+def test_bwd_striped_gqa_fullsize_sampled():
+    """Backward of the striped GQA workload at full size (B=1, H=8 / Hkv=2,
+    N=131072, d=128, causal, striped, P=8, bf16; its seeded inputs and a
+    seeded upstream gradient).  As in the backward share test, the oracle's
+    backward of a set of query rows at their positions gives those rows' dq
+    exactly and the complete dk, dv of keys that only those rows see: the
+    sample holds the last 64 positions (the only rows that see the last 64
+    keys) plus boundary and random rows, for all four query heads of kv
+    head 1, so that dk, dv of those keys sum the whole group."""
+    import torch
+    B, H, Hkv, N, d, P, seed = 1, 8, 2, 131072, 128, 8, 3
+    _log("bwd striped gqa: generating q, k, v, dout")
+    q, k, v = synth.qkv(seed, B, H, Hkv, N, d, "bf16")
+    do = synth.tensor(seed, synth.TENSOR_DOUT, B, H, N, d, "bf16")
+    qd, kd, vd, dod = (to_dev(x, "bf16") for x in (q, k, v, do))
+    _log("bwd striped gqa: running ring_attn_fwd and ring_attn_bwd")
+    out, lse = ra.ring_attn_fwd(qd, kd, vd, P=P, causal=True, layout="striped")
+    dq, dk, dv = ra.ring_attn_bwd(qd, kd, vd, out, dod, lse, P=P, causal=True, layout="striped")
+    torch.cuda.synchronize()
+    g, group = 1, H // Hkv
+    heads = list(range(g * group, (g + 1) * group))
+    keys = N - 64 + np.arange(64)
+    rows = np.unique(np.concatenate([np.arange(0, 9), np.arange(N // 2 - 4, N // 2 + 4),
+                                     np.random.default_rng(seed).integers(0, N - 64, 24), keys]))
+    rows_t = torch.from_numpy(rows).to(dq.device)
+    keys_t = torch.from_numpy(keys).to(dq.device)
+    got_dq = from_dev(dq[0].index_select(1, rows_t))
+    got_dk = from_dev(dk[0, g].index_select(0, keys_t))
+    got_dv = from_dev(dv[0, g].index_select(0, keys_t))
+    assert all(np.all(np.isfinite(x)) for x in (got_dq, got_dk, got_dv))
+    del qd, kd, vd, dod, out, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    scale = 1 / math.sqrt(d)
+    e = 2.0 ** -8
+    K, V = (host_vals(x[:, g:g + 1], "bf16") for x in (k, v))
+    Ka, Va = np.abs(K[0, 0].astype(np.float64)), np.abs(V[0, 0].astype(np.float64))
+    dk_ref = np.zeros((64, d))
+    dv_ref = np.zeros((64, d))
+    bk = np.zeros((64, d))
+    bv = np.zeros((64, d))
+    for h in heads:
+        _log(f"bwd striped gqa: oracle on head {h}, {len(rows)} rows against {N} keys")
+        Q, dO = (host_vals(x[:, h:h + 1, rows], "bf16") for x in (q, do))
+        dq_r, dk_r, dv_r, parts = oracle.attention_bwd(Q, K, V, dO, scale=scale, causal=True, q_pos=rows,
+                                                       parts=True)
+        pt = parts[(0, 0)]
+        Pm, dS = pt["P"], pt["dS"]
+        Qa, dOa = np.abs(Q[0, 0].astype(np.float64)), np.abs(dO[0, 0].astype(np.float64))
+        O = Pm @ V[0, 0].astype(np.float64)
+        w = e * np.abs(dS) + Pm * (e * (dOa * (np.abs(O) + Pm @ Va)).sum(axis=1))[:, None]
+        bq = scale * (w @ Ka) + e * np.abs(dq_r[0, 0])
+        err = np.abs(got_dq[h] - dq_r[0, 0])
+        ratio = float((err / (2 * bq + 1e-6)).max())
+        nw = _normwise(got_dq[h], dq_r[0, 0])
+        _log(f"bwd striped gqa h={h}: dq max|err|={err.max():.3e} normwise={nw:.2e} worst err/bound={ratio:.3f}")
+        assert ratio <= 1.0 and nw <= NORMWISE, f"bwd striped gqa h={h}: dq err/bound {ratio:.3f}, normwise {nw:.2e}"
+        dk_ref += dk_r[0, 0, keys]
+        dv_ref += dv_r[0, 0, keys]
+        bk += scale * (w[:, keys].T @ Qa)
+        bv += e * (Pm[:, keys].T @ dOa)
+        del Pm, dS, O, w, parts
+    bk += e * np.abs(dk_ref)
+    bv += e * np.abs(dv_ref)
+    for nm, got, ref, bnd in (("dk", got_dk, dk_ref, bk), ("dv", got_dv, dv_ref, bv)):
+        err = np.abs(got - ref)
+        ratio = float((err / (2 * bnd + 1e-6)).max())
+        nw = _normwise(got, ref)
+        _log(f"bwd striped gqa: {nm} of the last 64 keys max|err|={err.max():.3e} normwise={nw:.2e} "
+             f"worst err/bound={ratio:.3f}")
+        assert ratio <= 1.0, f"bwd striped gqa: {nm} exceeds its bound (err/bound {ratio:.3f})"
+        assert nw <= NORMWISE, f"bwd striped gqa: {nm} normwise relative error {nw:.2e}"
 
 
 def test_decode_fullsize():
