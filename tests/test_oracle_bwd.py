@@ -142,3 +142,30 @@ def test_sampled_gradients_equal_full(causal, chunk):
                                   causal=causal)
         np.testing.assert_allclose(parts["O"], O[0, 0], atol=1e-12)
         np.testing.assert_allclose(parts["lse"], lse[0, 0], atol=1e-12)
+
+
+def test_row_subset_gives_its_rows_and_the_keys_only_they_see():
+    """The full-size backward tests evaluate the oracle on a subset of query
+    rows at their positions: each row's softmax depends on no other row, so
+    the subset's dq equals the full dq at those rows, and the subset's dk, dv
+    of keys that only those rows see (causal: the last keys) equal the full
+    ones, with GQA's query heads of a kv head summed."""
+    rng = np.random.default_rng(38)
+    B, H, Hkv, N, d = 1, 4, 2, 96, 8
+    q, dO = _rand(rng, B, H, N, d), _rand(rng, B, H, N, d)
+    k, v = _rand(rng, B, Hkv, N, d), _rand(rng, B, Hkv, N, d)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, dO, causal=True, scale=0.35)
+    keys = np.arange(N - 8, N)
+    rows = np.unique(np.concatenate([[0, 1, 40, 57], keys]))
+    g, group = 1, H // Hkv
+    sk, sv = np.zeros((len(keys), d)), np.zeros((len(keys), d))
+    for h in range(g * group, (g + 1) * group):
+        dqs, dks, dvs = oracle.attention_bwd(q[:, h:h + 1, rows], k[:, g:g + 1], v[:, g:g + 1], dO[:, h:h + 1, rows],
+                                             causal=True, scale=0.35, q_pos=rows)
+        np.testing.assert_allclose(dqs[0, 0], dq[0, h, rows], atol=1e-13)
+        sk += dks[0, 0, keys]
+        sv += dvs[0, 0, keys]
+    np.testing.assert_allclose(sk, dk[0, g, keys], atol=1e-13)
+    np.testing.assert_allclose(sv, dv[0, g, keys], atol=1e-13)
+    # a key also seen by rows outside the subset is not complete
+    assert np.abs(dks[0, 0, 10] - dk[0, g, 10]).max() > 1e-6
