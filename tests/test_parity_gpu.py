@@ -184,6 +184,27 @@ def test_share_matches_oracle(layout, dtype):
 
 
 @pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
+def test_shares_assemble_the_full_ring_bitwise(layout):
+    """The P shares, each rank's queries against every kv block in its ring
+    order, run the same kernel over the same blocks in the same order as
+    the full ring does for that host: put back at their positions, their
+    outputs and lse are bitwise those of ring_attn_fwd."""
+    import torch
+    B, H, Hkv, N, d, P = 1, 4, 2, 8 * 160, 128, 8
+    q, k, v = _case(10, B, H, Hkv, N, d, "bf16")
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    out, lse = ra.ring_attn_fwd(qd, kd, vd, P=P, causal=True, layout=layout)
+    torch.cuda.synchronize()
+    out, lse = from_dev(out), from_dev(lse)
+    for rank, pos in enumerate(oracle.host_positions(N, P, layout)):
+        o, l = ra.ring_attn_fwd_share(to_dev(np.ascontiguousarray(q[:, :, pos]), "bf16"), kd, vd, P=P, rank=rank,
+                                      causal=True, layout=layout)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(o), out[:, :, pos]), f"rank {rank}: output differs"
+        assert np.array_equal(from_dev(l), lse[:, :, pos]), f"rank {rank}: lse differs"
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_step_state_against_oracle(layout, dtype):
     """ring_attn_step on one (q block, kv block) pair, then on a second kv
