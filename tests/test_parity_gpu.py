@@ -183,21 +183,22 @@ def test_share_matches_oracle(layout, dtype):
         assert_close(from_dev(o), from_dev(l), Ow, Lw, dtype, f"share rank={rank} {layout}")
 
 
-@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
-def test_shares_assemble_the_full_ring_bitwise(layout):
+@pytest.mark.parametrize("layout,dtype", [("contiguous", "bf16"), ("striped", "bf16"), ("zigzag", "bf16"),
+                                          ("striped", "f32")])
+def test_shares_assemble_the_full_ring_bitwise(layout, dtype):
     """The P shares, each rank's queries against every kv block in its ring
     order, run the same kernel over the same blocks in the same order as
     the full ring does for that host: put back at their positions, their
     outputs and lse are bitwise those of ring_attn_fwd."""
     import torch
     B, H, Hkv, N, d, P = 1, 4, 2, 8 * 160, 128, 8
-    q, k, v = _case(10, B, H, Hkv, N, d, "bf16")
-    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    q, k, v = _case(10, B, H, Hkv, N, d, dtype)
+    qd, kd, vd = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
     out, lse = ra.ring_attn_fwd(qd, kd, vd, P=P, causal=True, layout=layout)
     torch.cuda.synchronize()
     out, lse = from_dev(out), from_dev(lse)
     for rank, pos in enumerate(oracle.host_positions(N, P, layout)):
-        o, l = ra.ring_attn_fwd_share(to_dev(np.ascontiguousarray(q[:, :, pos]), "bf16"), kd, vd, P=P, rank=rank,
+        o, l = ra.ring_attn_fwd_share(to_dev(np.ascontiguousarray(q[:, :, pos]), dtype), kd, vd, P=P, rank=rank,
                                       causal=True, layout=layout)
         torch.cuda.synchronize()
         assert np.array_equal(from_dev(o), out[:, :, pos]), f"rank {rank}: output differs"
